@@ -1,0 +1,18 @@
+"""CPU oracle for the audio-encoder forward pass.  TEST INFRASTRUCTURE ONLY.
+
+Plain, slow NumPy float64 code written from the pages' description of the
+model (the model card "MOSS-Transcribe-preview-2B-GGUF": Architecture table,
+"Implementation notes (correctness)" and the gotcha list).  It shares no code
+with the HIP library and imports nothing from it; only the test suite, the
+package's smoke check and the benchmark's CPU-baseline leg may call it.
+
+Modules
+  logmel   waveform -> normalised log-mel frames
+  encoder  log-mel -> encoder frames (conv front-end, windowed-attention
+           tower, head, optional SwiGLU adapter)
+
+Every function below is pinned by tests under ``tests/`` that check it against
+closed forms, invariants, brute force, or an independent library routine.
+"""
+
+from . import logmel, encoder  # noqa: F401
