@@ -1,0 +1,199 @@
+"""Throughput of the windowed-attention audio encoder on one MI355X.
+
+A step is one pass of the whole forward path over one batch: waveform ->
+log-mel (mt_logmel) -> conv front-end, 32 windowed-attention layers and the
+encoder head (mt_encode).  The workload is 16 clips of 30 s of synthetic
+16 kHz audio (sum of three tones plus noise, 20 % silent gaps), bf16 weights
+and matrix operands with fp32 accumulation, window 104 encoder frames.
+Inputs are resident in device memory before the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is encoder audio-seconds per second.
+`roofline` describes the dominant kernel (the FFN up-projection GEMM with
+fused bias + GELU), timed live with HIP events on the launch stream during
+the timed steps; `cpu_baseline` times the CPU oracle on one clip of the same
+workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_flops(geom, lens_T, window):
+    """Multiply-add count x 2 of one forward pass (excluding the log-mel)."""
+    C, D, F, O, A = (geom[k] for k in ("conv_ch", "d_model", "d_ffn", "d_out", "adapter_hidden"))
+    L = geom["n_layers"]
+    tot = dict(conv1=0, conv2=0, conv3=0, conv_out=0, qkv=0, attn=0, o=0, ffn=0, head=0, adapter=0)
+    for T in lens_T:
+        T1 = (T + 1) // 2
+        T2 = (T1 + 1) // 2
+        N = (T2 + 1) // 2
+        tot["conv1"] += 2 * 9 * C * T1 * 64
+        tot["conv2"] += 2 * 9 * C * C * T2 * 32
+        tot["conv3"] += 2 * 9 * C * C * N * 16
+        tot["conv_out"] += 2 * 16 * C * D * N
+        tot["qkv"] += L * 2 * N * D * 3 * D
+        tot["o"] += L * 2 * N * D * D
+        tot["ffn"] += L * 2 * 2 * N * D * F
+        ws = [min(window, N - s) for s in range(0, N, window)]
+        tot["attn"] += L * sum(4 * w * w * D for w in ws)
+        tot["head"] += 2 * N * D * (D + O)
+        tot["adapter"] += 2 * N * O * 3 * A
+    return tot
+
+
+def cpu_baseline(clip, weights, geom, window, min_seconds=10.0, max_clips=4):
+    """The oracle (NumPy float64) on whole clips of the workload, until about
+    min_seconds of CPU time have passed."""
+    import numpy as np  # noqa: F401
+    from oracle import encoder as OE
+    from oracle import logmel as OL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    P = OE.as_f64(weights)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        mel = OL.log_mel(clip)
+        OE.encode_clip(mel, P, geom, window)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or done >= max_clips:
+            break
+    audio = done * len(clip) / 16000.0
+    return {"value": audio / el, "unit": "audio-s/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} x 30 s clip (clip 0 of the 16 x 30 s workload): log-mel + "
+                      f"full encoder in NumPy float64, {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(clips are independent: a multi-GPU run is data-parallel with no "
+              "collective, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import windowed_attention_audio_amd as W
+
+    torch.cuda.set_device(0)
+    wl = synth.workload(2)
+    geom = synth.geom_for(wl)
+    clips = synth.make_clips(wl)
+    weights = synth.make_weights(geom, bf16=True)
+    lens = wl.n_samples
+    lens_T = [n // 160 for n in lens]
+    window = wl.window
+
+    dev_w = [torch.from_numpy(v).cuda() for v in weights.values()]
+    enc = W.mt_encoder_create(W.encoder_config(geom, W.MT_BF16), dev_w)
+    torch.cuda.synchronize()
+    del dev_w
+    wav = torch.from_numpy(np.concatenate(clips)).cuda()
+    mel = torch.empty((sum(lens_T), 128), dtype=torch.float32, device="cuda")
+    M = sum(W.mt_encoder_frames(t) for t in lens_T)
+    out = torch.empty((M, geom["d_out"]), dtype=torch.float32, device="cuda")
+    ws_mel = torch.empty(W.mt_logmel_workspace_size(lens), dtype=torch.uint8, device="cuda")
+    ws_enc = torch.empty(W.mt_encode_workspace_size(enc, lens_T, window), dtype=torch.uint8,
+                         device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream)
+        W.mt_encode(enc, mel, lens_T, window, out=out, ws=ws_enc, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    dominant = "fc1"
+    W.mt_trace_arm(dominant, max_launches=geom["n_layers"] * args.steps + 8)
+    W.mt_trace_collect()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    fc1_ms, fc1_n = W.mt_trace_collect()
+    W.mt_trace_arm(None)
+
+    audio_s = sum(lens) / 16000.0
+    flops = algorithmic_flops(geom, lens_T, window)
+    total_flops = sum(flops.values())
+    fc1_flops = 2.0 * M * geom["d_ffn"] * geom["d_model"]
+    fc1_avg = fc1_ms / max(fc1_n, 1)
+    fc1_tflops = fc1_flops / (fc1_avg * 1e-3) / 1e12
+
+    breakdown = {}
+    if not args.no_breakdown:
+        stages = ["mel", "mel_norm", "conv1", "conv2", "conv3", "conv_out", "ln1", "qkv", "attn",
+                  "o", "ln2", "fc1", "fc2", "ln_post", "proj1", "proj2"]
+        for st in stages:
+            W.mt_trace_arm(st, max_launches=64)
+            W.mt_trace_collect()
+            step()
+            torch.cuda.synchronize()
+            t, n = W.mt_trace_collect()
+            breakdown[st] = round(t, 4)
+        W.mt_trace_arm(None)
+        mel_bytes = 4 * sum(lens) + 4 * 128 * sum(lens_T)
+        breakdown["mel_GBps"] = round(mel_bytes / (breakdown["mel"] * 1e-3) / 1e9, 1)
+
+    res = {
+        "metric": "encoder audio-sec/sec (bf16, batch 16 x 30 s clips); % of bf16 MFMA peak",
+        "value": round(audio_s / (ms * 1e-3), 2),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded tones + noise + silent gaps; seeded random weights)",
+        "config": {"workload": wl.name, "clips": len(lens), "clip_seconds": 30, "window": window,
+                   "mel_frames": sum(lens_T), "encoder_frames": M, "layers": geom["n_layers"]},
+        "mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
+        "roofline": {"kernel": "fc1 (FFN up-projection GEMM + bias + GELU, M=%d N=%d K=%d)"
+                               % (M, geom["d_ffn"], geom["d_model"]),
+                     "bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fc1_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(fc1_avg, 5), "launches": fc1_n},
+    }
+    if breakdown:
+        res["breakdown_ms_per_step"] = breakdown
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(clips[0], weights, geom, window)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

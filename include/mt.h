@@ -1,0 +1,199 @@
+/*
+ * mt.h -- C ABI of the windowed-attention audio encoder for AMD MI355X (gfx950).
+ *
+ * The library computes the forward pass of the audio encoder described in the
+ * model card "MOSS-Transcribe-preview-2B-GGUF":
+ *   - Architecture table, row "Audio": 16 kHz mono input, 128 mel bins,
+ *     n_fft 400, hop 160, matching Whisper's feature extractor;
+ *   - gotcha list: Whisper drops the trailing STFT frame, so a clip of n
+ *     samples gives exactly n / hop mel frames;
+ *   - row "Conv front-end": three 3x3 stride-2 Conv2D (1 -> 480 -> 480 -> 480),
+ *     conv_out 480*16 = 7680 -> 1280 without bias, sinusoidal positions;
+ *   - row "Audio encoder": 32 pre-LN Transformer layers, d 1280, 20 heads of
+ *     64, FFN 5120, windowed (block-diagonal) attention;
+ *   - row "Encoder head": ln_post -> proj1 (1280 -> 1280) -> GELU -> proj2
+ *     (1280 -> 2048);
+ *   - row "Adapter": gated MLP (SwiGLU) 2048 -> 8192 -> 2048 (optional).
+ *
+ * Conventions for every entry point
+ *   - Device pointers point to memory of the current HIP device; host pointers
+ *     are read before the call returns and may be freed afterwards.
+ *   - The caller owns every device buffer (inputs, outputs, packed weights,
+ *     workspace).  The library never allocates device memory; it owns only
+ *     the small host handle of an encoder.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream and does not synchronise the host.
+ *   - Errors are returned as mt_status; nothing is launched when a call
+ *     fails validation.  mt_last_error() gives a thread-local description.
+ *   - Calls that share a workspace, or that write the same output, must be
+ *     ordered by the caller (for example by issuing them on one stream).
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MT_OK = 0,
+  MT_ERR_INVALID_ARG = 1, /* null pointer, bad length, bad layout, ... */
+  MT_ERR_UNSUPPORTED = 2, /* geometry or window the kernels are not built for */
+  MT_ERR_WORKSPACE = 3,   /* workspace or packed buffer too small */
+  MT_ERR_HIP = 4          /* a HIP runtime call failed */
+} mt_status;
+
+typedef enum { MT_F32 = 0, MT_BF16 = 1 } mt_dtype;
+
+typedef enum {
+  MT_PACKED = 0, /* sequences stored back to back, no padding */
+  MT_PADDED = 1  /* sequence i starts at row i * max_len */
+} mt_layout;
+
+/* A batch of variable-length sequences.  `len` is a HOST array of n_seqs
+ * lengths (samples for a waveform batch, mel frames for a log-mel batch).
+ * For MT_PADDED, max_len is the row stride per sequence and every len[i]
+ * must be <= max_len; for MT_PACKED max_len is ignored. */
+typedef struct {
+  int32_t layout;
+  int32_t n_seqs;
+  const int64_t* len;
+  int64_t max_len;
+} mt_batch;
+
+/* Encoder geometry and compute type.  The production geometry is
+ * {128, 480, 1280, 32, 20, 64, 5120, 2048, 0 or 8192}.  The kernels require
+ * n_mels == 128, head_dim == 64, n_heads * head_dim == d_model, conv_ch a
+ * multiple of 32 (at most 2048), d_ffn, d_out, adapter_hidden multiples of
+ * 64, and d_model a multiple of 256 (at most 2048).  n_layers may be 0
+ * (front-end only). */
+typedef struct {
+  int32_t n_mels;
+  int32_t conv_ch;
+  int32_t d_model;
+  int32_t n_layers;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t d_ffn;
+  int32_t d_out;
+  int32_t adapter_hidden; /* 0: no adapter */
+  int32_t dtype;          /* mt_dtype: MT_F32 = fp32 everywhere; MT_BF16 = bf16
+                             weights and matrix operands, fp32 accumulation,
+                             fp32 residual stream, statistics and softmax */
+  int32_t with_head;      /* 1: full output (d_out wide); 0: stop after the
+                             tower and return the fp32 residual stream
+                             (d_model wide) */
+  float ln_eps;           /* LayerNorm epsilon, 1e-5 */
+} mt_encoder_config;
+
+typedef struct mt_encoder mt_encoder; /* opaque host handle */
+
+/* ---- lengths ---------------------------------------------------------- */
+
+/* Mel frames of a clip of n samples: floor(n / 160) (trailing frame dropped).
+ * Returns -1 for n < 0. */
+int64_t mt_mel_frames(int64_t n_samples);
+
+/* Encoder frames for T mel frames: three stride-2 convs, ceil(ceil(ceil(T/2)/2)/2).
+ * Returns -1 for T < 0. */
+int64_t mt_encoder_frames(int64_t mel_frames);
+
+/* ---- log-mel ---------------------------------------------------------- */
+
+/* Workspace bytes for mt_logmel on this batch. */
+mt_status mt_logmel_workspace_size(const mt_batch* wav, size_t* bytes);
+
+/* Waveform -> normalised log-mel (Architecture table, row "Audio").
+ *   wav   device fp32 samples: packed [sum n_i] or padded [n_seqs, max_len];
+ *         each n_i >= 201 (reflect padding by 200 needs more than 200).
+ *   mel   device fp32 output, frame-major: packed [sum T_i, 128] or padded
+ *         [n_seqs, max_len / 160, 128] with rows t >= T_i set to 0;
+ *         T_i = floor(n_i / 160).
+ * Per clip: periodic Hann 400, reflect-padded centred frames, |rFFT|^2,
+ * Slaney mel filterbank (0..8 kHz), log10(max(., 1e-10)), clamp at the clip's
+ * own maximum minus 8, then (x + 4) / 4. */
+mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ---- encoder ---------------------------------------------------------- */
+
+/* Number of weight tensors create() expects for this geometry:
+ * 7 + 16 * n_layers + 6 (+ 3 with the adapter). */
+int32_t mt_encoder_n_weights(const mt_encoder_config* cfg);
+
+/* Bytes of the packed-weight buffer create() needs. */
+mt_status mt_encoder_packed_bytes(const mt_encoder_config* cfg, size_t* bytes);
+
+/* Build an encoder.  `weights` is a HOST array of n_weights DEVICE pointers to
+ * contiguous fp32 tensors in this canonical order (torch layouts: Linear
+ * [out, in], Conv2d [out, in, k_freq, k_time]):
+ *   conv1.weight [C,1,3,3], conv1.bias [C], conv2.weight [C,C,3,3], conv2.bias,
+ *   conv3.weight, conv3.bias, conv_out.weight [D, C*16];
+ *   per layer l: ln1.weight [D], ln1.bias, q.weight [D,D], q.bias, k.weight,
+ *     k.bias, v.weight, v.bias, o.weight, o.bias, ln2.weight, ln2.bias,
+ *     fc1.weight [F,D], fc1.bias [F], fc2.weight [D,F], fc2.bias [D];
+ *   ln_post.weight, ln_post.bias, proj1.weight [D,D], proj1.bias,
+ *   proj2.weight [O,D], proj2.bias [O];
+ *   adapter only: gate.weight [A,O], up.weight [A,O], down.weight [O,A].
+ * Feature j of conv_out's input is conv3 channel j / 16 at frequency j % 16.
+ * `packed` (device, >= mt_encoder_packed_bytes, 256-byte aligned) receives
+ * the weights in kernel layouts (bf16 rounded to nearest-even for MT_BF16);
+ * it must stay alive and unchanged until mt_encoder_destroy.  The source
+ * tensors may be freed once the repacking work on `stream` has completed. */
+mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* weights,
+                            int32_t n_weights, void* packed, size_t packed_bytes,
+                            void* stream, mt_encoder** out);
+
+void mt_encoder_destroy(mt_encoder* enc);
+
+/* Largest window (encoder frames) the attention kernel keeps on chip.  A
+ * larger `window` is accepted when no sequence is longer than this (the
+ * attention is then the same as with window = the longest sequence). */
+int32_t mt_max_window(void);
+
+/* Workspace bytes for mt_encode on this batch and window. */
+mt_status mt_encode_workspace_size(const mt_encoder* enc, const mt_batch* mel_b, int32_t window,
+                                   size_t* bytes);
+
+/* Log-mel -> encoder frames.
+ *   mel     device fp32, [sum T_i, n_mels] packed or [n_seqs, max_len, n_mels]
+ *           padded (rows t >= T_i are not read); each T_i >= 1.
+ *   window  W >= 1, in encoder frames: frames [kW, (k+1)W) of each sequence
+ *           attend only to each other, in every layer.
+ *   out     device fp32, packed [sum N_i, d] or padded
+ *           [n_seqs, mt_encoder_frames(max_len), d] with rows >= N_i set to 0;
+ *           N_i = mt_encoder_frames(T_i); d = d_out (or d_model when
+ *           with_head == 0).
+ *   ws      device workspace of >= mt_encode_workspace_size bytes, 256-byte
+ *           aligned; its contents on entry do not matter. */
+mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel_b,
+                    int32_t window, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- diagnostics -------------------------------------------------------- */
+
+/* Stage timer.  Arms timing of one stage of mt_logmel / mt_encode, named
+ * "mel", "mel_norm", "conv1", "conv2", "conv3", "conv_out", "ln1", "qkv",
+ * "attn", "o", "ln2", "fc1", "fc2", "ln_post", "proj1", "proj2",
+ * "adapter_gu", "adapter_down", "copy_rows" or "zero_pad": each later launch
+ * of that stage is bracketed by two hipEvents recorded on the call's stream,
+ * for up to max_launches launches.  NULL or "" disarms.  Timing only; results
+ * are unchanged.  Process-wide state, not thread-safe. */
+mt_status mt_trace_arm(const char* stage, int32_t max_launches);
+
+/* Waits for the recorded events, returns the summed duration (ms) and the
+ * number of timed launches, and clears the record (the stage stays armed). */
+mt_status mt_trace_collect(double* total_ms, int32_t* launches);
+
+/* ---- errors ----------------------------------------------------------- */
+
+const char* mt_status_string(mt_status s);
+const char* mt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MT_H */

@@ -1,0 +1,197 @@
+"""GPU parity at the workloads' full sizes, plus invariants of the HIP path.
+
+  * 16 x 30 s batch: the whole batch on the GPU, sampled clips on the oracle;
+  * 10-minute stream: the whole stream on the GPU, sampled windows on the
+    oracle (each from its receptive field, an 8-frame halo of mel frames,
+    encoded with the window's stream position);
+  * 32 clips of 2..60 s, packed, window 52, with the SwiGLU adapter: the
+    whole batch on the GPU, sampled clips on the oracle;
+  * packed == padded, run-to-run determinism, window locality (bitwise), a
+    workspace poisoned with NaN bytes, degenerate windows and lengths, and
+    the host-side rejections.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import encoder as OE
+from oracle import logmel as OL
+from tests.helpers import GpuModel, assert_bf16_rows, gpu_logmel, split_rows
+
+pytestmark = pytest.mark.gpu
+
+FULL = synth.FULL_GEOM
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def weights_bf16():
+    return synth.make_weights(FULL, bf16=True)
+
+
+@pytest.fixture(scope="module")
+def P64(weights_bf16):
+    return OE.as_f64(weights_bf16)
+
+
+@pytest.fixture(scope="module")
+def model(weights_bf16):
+    return GpuModel(FULL, "bf16", weights_bf16)
+
+
+def test_batch16x30s_sampled(model, P64):
+    w = synth.workload(2)
+    clips = synth.make_clips(w)
+    say("16x30s: GPU log-mel + encode")
+    mel = gpu_logmel(clips)
+    T = [len(c) // 160 for c in clips]
+    mels = split_rows(mel, T)
+    got = model.encode(mels, w.window)
+    assert got.shape == (6000, 2048)
+    rows = split_rows(got, [375] * 16)
+    for i in (0, 7, 15):
+        ref = OE.encode_clip(OL.log_mel(clips[i]), P64, FULL, w.window)
+        m = assert_bf16_rows(rows[i], ref, what=f"16x30s clip {i}")
+        say(f"  clip {i}: min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def test_stream_10min_sampled_windows(model, P64):
+    w = synth.workload(3)
+    wav = synth.make_clips(w)[0]
+    say("10 min stream: GPU log-mel + encode")
+    mel = gpu_logmel([wav])
+    got = model.encode([mel], w.window)
+    assert got.shape == (7500, 2048)
+    ref_mel = OL.log_mel(wav)
+    T, W = ref_mel.shape[0], w.window
+    for k in (0, 1, 40, 72):
+        s = max(0, 8 * (k * W - 1))
+        e = min(T, 8 * (k + 1) * W + 8)
+        seg = OE.encode_clip(ref_mel[s:e], P64, FULL, W, t0=s // 8)
+        r0 = k * W - s // 8
+        n = min(W, 7500 - k * W)
+        m = assert_bf16_rows(got[k * W:k * W + n], seg[r0:r0 + n], what=f"stream window {k}")
+        say(f"  window {k} ({n} rows): min cos {m['cos'].min():.6f} "
+            f"max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def test_varlen_packed_adapter_sampled(weights_bf16):
+    w = synth.workload(4)
+    geom = synth.geom_for(w)
+    wts = synth.make_weights(geom, bf16=True)
+    for k in weights_bf16:  # the tower is shared with the other workloads
+        assert np.array_equal(wts[k], weights_bf16[k])
+    ad = GpuModel(geom, "bf16", wts)
+    clips = synth.make_clips(w)
+    say("32 varlen clips + adapter, W=52")
+    mel = gpu_logmel(clips)
+    T = [len(c) // 160 for c in clips]
+    got = ad.encode(split_rows(mel, T), w.window)
+    N = [OE.encoder_frames(t) for t in T]
+    assert got.shape == (sum(N), 2048)
+    rows = split_rows(got, N)
+    P = OE.as_f64(wts)
+    order = np.argsort(N)
+    for i in (int(order[0]), int(order[len(order) // 2]), 5):
+        ref = OE.encode_clip(OL.log_mel(clips[i]), P, geom, w.window)
+        m = assert_bf16_rows(rows[i], ref, what=f"varlen clip {i} (N={N[i]})")
+        say(f"  clip {i} N={N[i]}: min cos {m['cos'].min():.6f} "
+            f"max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def _mels(seed, Ts):
+    rng = np.random.default_rng(seed)
+    return [rng.uniform(-1.0, 1.5, (t, 128)).astype(np.float32) for t in Ts]
+
+
+def test_packed_equals_padded(model):
+    mels = _mels(3, [3000, 1, 17, 800, 2999])
+    a = model.encode(mels, 104, layout=0)
+    b = model.encode(mels, 104, layout=1)
+    N = [OE.encoder_frames(m.shape[0]) for m in mels]
+    assert b.shape == (5, OE.encoder_frames(3000), 2048)
+    for i, r in enumerate(split_rows(a, N)):
+        assert np.array_equal(b[i, :N[i]], r)
+        assert np.all(b[i, N[i]:] == 0)
+
+
+def test_deterministic(model):
+    mels = _mels(4, [3000, 1200])
+    a = model.encode(mels, 104)
+    b = model.encode(mels, 104)
+    assert np.array_equal(a, b)
+
+
+def test_window_locality_bitwise(model):
+    W = 104
+    mel = _mels(5, [3000])[0]
+    base = model.encode([mel], W)
+    for k in (0, 1, 3):
+        m2 = mel.copy()
+        lo, hi = 8 * k * W, min(2999, 8 * (k + 1) * W - 8)
+        m2[lo:hi + 1] += 0.5
+        out = model.encode([m2], W)
+        inside = np.zeros(375, bool)
+        inside[k * W:min(375, (k + 1) * W)] = True
+        assert np.array_equal(out[~inside], base[~inside]), f"window {k} leaked"
+        assert np.abs(out[inside] - base[inside]).max() > 1e-3
+
+
+def test_poisoned_workspace(model):
+    import torch
+    import windowed_attention_audio_amd as W
+    mels = _mels(6, [3000, 640])
+    ref = model.encode(mels, 104)
+    lens = [m.shape[0] for m in mels]
+    mel = torch.from_numpy(np.concatenate(mels)).cuda()
+    ws = torch.full((W.mt_encode_workspace_size(model.enc, lens, 104),), 255, dtype=torch.uint8,
+                    device="cuda")
+    out = torch.full((sum(OE.encoder_frames(t) for t in lens), 2048), float("nan"),
+                     device="cuda")
+    W.mt_encode(model.enc, mel, lens, 104, out=out, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_degenerate_windows_and_lengths(model, P64):
+    mels = _mels(7, [1, 9, 200])
+    N = [OE.encoder_frames(m.shape[0]) for m in mels]
+    assert N == [1, 2, 25]
+    for W in (1, 2, 25, 1000):
+        got = split_rows(model.encode(mels, W), N)
+        for g, m in zip(got, mels):
+            ref = OE.encode_clip(m.astype(np.float64), P64, FULL, W)
+            assert_bf16_rows(g, ref, what=f"W={W} T={m.shape[0]}")
+
+
+def test_rejections(model):
+    import torch
+    import windowed_attention_audio_amd as W
+    mel = torch.zeros((3000, 128), device="cuda")
+    with pytest.raises(W.MtError) as e:
+        W.mt_encode(model.enc, mel, [3000], 300)  # 375 frames > on-chip window
+    assert e.value.status == W.MT_ERR_UNSUPPORTED
+    with pytest.raises(W.MtError) as e:
+        W.mt_encode(model.enc, mel, [3000], 0)
+    assert e.value.status == W.MT_ERR_INVALID_ARG
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(W.MtError) as e:
+        W.mt_encode(model.enc, mel, [3000], 104, ws=ws)
+    assert e.value.status == W.MT_ERR_WORKSPACE
+    with pytest.raises(W.MtError) as e:
+        W.mt_logmel(torch.zeros(200, device="cuda"), [200])
+    assert e.value.status == W.MT_ERR_INVALID_ARG

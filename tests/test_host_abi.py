@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/mt.h declares, and
+reject bad arguments on the host before any launch.  The length functions are
+checked against the closed forms, and the build's log-mel tables against the
+oracle's filterbank.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import windowed_attention_audio_amd as W
+from oracle import encoder as OE
+from oracle import logmel as OL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(W.LIB_PATH):
+        pytest.skip("libmt.so not built")
+    return W.lib()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), f"libmt.so does not export {n}"
+    assert set(names) == set(W.EXPORTS)
+
+
+@pytest.mark.parametrize("n", [0, 159, 160, 16000, 16077, 480000, 9600000])
+def test_mel_frames(L, n):
+    assert W.mt_mel_frames(n) == n // 160 == OL.frame_count(n)
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 7, 8, 9, 100, 3000, 60000, 60001])
+def test_encoder_frames(L, T):
+    c = lambda x: -(-x // 2)
+    assert W.mt_encoder_frames(T) == c(c(c(T))) == OE.encoder_frames(T) if T else True
+    assert W.mt_encoder_frames(T) == math.ceil(math.ceil(math.ceil(T / 2) / 2) / 2)
+
+
+def test_negative_lengths(L):
+    assert W.mt_mel_frames(-1) == -1 and W.mt_encoder_frames(-5) == -1
+
+
+def test_logmel_workspace_and_rejections(L):
+    assert W.mt_logmel_workspace_size([16000]) > 0
+    assert W.mt_logmel_workspace_size([16000] * 64) > W.mt_logmel_workspace_size([16000])
+    for bad in ([200], [201, 100], [-5]):
+        with pytest.raises(W.MtError) as e:
+            W.mt_logmel_workspace_size(bad)
+        assert e.value.status == W.MT_ERR_INVALID_ARG
+    with pytest.raises(W.MtError) as e:  # padded: length above the row stride
+        W.mt_logmel_workspace_size([3000, 5000], layout=W.MT_PADDED, max_len=4000)
+    assert e.value.status == W.MT_ERR_INVALID_ARG
+    b = W.make_batch([16000], layout=7)
+    n = ctypes.c_size_t()
+    assert L.mt_logmel_workspace_size(ctypes.byref(b), ctypes.byref(n)) == W.MT_ERR_INVALID_ARG
+    b = W.Batch(0, 0, None, 0)
+    assert L.mt_logmel_workspace_size(ctypes.byref(b), ctypes.byref(n)) == W.MT_ERR_INVALID_ARG
+    b = W.Batch(0, 2, None, 0)
+    assert L.mt_logmel_workspace_size(ctypes.byref(b), ctypes.byref(n)) == W.MT_ERR_INVALID_ARG
+    assert b"len is NULL" in L.mt_last_error()
+    # null device pointers are rejected before anything is launched
+    b = W.make_batch([16000])
+    assert L.mt_logmel(None, ctypes.byref(b), None, None, 0, None) == W.MT_ERR_INVALID_ARG
+
+
+def test_config_validation(L):
+    ok = W.encoder_config(synth.FULL_GEOM, W.MT_BF16)
+    assert W.mt_encoder_n_weights(ok) == 7 + 16 * 32 + 6
+    ad = W.encoder_config(dict(synth.FULL_GEOM, adapter_hidden=8192), W.MT_BF16)
+    assert W.mt_encoder_n_weights(ad) == 7 + 16 * 32 + 6 + 3
+    assert W.mt_encoder_n_weights(ad) == len(synth.weight_names(dict(synth.FULL_GEOM,
+                                                                     adapter_hidden=8192)))
+    for over, status in ((dict(n_mels=80), W.MT_ERR_UNSUPPORTED),
+                         (dict(head_dim=128, n_heads=10), W.MT_ERR_UNSUPPORTED),
+                         (dict(n_heads=19), W.MT_ERR_UNSUPPORTED),
+                         (dict(conv_ch=100), W.MT_ERR_UNSUPPORTED),
+                         (dict(d_ffn=0), W.MT_ERR_INVALID_ARG),
+                         (dict(n_layers=-1), W.MT_ERR_INVALID_ARG)):
+        cfg = W.encoder_config(dict(synth.FULL_GEOM, **over), W.MT_BF16)
+        with pytest.raises(W.MtError) as e:
+            W.mt_encoder_packed_bytes(cfg)
+        assert e.value.status == status, over
+    bad = W.encoder_config(synth.FULL_GEOM, 7)
+    with pytest.raises(W.MtError):
+        W.mt_encoder_packed_bytes(bad)
+
+
+def test_packed_bytes(L):
+    geom = synth.FULL_GEOM
+    names = synth.weight_names(geom)
+    n_params = sum(int(np.prod(s)) for _, s in names)
+    # vectors and conv1's 9 taps stay fp32; matrices become bf16
+    n_vec = sum(int(np.prod(s)) for n, s in names if len(s) == 1 or n == "conv1.weight")
+    f32 = W.mt_encoder_packed_bytes(W.encoder_config(geom, W.MT_F32))
+    b16 = W.mt_encoder_packed_bytes(W.encoder_config(geom, W.MT_BF16))
+    assert abs(n_params - 647.9e6) < 0.1e6  # encoder parameters, about 648 M
+    pad = 256 * len(names)
+    assert 4 * n_params <= f32 <= 4 * n_params + pad
+    # the head's two matrices are stored twice for the hi/lo-split activations
+    head = 1280 * 1280 + 2048 * 1280
+    expect = 2 * (n_params - n_vec + head) + 4 * n_vec
+    assert expect <= b16 <= expect + pad
+
+
+def test_create_rejects_before_launch(L):
+    cfg = W.encoder_config(dict(synth.FULL_GEOM, n_layers=1), W.MT_BF16)
+    n = W.mt_encoder_n_weights(cfg)
+    ptrs = (ctypes.c_void_p * n)(*([1] * n))
+    h = ctypes.c_void_p()
+    assert L.mt_encoder_create(ctypes.byref(cfg), ptrs, n - 1, ctypes.c_void_p(256), 1 << 40,
+                               None, ctypes.byref(h)) == W.MT_ERR_INVALID_ARG
+    ptrs[3] = None
+    assert L.mt_encoder_create(ctypes.byref(cfg), ptrs, n, ctypes.c_void_p(256), 1 << 40,
+                               None, ctypes.byref(h)) == W.MT_ERR_INVALID_ARG
+    ptrs[3] = 1
+    assert L.mt_encoder_create(ctypes.byref(cfg), ptrs, n, ctypes.c_void_p(256), 16,
+                               None, ctypes.byref(h)) == W.MT_ERR_WORKSPACE
+    assert L.mt_encoder_create(ctypes.byref(cfg), ptrs, n, ctypes.c_void_p(100), 1 << 40,
+                               None, ctypes.byref(h)) == W.MT_ERR_INVALID_ARG
+    assert not h.value
+
+
+def test_encode_rejects_null_encoder(L):
+    b = W.make_batch([3000])
+    n = ctypes.c_size_t()
+    assert L.mt_encode_workspace_size(None, ctypes.byref(b), 104, ctypes.byref(n)) == \
+        W.MT_ERR_INVALID_ARG
+    assert L.mt_encode(None, None, ctypes.byref(b), 104, None, None, 0, None) == \
+        W.MT_ERR_INVALID_ARG
+
+
+def test_status_strings_and_trace(L):
+    for s in range(5):
+        assert L.mt_status_string(s).startswith(b"MT_")
+    W.mt_trace_arm(None)
+    assert W.mt_trace_collect() == (0.0, 0)
+    assert W.mt_max_window() == 256
+
+
+def test_library_tables_match_oracle_filterbank():
+    from windowed_attention_audio_amd import gen_tables as G
+    rows = G.filterbank()
+    F = np.zeros((128, 201))
+    for m, (first, w) in enumerate(rows):
+        F[m, first:first + len(w)] = w
+    assert np.max(np.abs(F - OL.mel_filterbank())) < 1e-12

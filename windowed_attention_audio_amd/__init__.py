@@ -1,0 +1,259 @@
+"""Python binding of libmt.so, the MI355X (gfx950) windowed-attention audio
+encoder.  Argument marshalling only: every step of the forward pass runs in
+the library's HIP kernels.  PyTorch provides device memory and streams.
+
+The functions carry the names of the C entry points (include/mt.h):
+
+    mt_mel_frames(n)                 floor(n / 160)
+    mt_encoder_frames(T)             ceil(ceil(ceil(T / 2) / 2) / 2)
+    mt_logmel(wav, lens, ...)        waveform -> normalised log-mel
+    mt_encoder_create(cfg, weights)  -> Encoder (packed weights on device)
+    mt_encode(enc, mel, lens, W)     log-mel -> encoder frames
+
+Importing the package does not need a GPU; calling the compute entry points
+does, and raises if the compiled library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmt.so")
+
+MT_OK, MT_ERR_INVALID_ARG, MT_ERR_UNSUPPORTED, MT_ERR_WORKSPACE, MT_ERR_HIP = range(5)
+MT_F32, MT_BF16 = 0, 1
+MT_PACKED, MT_PADDED = 0, 1
+
+EXPORTS = (
+    "mt_mel_frames", "mt_encoder_frames", "mt_logmel_workspace_size", "mt_logmel",
+    "mt_encoder_n_weights", "mt_encoder_packed_bytes", "mt_encoder_create",
+    "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
+    "mt_status_string", "mt_last_error", "mt_trace_arm", "mt_trace_collect",
+)
+
+
+class MtError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("len", ctypes.POINTER(ctypes.c_int64)), ("max_len", ctypes.c_int64)]
+
+
+class EncoderConfig(ctypes.Structure):
+    _fields_ = [("n_mels", ctypes.c_int32), ("conv_ch", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_ffn", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("adapter_hidden", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("with_head", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmt.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m windowed_attention_audio_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        c_sz = ctypes.c_size_t
+        vp = ctypes.c_void_p
+        L.mt_mel_frames.restype = ctypes.c_int64
+        L.mt_mel_frames.argtypes = [ctypes.c_int64]
+        L.mt_encoder_frames.restype = ctypes.c_int64
+        L.mt_encoder_frames.argtypes = [ctypes.c_int64]
+        L.mt_logmel_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(c_sz)]
+        L.mt_logmel.argtypes = [vp, ctypes.POINTER(Batch), vp, vp, c_sz, vp]
+        L.mt_encoder_n_weights.argtypes = [ctypes.POINTER(EncoderConfig)]
+        L.mt_encoder_packed_bytes.argtypes = [ctypes.POINTER(EncoderConfig), ctypes.POINTER(c_sz)]
+        L.mt_encoder_create.argtypes = [ctypes.POINTER(EncoderConfig), ctypes.POINTER(vp),
+                                        ctypes.c_int32, vp, c_sz, vp, ctypes.POINTER(vp)]
+        L.mt_encoder_destroy.argtypes = [vp]
+        L.mt_encoder_destroy.restype = None
+        L.mt_max_window.restype = ctypes.c_int32
+        L.mt_encode_workspace_size.argtypes = [vp, ctypes.POINTER(Batch), ctypes.c_int32,
+                                               ctypes.POINTER(c_sz)]
+        L.mt_encode.argtypes = [vp, vp, ctypes.POINTER(Batch), ctypes.c_int32, vp, vp, c_sz, vp]
+        L.mt_trace_arm.argtypes = [ctypes.c_char_p, ctypes.c_int32]
+        L.mt_trace_arm.restype = ctypes.c_int
+        L.mt_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int32)]
+        L.mt_trace_collect.restype = ctypes.c_int
+        L.mt_status_string.restype = ctypes.c_char_p
+        L.mt_status_string.argtypes = [ctypes.c_int]
+        L.mt_last_error.restype = ctypes.c_char_p
+        for name in ("mt_logmel_workspace_size", "mt_logmel", "mt_encoder_packed_bytes",
+                     "mt_encoder_create", "mt_encode_workspace_size", "mt_encode"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != MT_OK:
+        L = lib()
+        raise MtError(status, L.mt_status_string(status).decode() + ": " +
+                      L.mt_last_error().decode())
+
+
+def make_batch(lens, layout=MT_PACKED, max_len=0):
+    arr = (ctypes.c_int64 * len(lens))(*[int(x) for x in lens])
+    b = Batch(layout, len(lens), arr, int(max_len))
+    b._keep = arr
+    return b
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def mt_mel_frames(n: int) -> int:
+    return lib().mt_mel_frames(int(n))
+
+
+def mt_encoder_frames(T: int) -> int:
+    return lib().mt_encoder_frames(int(T))
+
+
+def mt_max_window() -> int:
+    return lib().mt_max_window()
+
+
+def mt_logmel_workspace_size(lens, layout=MT_PACKED, max_len=0) -> int:
+    b = make_batch(lens, layout, max_len)
+    n = ctypes.c_size_t()
+    _check(lib().mt_logmel_workspace_size(ctypes.byref(b), ctypes.byref(n)))
+    return n.value
+
+
+def mt_logmel(wav, lens, layout=MT_PACKED, max_len=0, mel=None, ws=None, stream=None):
+    """wav: fp32 CUDA tensor, packed [sum n] or padded [B, max_len].
+    Returns the fp32 log-mel tensor [sum T, 128] or [B, max_len // 160, 128]."""
+    import torch
+    assert wav.is_cuda and wav.dtype == torch.float32 and wav.is_contiguous()
+    if layout == MT_PADDED:
+        max_len = wav.shape[1]
+        shape = (len(lens), max_len // 160, 128)
+    else:
+        shape = (sum(int(n) // 160 for n in lens), 128)
+    b = make_batch(lens, layout, max_len)
+    if mel is None:
+        mel = torch.empty(shape, dtype=torch.float32, device=wav.device)
+    nbytes = mt_logmel_workspace_size(lens, layout, max_len)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=wav.device)
+    _check(lib().mt_logmel(ctypes.c_void_p(wav.data_ptr()), ctypes.byref(b),
+                           ctypes.c_void_p(mel.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                           ws.numel(), _stream_ptr(stream)))
+    return mel
+
+
+def encoder_config(geom: dict, dtype: int, with_head: bool = True, ln_eps: float = 1e-5):
+    return EncoderConfig(geom["n_mels"], geom["conv_ch"], geom["d_model"], geom["n_layers"],
+                         geom["n_heads"], geom["head_dim"], geom["d_ffn"], geom["d_out"],
+                         geom.get("adapter_hidden", 0), dtype, 1 if with_head else 0, ln_eps)
+
+
+class Encoder:
+    """An encoder whose packed weights live in a torch-owned device buffer."""
+
+    def __init__(self, handle, cfg, packed):
+        self.handle = handle
+        self.cfg = cfg
+        self.packed = packed
+
+    @property
+    def d_out(self):
+        return self.cfg.d_out if self.cfg.with_head else self.cfg.d_model
+
+    def close(self):
+        if self.handle:
+            lib().mt_encoder_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mt_encoder_n_weights(cfg: EncoderConfig) -> int:
+    return lib().mt_encoder_n_weights(ctypes.byref(cfg))
+
+
+def mt_encoder_packed_bytes(cfg: EncoderConfig) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_encoder_packed_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def mt_encoder_create(cfg: EncoderConfig, weights, device="cuda", stream=None) -> Encoder:
+    """weights: fp32 CUDA tensors in the canonical order of include/mt.h."""
+    import torch
+    for w in weights:
+        assert w.is_cuda and w.dtype == torch.float32 and w.is_contiguous()
+    nbytes = mt_encoder_packed_bytes(cfg)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ptrs = (ctypes.c_void_p * len(weights))(*[w.data_ptr() for w in weights])
+    h = ctypes.c_void_p()
+    _check(lib().mt_encoder_create(ctypes.byref(cfg), ptrs, len(weights),
+                                   ctypes.c_void_p(packed.data_ptr()), nbytes,
+                                   _stream_ptr(stream), ctypes.byref(h)))
+    return Encoder(h, cfg, packed)
+
+
+def mt_encode_workspace_size(enc: Encoder, lens, window, layout=MT_PACKED, max_len=0) -> int:
+    b = make_batch(lens, layout, max_len)
+    n = ctypes.c_size_t()
+    _check(lib().mt_encode_workspace_size(enc.handle, ctypes.byref(b), int(window),
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def mt_encode(enc: Encoder, mel, lens, window, layout=MT_PACKED, out=None, ws=None, stream=None):
+    """mel: fp32 CUDA tensor [sum T, 128] (packed) or [B, max_len, 128] (padded).
+    Returns fp32 [sum N, d] or [B, N(max_len), d]."""
+    import torch
+    assert mel.is_cuda and mel.dtype == torch.float32 and mel.is_contiguous()
+    max_len = mel.shape[1] if layout == MT_PADDED else 0
+    d = enc.d_out
+    if layout == MT_PADDED:
+        shape = (len(lens), mt_encoder_frames(max_len), d)
+    else:
+        shape = (sum(mt_encoder_frames(int(t)) for t in lens), d)
+    b = make_batch(lens, layout, max_len)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=mel.device)
+    if ws is None:
+        nbytes = mt_encode_workspace_size(enc, lens, window, layout, max_len)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=mel.device)
+    _check(lib().mt_encode(enc.handle, ctypes.c_void_p(mel.data_ptr()), ctypes.byref(b),
+                           int(window), ctypes.c_void_p(out.data_ptr()),
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
+    return out
+
+
+def mt_trace_arm(stage, max_launches=4096):
+    """Time every launch of one named stage with HIP events (None disarms)."""
+    _check(lib().mt_trace_arm(stage.encode() if stage else None, int(max_launches)))
+
+
+def mt_trace_collect():
+    """(total_ms, launches) of the armed stage since the last collect."""
+    t = ctypes.c_double()
+    n = ctypes.c_int32()
+    _check(lib().mt_trace_collect(ctypes.byref(t), ctypes.byref(n)))
+    return t.value, n.value

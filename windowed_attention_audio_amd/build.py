@@ -1,0 +1,78 @@
+"""Builds libmt.so (the HIP kernels and the C ABI) for gfx950 in-tree.
+
+    python -m windowed_attention_audio_amd.build [--host-only]
+
+--host-only additionally builds libmt_host_check.so from api.cpp with g++ and
+stub launchers, so the argument validation can be run under sanitizers on a
+machine without a GPU (used by the CPU test-suite).
+"""
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmt.so")
+
+SOURCES = ["api.cpp", "mel.hip", "conv1.hip", "gemm.hip", "norm.hip", "attn.hip", "misc.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for p in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if p and os.path.exists(p):
+            return p
+    raise RuntimeError("hipcc not found")
+
+
+def flags():
+    return [
+        "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+        # no packed-fp32 instructions in generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
+        "-Wno-pass-failed",
+    ]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{out}")
+    return obj, out
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    subprocess.run([sys.executable, os.path.join(PKG, "gen_tables.py"),
+                    os.path.join(CSRC, "mel_tables.inc")], check=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    if verbose:
+        for (o, msg) in results:
+            if msg:
+                print(msg)
+    objs = [o for o, _ in results]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("linking libmt.so failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,730 @@
+// C ABI of the encoder library: argument validation, length planning,
+// workspace carving and the launch sequence.  All validation happens on the
+// host before the first launch, so a failing call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "mt.h"
+
+using namespace mt;
+
+namespace {
+
+thread_local std::string g_err;
+
+mt_status fail(mt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+mt_status hip_fail(hipError_t e, const char* where) {
+  return fail(MT_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call, where)                     \
+  do {                                           \
+    hipError_t e_ = (call);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// A launch of a named stage (timed when that stage is armed).
+#define STAGE(call, stage)                       \
+  do {                                           \
+    TraceScope ts_(stage, s);                    \
+    HIP_TRY(call, stage);                        \
+  } while (0)
+
+constexpr int64_t HOP = 160;
+constexpr int MAX_WINDOW = 256;
+constexpr int64_t MAX_SEQS = 1 << 20;
+constexpr size_t ALIGN = 256;
+
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// ---- stage timer (diagnostics): brackets launches of one named stage with
+// hipEvents recorded on the launch stream.
+struct Tracer {
+  std::string stage;
+  std::vector<hipEvent_t> ev;  // pairs
+  int used = 0;
+} g_trace;
+
+struct TraceScope {
+  hipEvent_t stop = nullptr;
+  hipStream_t s;
+  TraceScope(const char* stage, hipStream_t st) : s(st) {
+    if (g_trace.stage.empty() || g_trace.stage != stage) return;
+    if (2 * (g_trace.used + 1) > (int)g_trace.ev.size()) return;
+    hipEvent_t start = g_trace.ev[2 * g_trace.used];
+    stop = g_trace.ev[2 * g_trace.used + 1];
+    ++g_trace.used;
+    (void)hipEventRecord(start, s);
+  }
+  ~TraceScope() {
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
+inline int64_t half_up(int64_t x) { return (x + 1) / 2; }
+
+// Carves named regions out of one buffer.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+mt_status check_batch(const mt_batch* b, const char* what) {
+  if (!b) return fail(MT_ERR_INVALID_ARG, "%s: batch is NULL", what);
+  if (b->layout != MT_PACKED && b->layout != MT_PADDED)
+    return fail(MT_ERR_INVALID_ARG, "%s: layout %d is neither MT_PACKED nor MT_PADDED", what,
+                b->layout);
+  if (b->n_seqs < 1 || b->n_seqs > MAX_SEQS)
+    return fail(MT_ERR_INVALID_ARG, "%s: n_seqs %d out of range [1, %lld]", what, b->n_seqs,
+                (long long)MAX_SEQS);
+  if (!b->len) return fail(MT_ERR_INVALID_ARG, "%s: len is NULL", what);
+  for (int i = 0; i < b->n_seqs; ++i) {
+    if (b->len[i] < 0) return fail(MT_ERR_INVALID_ARG, "%s: len[%d] < 0", what, i);
+    if (b->layout == MT_PADDED && b->len[i] > b->max_len)
+      return fail(MT_ERR_INVALID_ARG, "%s: len[%d] = %lld exceeds max_len %lld", what, i,
+                  (long long)b->len[i], (long long)b->max_len);
+  }
+  return MT_OK;
+}
+
+// ------------------------------------------------------------------ log-mel plan
+struct MelPlan {
+  int B = 0;
+  std::vector<int64_t> sample_off, row_off;
+  std::vector<int32_t> seq_len, cu_frames;
+  int64_t total_frames = 0, out_rows = 0, tmax = 0;
+  size_t off_sample = 0, off_row = 0, off_len = 0, off_cu = 0, off_gmax = 0, bytes = 0;
+};
+
+mt_status plan_mel(const mt_batch* wb, MelPlan& p) {
+  mt_status st = check_batch(wb, "mt_logmel");
+  if (st != MT_OK) return st;
+  const int B = wb->n_seqs;
+  p.B = B;
+  p.sample_off.resize(B);
+  p.row_off.resize(B);
+  p.seq_len.resize(B);
+  p.cu_frames.assign(B + 1, 0);
+  p.tmax = wb->layout == MT_PADDED ? wb->max_len / HOP : 0;
+  int64_t s_acc = 0, t_acc = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t n = wb->len[i];
+    if (n <= 200)
+      return fail(MT_ERR_INVALID_ARG,
+                  "mt_logmel: len[%d] = %lld samples; reflect padding by 200 needs more than 200",
+                  i, (long long)n);
+    if (n > INT32_MAX) return fail(MT_ERR_UNSUPPORTED, "mt_logmel: len[%d] too long", i);
+    const int64_t T = n / HOP;
+    p.seq_len[i] = (int32_t)n;
+    p.sample_off[i] = wb->layout == MT_PADDED ? (int64_t)i * wb->max_len : s_acc;
+    p.row_off[i] = wb->layout == MT_PADDED ? (int64_t)i * p.tmax : t_acc;
+    s_acc += n;
+    t_acc += T;
+    if (t_acc > INT32_MAX / 2) return fail(MT_ERR_UNSUPPORTED, "mt_logmel: batch too long");
+    p.cu_frames[i + 1] = (int32_t)t_acc;
+  }
+  p.total_frames = t_acc;
+  p.out_rows = wb->layout == MT_PADDED ? (int64_t)B * p.tmax : t_acc;
+  Carver c;
+  p.off_sample = c.take(8 * (size_t)B);
+  p.off_row = c.take(8 * (size_t)B);
+  p.off_len = c.take(4 * (size_t)B);
+  p.off_cu = c.take(4 * (size_t)(B + 1));
+  p.off_gmax = c.take(4 * (size_t)B);
+  p.bytes = c.off;
+  return MT_OK;
+}
+
+// ------------------------------------------------------------------ encoder
+struct Layer {
+  const float *ln1_g, *ln1_b;
+  const void* wqkv;
+  const float* bqkv;
+  const void* wo;
+  const float* bo;
+  const float *ln2_g, *ln2_b;
+  const void* w1;
+  const float* b1;
+  const void* w2;
+  const float* b2;
+};
+
+struct PackedLayout {
+  size_t conv1_w, conv1_b, conv2_w, conv2_b, conv3_w, conv3_b, conv_out_w;
+  struct L {
+    size_t ln1_g, ln1_b, wqkv, bqkv, wo, bo, ln2_g, ln2_b, w1, b1, w2, b2;
+  };
+  std::vector<L> layers;
+  size_t lnp_g, lnp_b, wp1, bp1, wp2, bp2, wgu, wd;
+  size_t bytes;
+};
+
+mt_status check_config(const mt_encoder_config* c) {
+  if (!c) return fail(MT_ERR_INVALID_ARG, "config is NULL");
+  if (c->dtype != MT_F32 && c->dtype != MT_BF16)
+    return fail(MT_ERR_INVALID_ARG, "dtype %d is neither MT_F32 nor MT_BF16", c->dtype);
+  if (c->n_layers < 0 || c->n_heads < 1 || c->head_dim < 1 || c->conv_ch < 1 || c->d_model < 1 ||
+      c->d_ffn < 1 || c->d_out < 1 || c->adapter_hidden < 0 || c->n_mels < 1)
+    return fail(MT_ERR_INVALID_ARG, "non-positive size in config");
+  if (!(c->ln_eps > 0.f)) return fail(MT_ERR_INVALID_ARG, "ln_eps must be > 0");
+  if (c->with_head != 0 && c->with_head != 1)
+    return fail(MT_ERR_INVALID_ARG, "with_head must be 0 or 1");
+  if (c->n_mels != 128) return fail(MT_ERR_UNSUPPORTED, "n_mels must be 128");
+  if (c->head_dim != 64) return fail(MT_ERR_UNSUPPORTED, "head_dim must be 64");
+  if (c->n_heads * c->head_dim != c->d_model)
+    return fail(MT_ERR_UNSUPPORTED, "n_heads * head_dim must equal d_model");
+  if (c->d_model % 256 || c->d_model > 2048)
+    return fail(MT_ERR_UNSUPPORTED, "d_model must be a multiple of 256, at most 2048");
+  if (c->conv_ch % 32) return fail(MT_ERR_UNSUPPORTED, "conv_ch must be a multiple of 32");
+  if (c->d_ffn % 64 || c->d_out % 64 || c->adapter_hidden % 64)
+    return fail(MT_ERR_UNSUPPORTED, "d_ffn, d_out, adapter_hidden must be multiples of 64");
+  if (c->conv_ch > 2048) return fail(MT_ERR_UNSUPPORTED, "conv_ch must be at most 2048");
+  if (c->adapter_hidden && !c->with_head)
+    return fail(MT_ERR_INVALID_ARG, "the adapter needs with_head = 1");
+  return MT_OK;
+}
+
+PackedLayout packed_layout(const mt_encoder_config& c) {
+  const size_t es = c.dtype == MT_BF16 ? 2 : 4;
+  const size_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
+  const size_t KD = c.dtype == MT_BF16 ? 2 * D : D;  // hi/lo split head input
+  PackedLayout p;
+  Carver k;
+  p.conv1_w = k.take(C * 9 * 4);
+  p.conv1_b = k.take(C * 4);
+  p.conv2_w = k.take(C * 9 * C * es);
+  p.conv2_b = k.take(C * 4);
+  p.conv3_w = k.take(C * 9 * C * es);
+  p.conv3_b = k.take(C * 4);
+  p.conv_out_w = k.take(D * 16 * C * es);
+  p.layers.resize(c.n_layers);
+  for (auto& L : p.layers) {
+    L.ln1_g = k.take(D * 4);
+    L.ln1_b = k.take(D * 4);
+    L.wqkv = k.take(3 * D * D * es);
+    L.bqkv = k.take(3 * D * 4);
+    L.wo = k.take(D * D * es);
+    L.bo = k.take(D * 4);
+    L.ln2_g = k.take(D * 4);
+    L.ln2_b = k.take(D * 4);
+    L.w1 = k.take(F * D * es);
+    L.b1 = k.take(F * 4);
+    L.w2 = k.take(D * F * es);
+    L.b2 = k.take(D * 4);
+  }
+  p.lnp_g = k.take(D * 4);
+  p.lnp_b = k.take(D * 4);
+  p.wp1 = k.take(D * KD * es);
+  p.bp1 = k.take(D * 4);
+  p.wp2 = k.take(O * KD * es);
+  p.bp2 = k.take(O * 4);
+  p.wgu = A ? k.take(2 * A * O * es) : 0;
+  p.wd = A ? k.take(O * A * es) : 0;
+  p.bytes = k.off;
+  return p;
+}
+
+int n_weights_of(const mt_encoder_config& c) {
+  return 7 + 16 * c.n_layers + 6 + (c.adapter_hidden ? 3 : 0);
+}
+
+struct EncPlan {
+  int B = 0;
+  std::vector<int32_t> words;  // cu_T, cu_T1, cu_T2, cu_N, cu_win (B+1 each)
+  std::vector<int64_t> mel_row_off;
+  int64_t sumT = 0, sumT1 = 0, sumT2 = 0, M = 0, maxN = 0, n_windows = 0, out_stride = 0;
+  int wpad = 0;
+  // workspace offsets
+  size_t o_words, o_rowoff, o_act1, o_act2, o_act3, o_x, o_h, o_qkv, o_att, o_ffn, o_y, o_ahid, bytes;
+};
+
+}  // namespace
+
+struct mt_encoder {
+  mt_encoder_config cfg;
+  int dt;     // 1 = bf16
+  size_t es;  // element bytes of matrix operands
+  const float *conv1_w, *conv1_b, *conv2_b, *conv3_b;
+  const void *conv2_w, *conv3_w, *conv_out_w;
+  std::vector<Layer> layers;
+  const float *lnp_g, *lnp_b, *bp1, *bp2;
+  const void *wp1, *wp2, *wgu, *wd;
+};
+
+namespace {
+
+mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window, EncPlan& p) {
+  mt_status st = check_batch(mb, "mt_encode");
+  if (st != MT_OK) return st;
+  if (window < 1) return fail(MT_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+  const mt_encoder_config& c = enc->cfg;
+  const int B = mb->n_seqs;
+  p.B = B;
+  p.words.assign(5 * (size_t)(B + 1), 0);
+  int32_t* cuT = p.words.data();
+  int32_t* cuT1 = cuT + (B + 1);
+  int32_t* cuT2 = cuT1 + (B + 1);
+  int32_t* cuN = cuT2 + (B + 1);
+  int32_t* cuW = cuN + (B + 1);
+  p.mel_row_off.resize(B);
+  for (int i = 0; i < B; ++i) {
+    const int64_t T = mb->len[i];
+    if (T < 1) return fail(MT_ERR_INVALID_ARG, "mt_encode: len[%d] must be >= 1 mel frame", i);
+    const int64_t T1 = half_up(T), T2 = half_up(T1), N = half_up(T2);
+    p.mel_row_off[i] = mb->layout == MT_PADDED ? (int64_t)i * mb->max_len : p.sumT;
+    p.sumT += T;
+    p.sumT1 += T1;
+    p.sumT2 += T2;
+    p.M += N;
+    p.maxN = std::max(p.maxN, N);
+    p.n_windows += (N + window - 1) / window;
+    if (p.sumT1 * 64 > INT32_MAX)
+      return fail(MT_ERR_UNSUPPORTED, "mt_encode: batch too long (%lld mel frames)", (long long)p.sumT);
+    cuT[i + 1] = (int32_t)p.sumT;
+    cuT1[i + 1] = (int32_t)p.sumT1;
+    cuT2[i + 1] = (int32_t)p.sumT2;
+    cuN[i + 1] = (int32_t)p.M;
+    cuW[i + 1] = (int32_t)p.n_windows;
+  }
+  const int64_t weff = std::min<int64_t>(window, p.maxN);
+  if (weff > MAX_WINDOW)
+    return fail(MT_ERR_UNSUPPORTED, "mt_encode: window %d over sequences of up to %lld frames "
+                "exceeds the on-chip maximum %d", window, (long long)p.maxN, MAX_WINDOW);
+  p.wpad = (int)((weff + 63) / 64 * 64);  // whole key chunks of 64 stay on chip
+  p.out_stride = mb->layout == MT_PADDED ? half_up(half_up(half_up(mb->max_len))) : 0;
+
+  const size_t es = enc->es;
+  const size_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
+  const size_t M = (size_t)p.M;
+  Carver k;
+  p.o_words = k.take(4 * p.words.size());
+  p.o_rowoff = k.take(8 * (size_t)B);
+  p.o_act1 = k.take((size_t)p.sumT1 * 64 * C * es);
+  p.o_act2 = k.take((size_t)p.sumT2 * 32 * C * es);
+  p.o_act3 = k.take(M * 16 * C * es);
+  p.o_x = k.take(M * D * 4);
+  size_t hb = M * D * es;
+  if (c.with_head && enc->dt == 1) hb = std::max(hb, M * 2 * D * 2);
+  p.o_h = k.take(hb);
+  p.o_qkv = k.take(M * 3 * D * es);
+  p.o_att = k.take(M * D * es);
+  size_t fb = M * F * es;
+  if (c.with_head) fb = std::max(fb, enc->dt == 1 ? M * 2 * D * 2 : M * D * 4);
+  p.o_ffn = k.take(fb);
+  p.o_y = k.take(A ? M * O * es : 0);
+  p.o_ahid = k.take(A ? M * A * es : 0);
+  p.bytes = k.off;
+  return MT_OK;
+}
+
+GemmArgs gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K,
+              const float* bias, void* C, int64_t ldc) {
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.bias = bias;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+int64_t mt_mel_frames(int64_t n) { return n < 0 ? -1 : n / HOP; }
+
+int64_t mt_encoder_frames(int64_t T) { return T < 0 ? -1 : half_up(half_up(half_up(T))); }
+
+int32_t mt_max_window(void) { return MAX_WINDOW; }
+
+const char* mt_status_string(mt_status s) {
+  switch (s) {
+    case MT_OK: return "MT_OK";
+    case MT_ERR_INVALID_ARG: return "MT_ERR_INVALID_ARG";
+    case MT_ERR_UNSUPPORTED: return "MT_ERR_UNSUPPORTED";
+    case MT_ERR_WORKSPACE: return "MT_ERR_WORKSPACE";
+    case MT_ERR_HIP: return "MT_ERR_HIP";
+  }
+  return "unknown mt_status";
+}
+
+const char* mt_last_error(void) { return g_err.c_str(); }
+
+mt_status mt_logmel_workspace_size(const mt_batch* wav, size_t* bytes) {
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  MelPlan p;
+  mt_status st = plan_mel(wav, p);
+  if (st != MT_OK) return st;
+  *bytes = p.bytes;
+  return MT_OK;
+}
+
+mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* ws, size_t ws_bytes,
+                    void* stream) {
+  MelPlan p;
+  mt_status st = plan_mel(wav_b, p);
+  if (st != MT_OK) return st;
+  if (!wav || !mel || !ws) return fail(MT_ERR_INVALID_ARG, "mt_logmel: NULL device pointer");
+  if ((uintptr_t)ws % ALIGN || (uintptr_t)mel % 16)
+    return fail(MT_ERR_INVALID_ARG, "mt_logmel: ws must be 256-byte and mel 16-byte aligned");
+  if (ws_bytes < p.bytes)
+    return fail(MT_ERR_WORKSPACE, "mt_logmel: workspace %zu bytes < required %zu", ws_bytes, p.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  // one upload: sample_off | row_off | seq_len | cu_frames (contiguous regions)
+  std::vector<uint32_t> words(p.off_gmax / 4, 0);
+  memcpy((char*)words.data() + p.off_sample, p.sample_off.data(), 8 * (size_t)p.B);
+  memcpy((char*)words.data() + p.off_row, p.row_off.data(), 8 * (size_t)p.B);
+  memcpy((char*)words.data() + p.off_len, p.seq_len.data(), 4 * (size_t)p.B);
+  memcpy((char*)words.data() + p.off_cu, p.cu_frames.data(), 4 * (size_t)(p.B + 1));
+  HIP_TRY(upload_words((uint32_t*)w, words.data(), (int64_t)words.size(), s), "upload tables");
+  int* gmax = (int*)(w + p.off_gmax);
+  const float ninf = -INFINITY;
+  int key;
+  memcpy(&key, &ninf, 4);
+  key = key >= 0 ? key : key ^ 0x7fffffff;
+  HIP_TRY(launch_fill_i32(gmax, key, p.B, s), "fill");
+  MelArgs a;
+  a.wav = wav;
+  a.mel = mel;
+  a.seq_sample_off = (const int64_t*)(w + p.off_sample);
+  a.seq_len = (const int32_t*)(w + p.off_len);
+  a.cu_frames = (const int32_t*)(w + p.off_cu);
+  a.seq_row_off = (const int64_t*)(w + p.off_row);
+  a.gmax = gmax;
+  a.nseq = p.B;
+  a.total_frames = p.total_frames;
+  a.out_rows = p.out_rows;
+  a.padded = wav_b->layout == MT_PADDED;
+  STAGE(launch_mel(a, s), "mel");
+  STAGE(launch_mel_norm(a, p.tmax, s), "mel_norm");
+  return MT_OK;
+}
+
+int32_t mt_encoder_n_weights(const mt_encoder_config* cfg) {
+  if (check_config(cfg) != MT_OK) return -1;
+  return n_weights_of(*cfg);
+}
+
+mt_status mt_encoder_packed_bytes(const mt_encoder_config* cfg, size_t* bytes) {
+  mt_status st = check_config(cfg);
+  if (st != MT_OK) return st;
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = packed_layout(*cfg).bytes;
+  return MT_OK;
+}
+
+mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wts, int32_t n_weights,
+                            void* packed, size_t packed_bytes, void* stream, mt_encoder** out) {
+  mt_status st = check_config(cfg);
+  if (st != MT_OK) return st;
+  if (!out) return fail(MT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const mt_encoder_config c = *cfg;
+  if (!wts) return fail(MT_ERR_INVALID_ARG, "weights is NULL");
+  if (n_weights != n_weights_of(c))
+    return fail(MT_ERR_INVALID_ARG, "expected %d weight tensors, got %d", n_weights_of(c), n_weights);
+  for (int i = 0; i < n_weights; ++i)
+    if (!wts[i]) return fail(MT_ERR_INVALID_ARG, "weights[%d] is NULL", i);
+  const PackedLayout L = packed_layout(c);
+  if (!packed) return fail(MT_ERR_INVALID_ARG, "packed is NULL");
+  if ((uintptr_t)packed % ALIGN) return fail(MT_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+  if (packed_bytes < L.bytes)
+    return fail(MT_ERR_WORKSPACE, "packed buffer %zu bytes < required %zu", packed_bytes, L.bytes);
+
+  hipStream_t s = (hipStream_t)stream;
+  const int bf = c.dtype == MT_BF16;
+  char* P = (char*)packed;
+  const int64_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
+  const size_t es = bf ? 2 : 4;
+  int wi = 0;
+  auto next = [&]() { return wts[wi++]; };
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_w), C * 9, s), "pack conv1");
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_b), C, s), "pack conv1 bias");
+  HIP_TRY(launch_pack_conv(next(), P + L.conv2_w, (int)C, bf, s), "pack conv2");
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv2_b), C, s), "pack conv2 bias");
+  HIP_TRY(launch_pack_conv(next(), P + L.conv3_w, (int)C, bf, s), "pack conv3");
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv3_b), C, s), "pack conv3 bias");
+  HIP_TRY(launch_pack_conv_out(next(), P + L.conv_out_w, (int)D, (int)C, 16, bf, s), "pack conv_out");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& Ll = L.layers[l];
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.ln1_g), D, s), "pack ln1");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.ln1_b), D, s), "pack ln1");
+    for (int j = 0; j < 3; ++j) {  // q, k, v stacked into [3D][D]
+      HIP_TRY(launch_convert(next(), P + Ll.wqkv + (size_t)j * D * D * es, D, D, D, 0, bf, s),
+              "pack qkv");
+      HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.bqkv) + j * D, D, s), "pack qkv bias");
+    }
+    HIP_TRY(launch_convert(next(), P + Ll.wo, D, D, D, 0, bf, s), "pack o");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.bo), D, s), "pack o bias");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.ln2_g), D, s), "pack ln2");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.ln2_b), D, s), "pack ln2");
+    HIP_TRY(launch_convert(next(), P + Ll.w1, F, D, D, 0, bf, s), "pack fc1");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.b1), F, s), "pack fc1 bias");
+    HIP_TRY(launch_convert(next(), P + Ll.w2, D, F, F, 0, bf, s), "pack fc2");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.b2), D, s), "pack fc2 bias");
+  }
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.lnp_g), D, s), "pack ln_post");
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.lnp_b), D, s), "pack ln_post");
+  const int64_t KD = bf ? 2 * D : D;
+  {
+    const float* w = next();
+    HIP_TRY(launch_convert(w, P + L.wp1, D, D, KD, 0, bf, s), "pack proj1");
+    if (bf) HIP_TRY(launch_convert(w, P + L.wp1, D, D, KD, D, bf, s), "pack proj1");
+  }
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.bp1), D, s), "pack proj1 bias");
+  {
+    const float* w = next();
+    HIP_TRY(launch_convert(w, P + L.wp2, O, D, KD, 0, bf, s), "pack proj2");
+    if (bf) HIP_TRY(launch_convert(w, P + L.wp2, O, D, KD, D, bf, s), "pack proj2");
+  }
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.bp2), O, s), "pack proj2 bias");
+  if (A) {
+    const float* g = next();
+    const float* u = next();
+    HIP_TRY(launch_pack_swiglu(g, u, P + L.wgu, (int)A, (int)O, bf, s), "pack adapter gate/up");
+    HIP_TRY(launch_convert(next(), P + L.wd, O, A, A, 0, bf, s), "pack adapter down");
+  }
+
+  mt_encoder* e = new mt_encoder();
+  e->cfg = c;
+  e->dt = bf;
+  e->es = es;
+  e->conv1_w = (const float*)(P + L.conv1_w);
+  e->conv1_b = (const float*)(P + L.conv1_b);
+  e->conv2_w = P + L.conv2_w;
+  e->conv2_b = (const float*)(P + L.conv2_b);
+  e->conv3_w = P + L.conv3_w;
+  e->conv3_b = (const float*)(P + L.conv3_b);
+  e->conv_out_w = P + L.conv_out_w;
+  e->layers.resize(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& Ll = L.layers[l];
+    Layer& y = e->layers[l];
+    y.ln1_g = (const float*)(P + Ll.ln1_g);
+    y.ln1_b = (const float*)(P + Ll.ln1_b);
+    y.wqkv = P + Ll.wqkv;
+    y.bqkv = (const float*)(P + Ll.bqkv);
+    y.wo = P + Ll.wo;
+    y.bo = (const float*)(P + Ll.bo);
+    y.ln2_g = (const float*)(P + Ll.ln2_g);
+    y.ln2_b = (const float*)(P + Ll.ln2_b);
+    y.w1 = P + Ll.w1;
+    y.b1 = (const float*)(P + Ll.b1);
+    y.w2 = P + Ll.w2;
+    y.b2 = (const float*)(P + Ll.b2);
+  }
+  e->lnp_g = (const float*)(P + L.lnp_g);
+  e->lnp_b = (const float*)(P + L.lnp_b);
+  e->wp1 = P + L.wp1;
+  e->bp1 = (const float*)(P + L.bp1);
+  e->wp2 = P + L.wp2;
+  e->bp2 = (const float*)(P + L.bp2);
+  e->wgu = A ? P + L.wgu : nullptr;
+  e->wd = A ? P + L.wd : nullptr;
+  *out = e;
+  return MT_OK;
+}
+
+void mt_encoder_destroy(mt_encoder* enc) { delete enc; }
+
+mt_status mt_trace_arm(const char* stage, int32_t max_launches) {
+  g_trace.stage.clear();
+  g_trace.used = 0;
+  if (!stage || !*stage) return MT_OK;
+  if (max_launches < 1 || max_launches > 1 << 16)
+    return fail(MT_ERR_INVALID_ARG, "max_launches must be in [1, 65536]");
+  while ((int)g_trace.ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e), "hipEventCreate");
+    g_trace.ev.push_back(e);
+  }
+  g_trace.stage = stage;
+  return MT_OK;
+}
+
+mt_status mt_trace_collect(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(MT_ERR_INVALID_ARG, "NULL output pointer");
+  double tot = 0.0;
+  for (int i = 0; i < g_trace.used; ++i) {
+    HIP_TRY(hipEventSynchronize(g_trace.ev[2 * i + 1]), "hipEventSynchronize");
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]), "hipEventElapsedTime");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = g_trace.used;
+  g_trace.used = 0;
+  return MT_OK;
+}
+
+mt_status mt_encode_workspace_size(const mt_encoder* enc, const mt_batch* mel_b, int32_t window,
+                                   size_t* bytes) {
+  if (!enc) return fail(MT_ERR_INVALID_ARG, "encoder is NULL");
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  EncPlan p;
+  mt_status st = plan_encode(enc, mel_b, window, p);
+  if (st != MT_OK) return st;
+  *bytes = p.bytes;
+  return MT_OK;
+}
+
+mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel_b, int32_t window,
+                    float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!enc) return fail(MT_ERR_INVALID_ARG, "encoder is NULL");
+  EncPlan p;
+  mt_status st = plan_encode(enc, mel_b, window, p);
+  if (st != MT_OK) return st;
+  if (!mel || !out || !ws) return fail(MT_ERR_INVALID_ARG, "mt_encode: NULL device pointer");
+  if ((uintptr_t)ws % ALIGN || (uintptr_t)out % 16 || (uintptr_t)mel % 16)
+    return fail(MT_ERR_INVALID_ARG, "mt_encode: ws must be 256-byte, mel and out 16-byte aligned");
+  if (ws_bytes < p.bytes)
+    return fail(MT_ERR_WORKSPACE, "mt_encode: workspace %zu bytes < required %zu", ws_bytes, p.bytes);
+
+  const mt_encoder_config& c = enc->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = enc->dt;
+  char* w = (char*)ws;
+  const int B = p.B;
+  const int M = (int)p.M;
+  const int C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
+
+  // tables: words (cu_T | cu_T1 | cu_T2 | cu_N | cu_win), then mel row offsets
+  HIP_TRY(upload_words((uint32_t*)(w + p.o_words), (const uint32_t*)p.words.data(),
+                       (int64_t)p.words.size(), s), "upload tables");
+  HIP_TRY(upload_words((uint32_t*)(w + p.o_rowoff), (const uint32_t*)p.mel_row_off.data(),
+                       2 * (int64_t)B, s), "upload tables");
+  const int32_t* cuT = (const int32_t*)(w + p.o_words);
+  const int32_t* cuT1 = cuT + (B + 1);
+  const int32_t* cuT2 = cuT1 + (B + 1);
+  const int32_t* cuN = cuT2 + (B + 1);
+  const int32_t* cuW = cuN + (B + 1);
+  void* act1 = w + p.o_act1;
+  void* act2 = w + p.o_act2;
+  void* act3 = w + p.o_act3;
+  float* x = (float*)(w + p.o_x);
+  void* h = w + p.o_h;
+  void* qkv = w + p.o_qkv;
+  void* att = w + p.o_att;
+  void* ffn = w + p.o_ffn;
+  void* ybuf = w + p.o_y;
+  void* ahid = w + p.o_ahid;
+
+  // ---- front-end
+  Conv1Args c1;
+  c1.mel = mel;
+  c1.mel_row_off = (const int64_t*)(w + p.o_rowoff);
+  c1.cu_T = cuT;
+  c1.cu_T1 = cuT1;
+  c1.nseq = B;
+  c1.total_T1 = p.sumT1;
+  c1.w = enc->conv1_w;
+  c1.b = enc->conv1_b;
+  c1.out = act1;
+  c1.C = C;
+  c1.bf16 = dt;
+  STAGE(launch_conv1(c1, s), "conv1");
+
+  GemmArgs g = gemm(act1, 0, enc->conv2_w, 9 * C, (int)(p.sumT2 * 32), C, 9 * C, enc->conv2_b, act2, C);
+  g.conv_C = C;
+  g.conv_Fin = 64;
+  g.conv_Fout = 32;
+  g.cu_in = cuT1;
+  g.cu_out = cuT2;
+  g.nseq = B;
+  STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv2");
+  g = gemm(act2, 0, enc->conv3_w, 9 * C, (int)(p.M * 16), C, 9 * C, enc->conv3_b, act3, C);
+  g.conv_C = C;
+  g.conv_Fin = 32;
+  g.conv_Fout = 16;
+  g.cu_in = cuT2;
+  g.cu_out = cuN;
+  g.nseq = B;
+  STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv3");
+  g = gemm(act3, 16 * C, enc->conv_out_w, 16 * C, M, D, 16 * C, nullptr, x, D);
+  g.cu_rows = cuN;
+  g.nseq = B;
+  STAGE(launch_gemm(g, EPI_PE, dt, false, s), "conv_out");
+
+  // ---- tower
+  AttnArgs aa;
+  aa.qkv = qkv;
+  aa.out = att;
+  aa.cu_rows = cuN;
+  aa.cu_win = cuW;
+  aa.nseq = B;
+  aa.n_windows = (int)p.n_windows;
+  aa.window = window;
+  aa.n_heads = c.n_heads;
+  aa.D = D;
+  aa.wpad = p.wpad;
+  const int lnm = dt ? 1 : 0;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& L = enc->layers[l];
+    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, lnm, s), "ln1");
+    STAGE(launch_gemm(gemm(h, D, L.wqkv, D, M, 3 * D, D, L.bqkv, qkv, 3 * D), EPI_ACT, dt, false, s), "qkv");
+    STAGE(launch_attention(aa, dt, s), "attn");
+    STAGE(launch_gemm(gemm(att, D, L.wo, D, M, D, D, L.bo, x, D), EPI_RESID, dt, false, s), "o");
+    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, lnm, s), "ln2");
+    STAGE(launch_gemm(gemm(h, D, L.w1, D, M, F, D, L.b1, ffn, F), EPI_GELU, dt, false, s), "fc1");
+    STAGE(launch_gemm(gemm(ffn, F, L.w2, F, M, D, F, L.b2, x, D), EPI_RESID, dt, false, s), "fc2");
+  }
+
+  // ---- head / output
+  const int64_t stride = p.out_stride;
+  int out_d = D;
+  if (!c.with_head) {
+    STAGE(launch_copy_rows(x, out, M, D, cuN, B, stride, s), "copy_rows");
+  } else {
+    out_d = O;
+    const int KD = dt ? 2 * D : D;
+    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt ? 2 : 0, s), "ln_post");
+    STAGE(launch_gemm(gemm(h, KD, enc->wp1, KD, M, D, KD, enc->bp1, ffn, KD),
+                        dt ? EPI_GELU_SPLIT : EPI_GELU, dt, false, s), "proj1");
+    GemmArgs g2 = gemm(ffn, KD, enc->wp2, KD, M, O, KD, enc->bp2, A ? ybuf : (void*)out, O);
+    g2.cu_rows = cuN;
+    g2.nseq = B;
+    g2.out_seq_stride = A ? 0 : stride;
+    STAGE(launch_gemm(g2, A ? EPI_ACT : EPI_OUT, dt, false, s), "proj2");
+    if (A) {
+      STAGE(launch_gemm(gemm(ybuf, O, enc->wgu, O, M, 2 * A, O, nullptr, ahid, A), EPI_SWIGLU, dt,
+                          false, s), "adapter_gu");
+      GemmArgs g3 = gemm(ahid, A, enc->wd, A, M, O, A, nullptr, out, O);
+      g3.cu_rows = cuN;
+      g3.nseq = B;
+      g3.out_seq_stride = stride;
+      STAGE(launch_gemm(g3, EPI_OUT, dt, false, s), "adapter_down");
+    }
+  }
+  if (stride > 0) STAGE(launch_zero_pad_rows(out, cuN, B, stride, out_d, s), "zero_pad");
+  return MT_OK;
+}
+
+}  // extern "C"

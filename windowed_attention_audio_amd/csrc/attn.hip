@@ -1,0 +1,219 @@
+// Block-diagonal (windowed) self-attention on the matrix cores.
+//
+// Model card "MOSS-Transcribe-preview-2B-GGUF", Architecture table, Audio
+// encoder row: 20 heads of 64 with windowed, block-diagonal attention.  The
+// encoder frames [kW, min((k+1)W, N)) of each sequence form window k; a row
+// attends only to the rows of its own window: o = softmax(q k^T / 8) v.
+//
+// One workgroup per (window, head).  The window's K (row-major) and V
+// (transposed, d-major) are staged in LDS once; each wavefront then takes
+// groups of 16 query rows and walks the keys in chunks of 64 with an online
+// softmax (running max and sum in fp32 registers).  Scores are computed
+// transposed, S^T = K Q^T, so that every lane owns one query row (its lane
+// index mod 16): the row statistics need only two cross-lane steps, and the
+// probabilities already sit where the next product, O^T = V^T P^T, wants its
+// second operand.  For bf16 the keys of each 32-wide step are stored in V^T
+// in the order in which a lane holds its probabilities, so each operand
+// fragment is one 16-byte LDS read.
+#include "common.h"
+#include "kernels.h"
+
+namespace mt {
+
+namespace {
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// position of key kv inside a V^T row (bf16: permuted within 32-key blocks)
+template <typename T>
+__device__ __forceinline__ int vt_pos(int kv) {
+  if constexpr (sizeof(T) == 2) {
+    const int u = kv >> 5, h = (kv >> 4) & 1, g = (kv >> 2) & 3, j = kv & 3;
+    return (u << 5) | (g << 3) | (h << 2) | j;
+  } else {
+    return kv;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
+  constexpr int HD = 64;
+  constexpr int EPC = Elem<T>::per16;      // elements per 16-byte chunk
+  constexpr int CPR = HD / EPC;            // chunks per K row
+  extern __shared__ uint4 smem[];
+  const int wpad = a.wpad;
+  uint4* Ks = smem;                                   // [wpad][CPR] chunks
+  T* Vt = (T*)(smem + wpad * CPR);                    // [HD][vstride]
+  const int vstride = wpad + 16 / (int)sizeof(T);     // +16 bytes per row
+
+  const int win = blockIdx.x;
+  const int head = blockIdx.y;
+  const int sq = find_seq(a.cu_win, a.nseq, win);
+  const int kwin = win - a.cu_win[sq];
+  const int N = a.cu_rows[sq + 1] - a.cu_rows[sq];
+  const int s0 = a.cu_rows[sq] + kwin * a.window;
+  const int w = min(a.window, N - kwin * a.window);
+  const int64_t ld = 3 * (int64_t)a.D;
+  const T* qkv = (const T*)a.qkv;
+  const T* Qg = qkv + (int64_t)s0 * ld + head * HD;
+  const T* Kg = Qg + a.D;
+  const T* Vg = Qg + 2 * a.D;
+
+  // ---- stage K and V^T (rows >= w are zero)
+  for (int idx = threadIdx.x; idx < wpad * CPR; idx += 256) {
+    const int kv = idx / CPR, c = idx - kv * CPR;
+    uint4 kvec = make_uint4(0, 0, 0, 0), vvec = make_uint4(0, 0, 0, 0);
+    if (kv < w) {
+      kvec = *(const uint4*)(Kg + (int64_t)kv * ld + c * EPC);
+      vvec = *(const uint4*)(Vg + (int64_t)kv * ld + c * EPC);
+    }
+    Ks[kv * CPR + (c ^ swz(kv))] = kvec;
+    const T* ve = (const T*)&vvec;
+    const int p = vt_pos<T>(kv);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) Vt[(c * EPC + e) * vstride + p] = ve[e];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+  const int nqg = (w + 15) >> 4;
+  const int nkc = (w + 63) >> 6;
+
+  for (int qg = wave; qg < nqg; qg += 4) {
+    const int q = qg * 16 + l16;  // this lane's query row (window-local)
+    // Q fragments: k-chunks (4s + g) of row q
+    constexpr int QS = CPR / 4;
+    uint4 qf[QS];
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      qf[s] = make_uint4(0, 0, 0, 0);
+      if (q < w) qf[s] = *(const uint4*)(Qg + (int64_t)q * ld + (4 * s + g) * EPC);
+    }
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4 o[4];
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kc = 0; kc < nkc; ++kc) {
+      f32x4 st[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int kvr = kc * 64 + t * 16 + l16;
+#pragma unroll
+        for (int s = 0; s < QS; ++s) {
+          const int cc = 4 * s + g;
+          const uint4 kf = Ks[kvr * CPR + (cc ^ swz(kvr))];
+          if constexpr (sizeof(T) == 2) {
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                           __builtin_bit_cast(bf16x8, qf[s]), st[t],
+                                                           0, 0, 0);
+          } else {
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.x), __uint_as_float(qf[s].x), st[t], 0, 0, 0);
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.y), __uint_as_float(qf[s].y), st[t], 0, 0, 0);
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.z), __uint_as_float(qf[s].z), st[t], 0, 0, 0);
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.w), __uint_as_float(qf[s].w), st[t], 0, 0, 0);
+          }
+        }
+      }
+      // lane holds S^T[kv = kc*64 + 16t + 4g + e][q]; scale, mask, row max
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kv = kc * 64 + t * 16 + 4 * g + e;
+          const float v = kv < w ? st[t][e] * sl2 : -INFINITY;
+          st[t][e] = v;
+          cmax = fmaxf(cmax, v);
+        }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2f(st[t][e] - m_new);
+          st[t][e] = p;
+          psum += p;
+        }
+      l_part = l_part * alpha + psum;
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
+
+      // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) {
+        const T* vrow = Vt + (nd * 16 + l16) * vstride + kc * 64;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint4 vf = *(const uint4*)(vrow + 32 * u + 8 * g);
+            uint4 pf;
+            pf.x = (uint32_t)f2bf(st[2 * u][0]) | ((uint32_t)f2bf(st[2 * u][1]) << 16);
+            pf.y = (uint32_t)f2bf(st[2 * u][2]) | ((uint32_t)f2bf(st[2 * u][3]) << 16);
+            pf.z = (uint32_t)f2bf(st[2 * u + 1][0]) | ((uint32_t)f2bf(st[2 * u + 1][1]) << 16);
+            pf.w = (uint32_t)f2bf(st[2 * u + 1][2]) | ((uint32_t)f2bf(st[2 * u + 1][3]) << 16);
+            o[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf),
+                                                           __builtin_bit_cast(bf16x8, pf), o[nd], 0,
+                                                           0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float4 vf = *(const float4*)(vrow + 16 * t + 4 * g);
+            o[nd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.x, st[t][0], o[nd], 0, 0, 0);
+            o[nd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.y, st[t][1], o[nd], 0, 0, 0);
+            o[nd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.z, st[t][2], o[nd], 0, 0, 0);
+            o[nd] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.w, st[t][3], o[nd], 0, 0, 0);
+          }
+        }
+      }
+    }
+    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (q < w) {
+      T* orow = (T*)a.out + (int64_t)(s0 + q) * a.D + head * HD;
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) {
+        const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
+        if constexpr (sizeof(T) == 2) {
+          uint2 pk;
+          pk.x = (uint32_t)f2bf(o[nd][0] * inv) | ((uint32_t)f2bf(o[nd][1] * inv) << 16);
+          pk.y = (uint32_t)f2bf(o[nd][2] * inv) | ((uint32_t)f2bf(o[nd][3] * inv) << 16);
+          *(uint2*)(orow + d0) = pk;
+        } else {
+          *(float4*)(orow + d0) =
+              make_float4(o[nd][0] * inv, o[nd][1] * inv, o[nd][2] * inv, o[nd][3] * inv);
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t run_attn(const AttnArgs& a, hipStream_t s) {
+  if (a.n_windows == 0) return hipSuccess;
+  const size_t lds = (size_t)a.wpad * 64 * sizeof(T) + (size_t)64 * (a.wpad * sizeof(T) + 16);
+  hipError_t e = hipFuncSetAttribute((const void*)wattn_kernel<T>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(wattn_kernel<T>, dim3(a.n_windows, a.n_heads), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
+  return dtype == 1 ? run_attn<bf16_t>(a, s) : run_attn<float>(a, s);
+}
+
+}  // namespace mt

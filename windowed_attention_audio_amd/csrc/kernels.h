@@ -1,0 +1,122 @@
+// Host-side launchers of the HIP kernels.  Every launcher enqueues work on
+// `s` and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mt {
+
+// ---------------------------------------------------------------- tables
+// Copies n 32-bit words from host memory into device memory through kernel
+// arguments (graph-capturable, no host buffer needs to outlive the call).
+hipError_t upload_words(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- log-mel
+struct MelArgs {
+  const float* wav;
+  float* mel;
+  const int64_t* seq_sample_off;  // [B]  first sample of sequence i in wav
+  const int32_t* seq_len;         // [B]  samples n_i
+  const int32_t* cu_frames;       // [B+1] prefix of T_i (packed frame numbering)
+  const int64_t* seq_row_off;     // [B]  output row of frame 0 of sequence i
+  int* gmax;                      // [B]  ordered-int keys of each clip's max
+  int nseq;
+  int64_t total_frames;
+  int64_t out_rows;               // rows of the mel output (padded: B * Tmax)
+  int padded;
+};
+hipError_t launch_mel(const MelArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- conv1
+struct Conv1Args {
+  const float* mel;          // normalised log-mel rows
+  const int64_t* mel_row_off;  // [B] row of frame 0 of sequence i
+  const int32_t* cu_T;       // [B+1] mel frames prefix
+  const int32_t* cu_T1;      // [B+1] conv1 output rows prefix
+  int nseq;
+  int64_t total_T1;
+  const float* w;            // [C][9] (tap = df*3 + dt)
+  const float* b;            // [C]
+  void* out;                 // [sum T1][64][C] channels-last, bf16 or f32
+  int C;
+  int bf16;
+};
+hipError_t launch_conv1(const Conv1Args& a, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+enum Epi : int {
+  EPI_F32 = 0,         // C (fp32) = acc (+ bias)
+  EPI_ACT = 1,         // C (T) = acc + bias
+  EPI_GELU = 2,        // C (T) = GELU(acc + bias)
+  EPI_GELU_SPLIT = 3,  // C (bf16) [row][col] = hi, [row][N + col] = lo of GELU(acc + bias)
+  EPI_RESID = 4,       // C (fp32) += acc + bias
+  EPI_PE = 5,          // C (fp32) = acc + sinusoid(position of row, col)
+  EPI_SWIGLU = 6,      // C (T) [row][f] = SiLU(gate) * up (gate/up interleaved by 16)
+  EPI_OUT = 7,         // C (fp32) [mapped row][col] = acc (+ bias)
+};
+
+struct GemmArgs {
+  const void* A;
+  int64_t lda;  // elements
+  const void* B;
+  int64_t ldb;  // elements; B is [N][K] row-major
+  int M, N, K;
+  const float* bias;
+  void* C;
+  int64_t ldc;
+  // implicit-GEMM convolution (A gathered from a channels-last activation)
+  int conv_C, conv_Fin, conv_Fout;
+  const int32_t* cu_in;   // [nseq+1] input time rows prefix
+  const int32_t* cu_out;  // [nseq+1] output time rows prefix
+  int nseq;
+  // row -> sequence position (EPI_PE, EPI_OUT)
+  const int32_t* cu_rows;  // [nseq+1]
+  int64_t out_seq_stride;  // EPI_OUT padded: rows per sequence (0 = packed)
+};
+
+// dtype: 0 = fp32 operands, 1 = bf16 operands.  conv: gather A as a 3x3
+// stride-2 convolution input.
+hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStream_t s);
+
+// ---------------------------------------------------------------- LayerNorm
+// out = LN(x) * g + b per row of D fp32 values.  mode 0: T = fp32, 1: bf16,
+// 2: bf16 hi/lo split written as [row][2D].
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D,
+                            float eps, int mode, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* qkv;  // [M][3D] (q | k | v), head h at columns h*64 .. h*64+63
+  void* out;        // [M][D]
+  const int32_t* cu_rows;  // [nseq+1]
+  const int32_t* cu_win;   // [nseq+1] prefix of window counts
+  int nseq;
+  int n_windows;
+  int window;
+  int n_heads;
+  int D;
+  int wpad;  // longest window rounded up to 64 (K/V rows held on chip, zero-filled)
+};
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- misc
+// Second log-mel pass: clamp at each clip's maximum - 8, then (x + 4) / 4;
+// padded rows beyond a clip are zeroed.  tmax = padded rows per sequence.
+hipError_t launch_mel_norm(const MelArgs& a, int64_t tmax, hipStream_t s);
+hipError_t launch_fill_i32(int* p, int v, int64_t n, hipStream_t s);
+hipError_t launch_zero_pad_rows(float* out, const int32_t* cu_rows, int nseq, int64_t seq_stride,
+                                int D, hipStream_t s);
+hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int32_t* cu_rows,
+                            int nseq, int64_t stride, hipStream_t s);
+// Weight repacking (fp32 masters -> kernel layouts).
+hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
+                          int64_t dst_col0, int bf16, hipStream_t s);
+hipError_t launch_pack_conv(const float* w, void* dst, int C, int bf16, hipStream_t s);
+hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int bf16,
+                                hipStream_t s);
+hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int bf16,
+                              hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+}  // namespace mt

@@ -1,0 +1,221 @@
+// Small kernels: table upload, fills, the log-mel clamp pass, row copies and
+// the one-time weight repacking.
+#include "common.h"
+#include "kernels.h"
+
+namespace mt {
+
+namespace {
+
+constexpr int BLOB_WORDS = 960;
+struct Blob {
+  int32_t n;
+  uint32_t w[BLOB_WORDS];
+};
+
+__global__ void words_kernel(uint32_t* __restrict__ dst, Blob b) {
+  for (int i = threadIdx.x; i < b.n; i += blockDim.x) dst[i] = b.w[i];
+}
+
+__global__ void fill_i32_kernel(int* p, int v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// Log-mel clamp: y = (max(x, g - 8) + 4) / 4 with g the clip's maximum;
+// padded rows beyond a clip are set to 0.  One float4 per thread.
+__global__ void mel_norm_kernel(MelArgs a, int64_t tmax) {
+  const int64_t i4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i4 >= a.out_rows * 32) return;
+  const int64_t row = i4 >> 5;
+  int sq;
+  bool valid;
+  if (a.padded) {
+    sq = (int)(row / tmax);
+    const int64_t t = row - sq * tmax;
+    valid = t < (int64_t)(a.cu_frames[sq + 1] - a.cu_frames[sq]);
+  } else {
+    sq = find_seq(a.cu_frames, a.nseq, (int)row);
+    valid = true;
+  }
+  float4* p = (float4*)a.mel + i4;
+  if (!valid) {
+    *p = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const float lo = key_float(a.gmax[sq]) - 8.0f;
+  float4 v = *p;
+  v.x = (fmaxf(v.x, lo) + 4.0f) * 0.25f;
+  v.y = (fmaxf(v.y, lo) + 4.0f) * 0.25f;
+  v.z = (fmaxf(v.z, lo) + 4.0f) * 0.25f;
+  v.w = (fmaxf(v.w, lo) + 4.0f) * 0.25f;
+  *p = v;
+}
+
+// Rows >= N_i of each padded output sequence are set to 0.
+__global__ void zero_pad_kernel(float* out, const int32_t* cu_rows, int64_t stride, int D) {
+  const int sq = blockIdx.y;
+  const int n = cu_rows[sq + 1] - cu_rows[sq];
+  const int64_t cnt = (stride - n) * (int64_t)D;
+  float* base = out + ((int64_t)sq * stride + n) * D;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cnt;
+       i += (int64_t)gridDim.x * blockDim.x)
+    base[i] = 0.f;
+}
+
+// Copy packed rows [M][D] into packed or padded output rows.
+__global__ void copy_rows_kernel(const float* __restrict__ x, float* __restrict__ out, int M, int D,
+                                 const int32_t* cu_rows, int nseq, int64_t stride) {
+  const int row = blockIdx.x;
+  int64_t orow = row;
+  if (stride > 0) {
+    const int sq = find_seq(cu_rows, nseq, row);
+    orow = (int64_t)sq * stride + (row - cu_rows[sq]);
+  }
+  for (int c = threadIdx.x; c < D; c += blockDim.x) out[orow * D + c] = x[(int64_t)row * D + c];
+}
+
+__device__ __forceinline__ void put(void* dst, int64_t i, float v, int bf16) {
+  if (bf16) ((bf16_t*)dst)[i] = f2bf(v);
+  else ((float*)dst)[i] = v;
+}
+
+// dst[r * dst_ld + col0 + c] = src[r * cols + c]
+__global__ void convert_kernel(const float* __restrict__ src, void* dst, int64_t rows, int64_t cols,
+                               int64_t dst_ld, int64_t col0, int bf16) {
+  const int64_t n = rows * cols;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols, c = i - r * cols;
+    put(dst, r * dst_ld + col0 + c, src[i], bf16);
+  }
+}
+
+// conv [C][C][3][3] -> [C][9C], column (df * 3 + dt) * C + ci
+__global__ void pack_conv_kernel(const float* __restrict__ w, void* dst, int C, int bf16) {
+  const int64_t n = (int64_t)C * C * 9;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t co = i / (9LL * C);
+    const int64_t rem = i - co * 9LL * C;
+    const int tap = (int)(rem / C), ci = (int)(rem - (int64_t)tap * C);
+    put(dst, i, w[((co * C + ci) * 9) + tap], bf16);
+  }
+}
+
+// conv_out [D][C*F] (column c*F + f) -> [D][F*C] (column f*C + c), matching the
+// channels-last [t][f][c] output of the last convolution.
+__global__ void pack_conv_out_kernel(const float* __restrict__ w, void* dst, int D, int C, int F,
+                                     int bf16) {
+  const int64_t n = (int64_t)D * C * F;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t d = i / ((int64_t)C * F);
+    const int rem = (int)(i - d * C * F);
+    const int f = rem / C, c = rem - f * C;
+    put(dst, i, w[d * C * F + (int64_t)c * F + f], bf16);
+  }
+}
+
+// gate/up [A][O] -> [2A][O], rows interleaved in blocks of 16 (16 gate rows,
+// then the 16 up rows of the same features).
+__global__ void pack_swiglu_kernel(const float* __restrict__ gate, const float* __restrict__ up,
+                                   void* dst, int A, int O, int bf16) {
+  const int64_t n = 2LL * A * O;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / O, c = i - r * O;
+    const int64_t p = r >> 5, q = r & 31;
+    const float v = q < 16 ? gate[(p * 16 + q) * O + c] : up[(p * 16 + q - 16) * O + c];
+    put(dst, i, v, bf16);
+  }
+}
+
+__global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+inline dim3 grid_for(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return dim3((unsigned)b);
+}
+
+}  // namespace
+
+hipError_t upload_words(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s) {
+  for (int64_t off = 0; off < n; off += BLOB_WORDS) {
+    Blob b;
+    b.n = (int32_t)((n - off) < BLOB_WORDS ? (n - off) : BLOB_WORDS);
+    for (int i = 0; i < b.n; ++i) b.w[i] = src[off + i];
+    hipLaunchKernelGGL(words_kernel, dim3(1), dim3(256), 0, s, dst + off, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_fill_i32(int* p, int v, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, grid_for(n), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_mel_norm(const MelArgs& a, int64_t tmax, hipStream_t s) {
+  const int64_t n = a.out_rows * 32;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mel_norm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, tmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_pad_rows(float* out, const int32_t* cu_rows, int nseq, int64_t stride, int D,
+                                hipStream_t s) {
+  if (nseq == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_pad_kernel, dim3(64, nseq), dim3(256), 0, s, out, cu_rows, stride, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int32_t* cu_rows,
+                            int nseq, int64_t stride, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(M), dim3(256), 0, s, x, out, M, D, cu_rows, nseq, stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
+                          int64_t dst_col0, int bf16, hipStream_t s) {
+  hipLaunchKernelGGL(convert_kernel, grid_for(rows * cols), dim3(256), 0, s, src, dst, rows, cols,
+                     dst_ld, dst_col0, bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_conv(const float* w, void* dst, int C, int bf16, hipStream_t s) {
+  hipLaunchKernelGGL(pack_conv_kernel, grid_for(9LL * C * C), dim3(256), 0, s, w, dst, C, bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int bf16,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(pack_conv_out_kernel, grid_for((int64_t)D * C * F), dim3(256), 0, s, w, dst, D,
+                     C, F, bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int bf16,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(pack_swiglu_kernel, grid_for(2LL * A * O), dim3(256), 0, s, gate, up, dst, A,
+                     O, bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, grid_for(n), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace mt

@@ -1,0 +1,108 @@
+// LayerNorm over the fp32 residual stream: one wavefront per row.
+//
+// Pre-LN layers and ln_post (model card "MOSS-Transcribe-preview-2B-GGUF",
+// Architecture table, Audio encoder and Encoder head rows): y = (x - mean) /
+// sqrt(var + eps) * g + b with the biased variance, statistics in fp32.
+// A row of D = 256 * VEC floats is held in registers (VEC float4 per lane);
+// mean and variance are two wavefront reductions over the register copy, so
+// the row is read from memory once.
+#include "common.h"
+#include "kernels.h"
+
+namespace mt {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int VEC, int MODE>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x,
+                                                        const float* __restrict__ g,
+                                                        const float* __restrict__ b,
+                                                        void* __restrict__ out, int M, float eps) {
+  constexpr int D = 256 * VEC;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float4* xr = (const float4*)(x + (int64_t)row * D);
+  float4 v[VEC];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    v[i] = xr[lane + 64 * i];
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  const float mean = wave_sum(s) * (1.0f / D);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+    q += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + eps);
+  const float4* g4 = (const float4*)g;
+  const float4* b4 = (const float4*)b;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    const int c4 = lane + 64 * i;
+    const float4 gg = g4[c4], bb = b4[c4];
+    float4 y;
+    y.x = (v[i].x - mean) * rstd * gg.x + bb.x;
+    y.y = (v[i].y - mean) * rstd * gg.y + bb.y;
+    y.z = (v[i].z - mean) * rstd * gg.z + bb.z;
+    y.w = (v[i].w - mean) * rstd * gg.w + bb.w;
+    if constexpr (MODE == 0) {
+      ((float4*)out)[(int64_t)row * (D / 4) + c4] = y;
+    } else {
+      const bf16_t h0 = f2bf(y.x), h1 = f2bf(y.y), h2 = f2bf(y.z), h3 = f2bf(y.w);
+      uint2 hi;
+      hi.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+      if constexpr (MODE == 1) {
+        ((uint2*)out)[(int64_t)row * (D / 4) + c4] = hi;
+      } else {
+        const bf16_t l0 = f2bf(y.x - bf2f(h0)), l1 = f2bf(y.y - bf2f(h1));
+        const bf16_t l2 = f2bf(y.z - bf2f(h2)), l3 = f2bf(y.w - bf2f(h3));
+        uint2 lo;
+        lo.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        lo.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+        ((uint2*)out)[(int64_t)row * (D / 2) + c4] = hi;
+        ((uint2*)out)[(int64_t)row * (D / 2) + D / 4 + c4] = lo;
+      }
+    }
+  }
+}
+
+template <int VEC>
+hipError_t ln_mode(const float* x, const float* g, const float* b, void* out, int M, float eps,
+                   int mode, hipStream_t s) {
+  const dim3 grid((M + 3) / 4), block(256);
+  if (M == 0) return hipSuccess;
+  if (mode == 0) hipLaunchKernelGGL((layernorm_kernel<VEC, 0>), grid, block, 0, s, x, g, b, out, M, eps);
+  else if (mode == 1) hipLaunchKernelGGL((layernorm_kernel<VEC, 1>), grid, block, 0, s, x, g, b, out, M, eps);
+  else hipLaunchKernelGGL((layernorm_kernel<VEC, 2>), grid, block, 0, s, x, g, b, out, M, eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D,
+                            float eps, int mode, hipStream_t s) {
+  switch (D / 256) {
+    case 1: return ln_mode<1>(x, g, b, out, M, eps, mode, s);
+    case 2: return ln_mode<2>(x, g, b, out, M, eps, mode, s);
+    case 3: return ln_mode<3>(x, g, b, out, M, eps, mode, s);
+    case 4: return ln_mode<4>(x, g, b, out, M, eps, mode, s);
+    case 5: return ln_mode<5>(x, g, b, out, M, eps, mode, s);
+    case 6: return ln_mode<6>(x, g, b, out, M, eps, mode, s);
+    case 7: return ln_mode<7>(x, g, b, out, M, eps, mode, s);
+    case 8: return ln_mode<8>(x, g, b, out, M, eps, mode, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mt
