@@ -79,7 +79,7 @@ def conv3x3_s2(img, w, b):
     for di in range(3):
         for dj in range(3):
             tap = xp[:, di:di + 2 * Ho:2, dj:dj + 2 * Wo:2].reshape(C, Ho * Wo)
-            y += w[:, :, di, dj] @ tap
+            y += np.ascontiguousarray(w[:, :, di, dj]) @ tap
     return y.reshape(O, Ho, Wo)
 
 
