@@ -3,8 +3,10 @@
 A step is one pass of the whole forward path over one batch: waveform ->
 log-mel (mt_logmel) -> conv front-end, 32 windowed-attention layers and the
 encoder head (mt_encode).  The workload is 16 clips of 30 s of synthetic
-16 kHz audio (sum of three tones plus noise, 20 % silent gaps), bf16 weights
-and matrix operands with fp32 accumulation, window 104 encoder frames.
+16 kHz audio (sum of three tones plus noise, 20 % silent gaps), bf16-valued
+weights, fp16 matrix operands with fp32 accumulation (the 16-bit operand type
+that meets the parity bar; bf16 operands are selectable with --operands bf16),
+window 104 encoder frames.
 Inputs are resident in device memory before the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -25,7 +27,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
 
@@ -85,6 +87,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -108,7 +111,8 @@ def main():
     window = wl.window
 
     dev_w = [torch.from_numpy(v).cuda() for v in weights.values()]
-    enc = W.mt_encoder_create(W.encoder_config(geom, W.MT_BF16), dev_w)
+    op_dt = W.MT_F16 if args.operands == "f16" else W.MT_BF16
+    enc = W.mt_encoder_create(W.encoder_config(geom, op_dt), dev_w)
     torch.cuda.synchronize()
     del dev_w
     wav = torch.from_numpy(np.concatenate(clips)).cuda()
@@ -176,9 +180,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.operands,
         "data": "synthetic (seeded tones + noise + silent gaps; seeded random weights)",
         "config": {"workload": wl.name, "clips": len(lens), "clip_seconds": 30, "window": window,
+                   "weights": "bf16 values", "operands": args.operands, "accumulate": "f32",
                    "mel_frames": sum(lens_T), "encoder_frames": M, "layers": geom["n_layers"]},
         "mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "step_tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),

@@ -46,7 +46,16 @@ typedef enum {
   MT_ERR_HIP = 4          /* a HIP runtime call failed */
 } mt_status;
 
-typedef enum { MT_F32 = 0, MT_BF16 = 1 } mt_dtype;
+/* Compute type of the matrix operands (accumulation is fp32 in every case;
+ * the residual stream, LayerNorm statistics, softmax and epilogues are fp32).
+ *   MT_F32   fp32 operands everywhere;
+ *   MT_BF16  bf16 weights and activations at the matrix cores;
+ *   MT_F16   fp16 weights and activations at the matrix cores (weights given
+ *            as bf16 values are held exactly in fp16 unless |w| < 2^-17,
+ *            which moves by at most 2^-25; activations saturate at +-65504).
+ * With 16-bit operands the head's activations enter its two products as
+ * hi/lo pairs of the operand type. */
+typedef enum { MT_F32 = 0, MT_BF16 = 1, MT_F16 = 2 } mt_dtype;
 
 typedef enum {
   MT_PACKED = 0, /* sequences stored back to back, no padding */
@@ -80,9 +89,7 @@ typedef struct {
   int32_t d_ffn;
   int32_t d_out;
   int32_t adapter_hidden; /* 0: no adapter */
-  int32_t dtype;          /* mt_dtype: MT_F32 = fp32 everywhere; MT_BF16 = bf16
-                             weights and matrix operands, fp32 accumulation,
-                             fp32 residual stream, statistics and softmax */
+  int32_t dtype;          /* mt_dtype */
   int32_t with_head;      /* 1: full output (d_out wide); 0: stop after the
                              tower and return the fp32 residual stream
                              (d_model wide) */
@@ -140,7 +147,7 @@ mt_status mt_encoder_packed_bytes(const mt_encoder_config* cfg, size_t* bytes);
  *   adapter only: gate.weight [A,O], up.weight [A,O], down.weight [O,A].
  * Feature j of conv_out's input is conv3 channel j / 16 at frequency j % 16.
  * `packed` (device, >= mt_encoder_packed_bytes, 256-byte aligned) receives
- * the weights in kernel layouts (bf16 rounded to nearest-even for MT_BF16);
+ * the weights in kernel layouts (rounded to nearest-even for 16-bit types);
  * it must stay alive and unchanged until mt_encoder_destroy.  The source
  * tensors may be freed once the repacking work on `stream` has completed. */
 mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* weights,

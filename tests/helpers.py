@@ -3,7 +3,8 @@
 Tolerances (the parity bar of this encoder):
   log-mel            max |gpu - oracle| <= 1e-4 over every valid entry
   fp32 encoder       per row ||gpu - ref|| / ||ref|| <= 1e-3
-  bf16 encoder       per row cosine >= 0.999 and max |gpu - ref| <= 0.02 * RMS(ref row)
+  16-bit encoder     per row cosine >= 0.999 and max |gpu - ref| <= 0.02 * RMS(ref row)
+                     (bf16-valued weights; matrix operands fp16 or bf16)
 Padded rows must be exactly zero.
 """
 
@@ -51,7 +52,7 @@ class GpuModel:
         import windowed_attention_audio_amd as W
         self.W = W
         self.geom = geom
-        self.dt = W.MT_BF16 if dtype_name == "bf16" else W.MT_F32
+        self.dt = {"bf16": W.MT_BF16, "f16": W.MT_F16, "f32": W.MT_F32}[dtype_name]
         self.cfg = W.encoder_config(geom, self.dt, with_head=with_head)
         self.dev_weights = [torch.from_numpy(np.ascontiguousarray(v)).cuda()
                             for v in weights.values()]

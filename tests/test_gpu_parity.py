@@ -115,10 +115,10 @@ def oracle_rows(mels, weights, geom, W, **kw):
     return [OE.encode_clip(m, P, geom, W, **kw) for m in mels]
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_front_end_only(dt, full_weights_f32, full_weights_bf16):
     geom = small_geom(0)
-    wts = sub_weights(full_weights_bf16 if dt == "bf16" else full_weights_f32, geom)
+    wts = sub_weights(full_weights_f32 if dt == "f32" else full_weights_bf16, geom)
     model = GpuModel(geom, dt, wts, with_head=False)
     rng = np.random.default_rng(1)
     mels = [rng.uniform(-1, 1.5, (T, 128)) for T in (100, 37, 8, 1)]
@@ -130,13 +130,13 @@ def test_front_end_only(dt, full_weights_f32, full_weights_bf16):
         if dt == "f32":
             assert_f32_rows(g, r, what="front-end f32")
         else:
-            assert_bf16_rows(g, r, what="front-end bf16")
+            assert_bf16_rows(g, r, what=f"front-end {dt}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_one_layer_random_ln(dt):
     geom = small_geom(1)
-    wts = synth.make_weights(geom, bf16=(dt == "bf16"), ln_random=True)
+    wts = synth.make_weights(geom, bf16=(dt != "f32"), ln_random=True)
     model = GpuModel(geom, dt, wts)
     rng = np.random.default_rng(2)
     mels = [rng.uniform(-1, 1.5, (T, 128)) for T in (300, 77, 1000)]
@@ -149,7 +149,7 @@ def test_one_layer_random_ln(dt):
             if dt == "f32":
                 assert_f32_rows(g, r, what=f"1 layer f32 W={W}")
             else:
-                assert_bf16_rows(g, r, what=f"1 layer bf16 W={W}")
+                assert_bf16_rows(g, r, what=f"1 layer {dt} W={W}")
 
 
 def test_c0_fp32_full(full_weights_f32):
@@ -164,13 +164,15 @@ def test_c0_fp32_full(full_weights_f32):
     say("  worst rel", m["rel"].max())
 
 
-def test_c1_bf16_full(full_weights_bf16):
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_c1_30s_full(full_weights_bf16, dt):
+    # bf16-valued weights; matrix operands fp16 (the default 16-bit type) or bf16
     w = synth.workload(1)
     mel = OL.log_mel(synth.make_clips(w)[0])
-    model = GpuModel(FULL, "bf16", full_weights_bf16)
-    say("c1 bf16 full")
+    model = GpuModel(FULL, dt, full_weights_bf16)
+    say("c1 30 s full,", dt, "operands")
     got = model.encode([mel], w.window)
     ref = oracle_rows([mel], full_weights_bf16, FULL, w.window)[0]
     assert got.shape == (375, 2048)
-    m = assert_bf16_rows(got, ref, what="c1")
+    m = assert_bf16_rows(got, ref, what=f"c1 {dt}")
     say("  min cos", m["cos"].min(), "max |d|/rms", m["maxabs_rms"].max())

@@ -50,7 +50,8 @@ def P64(weights_bf16):
 
 @pytest.fixture(scope="module")
 def model(weights_bf16):
-    return GpuModel(FULL, "bf16", weights_bf16)
+    # bf16-valued weights, fp16 matrix operands, fp32 accumulation
+    return GpuModel(FULL, "f16", weights_bf16)
 
 
 def test_batch16x30s_sampled(model, P64):
@@ -95,7 +96,7 @@ def test_varlen_packed_adapter_sampled(weights_bf16):
     wts = synth.make_weights(geom, bf16=True)
     for k in weights_bf16:  # the tower is shared with the other workloads
         assert np.array_equal(wts[k], weights_bf16[k])
-    ad = GpuModel(geom, "bf16", wts)
+    ad = GpuModel(geom, "f16", wts)
     clips = synth.make_clips(w)
     say("32 varlen clips + adapter, W=52")
     mel = gpu_logmel(clips)

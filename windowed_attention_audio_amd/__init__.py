@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmt.so")
 
 MT_OK, MT_ERR_INVALID_ARG, MT_ERR_UNSUPPORTED, MT_ERR_WORKSPACE, MT_ERR_HIP = range(5)
-MT_F32, MT_BF16 = 0, 1
+MT_F32, MT_BF16, MT_F16 = 0, 1, 2
 MT_PACKED, MT_PADDED = 0, 1
 
 EXPORTS = (

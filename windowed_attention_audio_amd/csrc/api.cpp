@@ -179,8 +179,8 @@ struct PackedLayout {
 
 mt_status check_config(const mt_encoder_config* c) {
   if (!c) return fail(MT_ERR_INVALID_ARG, "config is NULL");
-  if (c->dtype != MT_F32 && c->dtype != MT_BF16)
-    return fail(MT_ERR_INVALID_ARG, "dtype %d is neither MT_F32 nor MT_BF16", c->dtype);
+  if (c->dtype != MT_F32 && c->dtype != MT_BF16 && c->dtype != MT_F16)
+    return fail(MT_ERR_INVALID_ARG, "dtype %d is not MT_F32, MT_BF16 or MT_F16", c->dtype);
   if (c->n_layers < 0 || c->n_heads < 1 || c->head_dim < 1 || c->conv_ch < 1 || c->d_model < 1 ||
       c->d_ffn < 1 || c->d_out < 1 || c->adapter_hidden < 0 || c->n_mels < 1)
     return fail(MT_ERR_INVALID_ARG, "non-positive size in config");
@@ -203,9 +203,10 @@ mt_status check_config(const mt_encoder_config* c) {
 }
 
 PackedLayout packed_layout(const mt_encoder_config& c) {
-  const size_t es = c.dtype == MT_BF16 ? 2 : 4;
+  const bool half = c.dtype != MT_F32;
+  const size_t es = half ? 2 : 4;
   const size_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
-  const size_t KD = c.dtype == MT_BF16 ? 2 * D : D;  // hi/lo split head input
+  const size_t KD = half ? 2 * D : D;  // hi/lo split head input
   PackedLayout p;
   Carver k;
   p.conv1_w = k.take(C * 9 * 4);
@@ -260,7 +261,7 @@ struct EncPlan {
 
 struct mt_encoder {
   mt_encoder_config cfg;
-  int dt;     // 1 = bf16
+  int dt;     // element type of matrix operands (DT_F32, DT_BF16, DT_F16)
   size_t es;  // element bytes of matrix operands
   const float *conv1_w, *conv1_b, *conv2_b, *conv3_b;
   const void *conv2_w, *conv3_w, *conv_out_w;
@@ -322,12 +323,12 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   p.o_act3 = k.take(M * 16 * C * es);
   p.o_x = k.take(M * D * 4);
   size_t hb = M * D * es;
-  if (c.with_head && enc->dt == 1) hb = std::max(hb, M * 2 * D * 2);
+  if (c.with_head && enc->dt != DT_F32) hb = std::max(hb, M * 2 * D * 2);
   p.o_h = k.take(hb);
   p.o_qkv = k.take(M * 3 * D * es);
   p.o_att = k.take(M * D * es);
   size_t fb = M * F * es;
-  if (c.with_head) fb = std::max(fb, enc->dt == 1 ? M * 2 * D * 2 : M * D * 4);
+  if (c.with_head) fb = std::max(fb, enc->dt != DT_F32 ? M * 2 * D * 2 : M * D * 4);
   p.o_ffn = k.take(fb);
   p.o_y = k.take(A ? M * O * es : 0);
   p.o_ahid = k.take(A ? M * A * es : 0);
@@ -460,10 +461,11 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
     return fail(MT_ERR_WORKSPACE, "packed buffer %zu bytes < required %zu", packed_bytes, L.bytes);
 
   hipStream_t s = (hipStream_t)stream;
-  const int bf = c.dtype == MT_BF16;
+  const int bf = c.dtype == MT_BF16 ? DT_BF16 : c.dtype == MT_F16 ? DT_F16 : DT_F32;  // element type
+  const bool half = bf != DT_F32;
   char* P = (char*)packed;
   const int64_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
-  const size_t es = bf ? 2 : 4;
+  const size_t es = half ? 2 : 4;
   int wi = 0;
   auto next = [&]() { return wts[wi++]; };
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_w), C * 9, s), "pack conv1");
@@ -493,17 +495,17 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
   }
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.lnp_g), D, s), "pack ln_post");
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.lnp_b), D, s), "pack ln_post");
-  const int64_t KD = bf ? 2 * D : D;
+  const int64_t KD = half ? 2 * D : D;
   {
     const float* w = next();
     HIP_TRY(launch_convert(w, P + L.wp1, D, D, KD, 0, bf, s), "pack proj1");
-    if (bf) HIP_TRY(launch_convert(w, P + L.wp1, D, D, KD, D, bf, s), "pack proj1");
+    if (half) HIP_TRY(launch_convert(w, P + L.wp1, D, D, KD, D, bf, s), "pack proj1");
   }
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.bp1), D, s), "pack proj1 bias");
   {
     const float* w = next();
     HIP_TRY(launch_convert(w, P + L.wp2, O, D, KD, 0, bf, s), "pack proj2");
-    if (bf) HIP_TRY(launch_convert(w, P + L.wp2, O, D, KD, D, bf, s), "pack proj2");
+    if (half) HIP_TRY(launch_convert(w, P + L.wp2, O, D, KD, D, bf, s), "pack proj2");
   }
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.bp2), O, s), "pack proj2 bias");
   if (A) {
@@ -515,7 +517,7 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
 
   mt_encoder* e = new mt_encoder();
   e->cfg = c;
-  e->dt = bf;
+  e->dt = bf;  // DT_* code
   e->es = es;
   e->conv1_w = (const float*)(P + L.conv1_w);
   e->conv1_b = (const float*)(P + L.conv1_b);
@@ -649,7 +651,7 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
   c1.b = enc->conv1_b;
   c1.out = act1;
   c1.C = C;
-  c1.bf16 = dt;
+  c1.dtype = dt;
   STAGE(launch_conv1(c1, s), "conv1");
 
   GemmArgs g = gemm(act1, 0, enc->conv2_w, 9 * C, (int)(p.sumT2 * 32), C, 9 * C, enc->conv2_b, act2, C);
@@ -685,14 +687,14 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
   aa.n_heads = c.n_heads;
   aa.D = D;
   aa.wpad = p.wpad;
-  const int lnm = dt ? 1 : 0;
+  const bool half = dt != DT_F32;
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = enc->layers[l];
-    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, lnm, s), "ln1");
+    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, dt, false, s), "ln1");
     STAGE(launch_gemm(gemm(h, D, L.wqkv, D, M, 3 * D, D, L.bqkv, qkv, 3 * D), EPI_ACT, dt, false, s), "qkv");
     STAGE(launch_attention(aa, dt, s), "attn");
     STAGE(launch_gemm(gemm(att, D, L.wo, D, M, D, D, L.bo, x, D), EPI_RESID, dt, false, s), "o");
-    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, lnm, s), "ln2");
+    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, dt, false, s), "ln2");
     STAGE(launch_gemm(gemm(h, D, L.w1, D, M, F, D, L.b1, ffn, F), EPI_GELU, dt, false, s), "fc1");
     STAGE(launch_gemm(gemm(ffn, F, L.w2, F, M, D, F, L.b2, x, D), EPI_RESID, dt, false, s), "fc2");
   }
@@ -704,10 +706,11 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
     STAGE(launch_copy_rows(x, out, M, D, cuN, B, stride, s), "copy_rows");
   } else {
     out_d = O;
-    const int KD = dt ? 2 * D : D;
-    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt ? 2 : 0, s), "ln_post");
+    // 16-bit operands: the head's activations enter as hi/lo pairs (K doubled)
+    const int KD = half ? 2 * D : D;
+    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt, half, s), "ln_post");
     STAGE(launch_gemm(gemm(h, KD, enc->wp1, KD, M, D, KD, enc->bp1, ffn, KD),
-                        dt ? EPI_GELU_SPLIT : EPI_GELU, dt, false, s), "proj1");
+                        half ? EPI_GELU_SPLIT : EPI_GELU, dt, false, s), "proj1");
     GemmArgs g2 = gemm(ffn, KD, enc->wp2, KD, M, O, KD, enc->bp2, A ? ybuf : (void*)out, O);
     g2.cu_rows = cuN;
     g2.nseq = B;

@@ -8,11 +8,12 @@
 // One workgroup per (window, head).  The window's K (row-major) and V
 // (transposed, d-major) are staged in LDS once; each wavefront then takes
 // groups of 16 query rows and walks the keys in chunks of 64 with an online
-// softmax (running max and sum in fp32 registers).  Scores are computed
+// softmax (running max and sum in fp32 registers; probabilities enter the
+// second product in the operand type).  Scores are computed
 // transposed, S^T = K Q^T, so that every lane owns one query row (its lane
 // index mod 16): the row statistics need only two cross-lane steps, and the
 // probabilities already sit where the next product, O^T = V^T P^T, wants its
-// second operand.  For bf16 the keys of each 32-wide step are stored in V^T
+// second operand.  For 16-bit operands the keys of each 32-wide step are stored in V^T
 // in the order in which a lane holds its probabilities, so each operand
 // fragment is one 16-byte LDS read.
 #include "common.h"
@@ -107,16 +108,8 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
         for (int s = 0; s < QS; ++s) {
           const int cc = 4 * s + g;
           const uint4 kf = Ks[kvr * CPR + (cc ^ swz(kvr))];
-          if constexpr (sizeof(T) == 2) {
-            st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                           __builtin_bit_cast(bf16x8, qf[s]), st[t],
-                                                           0, 0, 0);
-          } else {
-            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.x), __uint_as_float(qf[s].x), st[t], 0, 0, 0);
-            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.y), __uint_as_float(qf[s].y), st[t], 0, 0, 0);
-            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.z), __uint_as_float(qf[s].z), st[t], 0, 0, 0);
-            st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.w), __uint_as_float(qf[s].w), st[t], 0, 0, 0);
-          }
+          if constexpr (sizeof(T) == 2) mma16(st[t], kf, qf[s], T{});
+          else mma_f32x4(st[t], kf, qf[s]);
         }
       }
       // lane holds S^T[kv = kc*64 + 16t + 4g + e][q]; scale, mask, row max
@@ -156,14 +149,13 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const uint4 vf = *(const uint4*)(vrow + 32 * u + 8 * g);
+            typedef Elem<T> E;
             uint4 pf;
-            pf.x = (uint32_t)f2bf(st[2 * u][0]) | ((uint32_t)f2bf(st[2 * u][1]) << 16);
-            pf.y = (uint32_t)f2bf(st[2 * u][2]) | ((uint32_t)f2bf(st[2 * u][3]) << 16);
-            pf.z = (uint32_t)f2bf(st[2 * u + 1][0]) | ((uint32_t)f2bf(st[2 * u + 1][1]) << 16);
-            pf.w = (uint32_t)f2bf(st[2 * u + 1][2]) | ((uint32_t)f2bf(st[2 * u + 1][3]) << 16);
-            o[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf),
-                                                           __builtin_bit_cast(bf16x8, pf), o[nd], 0,
-                                                           0, 0);
+            pf.x = pack2(E::from_f(st[2 * u][0]), E::from_f(st[2 * u][1]));
+            pf.y = pack2(E::from_f(st[2 * u][2]), E::from_f(st[2 * u][3]));
+            pf.z = pack2(E::from_f(st[2 * u + 1][0]), E::from_f(st[2 * u + 1][1]));
+            pf.w = pack2(E::from_f(st[2 * u + 1][2]), E::from_f(st[2 * u + 1][3]));
+            mma16(o[nd], vf, pf, T{});
           }
         } else {
 #pragma unroll
@@ -186,9 +178,10 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
       for (int nd = 0; nd < 4; ++nd) {
         const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
         if constexpr (sizeof(T) == 2) {
+          typedef Elem<T> E;
           uint2 pk;
-          pk.x = (uint32_t)f2bf(o[nd][0] * inv) | ((uint32_t)f2bf(o[nd][1] * inv) << 16);
-          pk.y = (uint32_t)f2bf(o[nd][2] * inv) | ((uint32_t)f2bf(o[nd][3] * inv) << 16);
+          pk.x = pack2(E::from_f(o[nd][0] * inv), E::from_f(o[nd][1] * inv));
+          pk.y = pack2(E::from_f(o[nd][2] * inv), E::from_f(o[nd][3] * inv));
           *(uint2*)(orow + d0) = pk;
         } else {
           *(float4*)(orow + d0) =
@@ -213,7 +206,9 @@ hipError_t run_attn(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
-  return dtype == 1 ? run_attn<bf16_t>(a, s) : run_attn<float>(a, s);
+  if (dtype == DT_BF16) return run_attn<bf16_t>(a, s);
+  if (dtype == DT_F16) return run_attn<f16_t>(a, s);
+  return run_attn<float>(a, s);
 }
 
 }  // namespace mt

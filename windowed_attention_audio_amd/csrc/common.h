@@ -6,19 +6,23 @@
 
 namespace mt {
 
-typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
+// 16-bit matrix-operand types.  Conversions from fp32 round to nearest even
+// (v_cvt_pk_bf16_f32 / v_cvt_f16_f32); fp16 saturates at +-65504.
+typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16, round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)f; }
+__device__ __forceinline__ float bf2f(bf16_t h) { return (float)h; }
+__device__ __forceinline__ f16_t f2h(float f) { return (f16_t)fminf(fmaxf(f, -65504.0f), 65504.0f); }
 
-__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+// Two 16-bit values packed into one 32-bit word (low half first).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(T a, T b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
 
 // Exact erf-based GELU, 0.5 x (1 + erf(x / sqrt 2)), through the device math
 // library's erff.
@@ -54,10 +58,32 @@ template <> struct Elem<bf16_t> {
   __device__ static __forceinline__ bf16_t from_f(float f) { return f2bf(f); }
   __device__ static __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
 };
+template <> struct Elem<f16_t> {
+  static constexpr int per16 = 8;
+  __device__ static __forceinline__ f16_t from_f(float f) { return f2h(f); }
+  __device__ static __forceinline__ float to_f(f16_t v) { return (float)v; }
+};
 template <> struct Elem<float> {
   static constexpr int per16 = 4;
   __device__ static __forceinline__ float from_f(float f) { return f; }
   __device__ static __forceinline__ float to_f(float v) { return v; }
 };
+
+// One 16 x 16 x 32 matrix-core step on 16-byte operand chunks (8 x 16-bit).
+__device__ __forceinline__ void mma16(f32x4& acc, const uint4& a, const uint4& b, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                               __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const uint4& a, const uint4& b, f16_t) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                              __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+// Four 16 x 16 x 4 fp32 steps, element e of every lane's chunk in step e.
+__device__ __forceinline__ void mma_f32x4(f32x4& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
 
 }  // namespace mt

@@ -61,10 +61,10 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
     }
     if constexpr (sizeof(T) == 2) {
       uint4 v;
-      v.x = (uint32_t)f2bf(y[0]) | ((uint32_t)f2bf(y[1]) << 16);
-      v.y = (uint32_t)f2bf(y[2]) | ((uint32_t)f2bf(y[3]) << 16);
-      v.z = (uint32_t)f2bf(y[4]) | ((uint32_t)f2bf(y[5]) << 16);
-      v.w = (uint32_t)f2bf(y[6]) | ((uint32_t)f2bf(y[7]) << 16);
+      v.x = pack2(Elem<T>::from_f(y[0]), Elem<T>::from_f(y[1]));
+      v.y = pack2(Elem<T>::from_f(y[2]), Elem<T>::from_f(y[3]));
+      v.z = pack2(Elem<T>::from_f(y[4]), Elem<T>::from_f(y[5]));
+      v.w = pack2(Elem<T>::from_f(y[6]), Elem<T>::from_f(y[7]));
       *(uint4*)(out + (int64_t)f1 * a.C) = v;
     } else {
       float4* o = (float4*)(out + (int64_t)f1 * a.C);
@@ -83,10 +83,10 @@ hipError_t launch_conv1(const Conv1Args& a, hipStream_t s) {
   if (pl < 1) return hipErrorInvalidValue;
   if (pl > 64) pl = 64;
   const int threads = ((CG * pl + 63) / 64) * 64;
-  if (a.bf16)
-    hipLaunchKernelGGL(conv1_kernel<bf16_t>, dim3((unsigned)a.total_T1), dim3(threads), 0, s, a, pl);
-  else
-    hipLaunchKernelGGL(conv1_kernel<float>, dim3((unsigned)a.total_T1), dim3(threads), 0, s, a, pl);
+  const dim3 grid((unsigned)a.total_T1), block(threads);
+  if (a.dtype == DT_BF16) hipLaunchKernelGGL(conv1_kernel<bf16_t>, grid, block, 0, s, a, pl);
+  else if (a.dtype == DT_F16) hipLaunchKernelGGL(conv1_kernel<f16_t>, grid, block, 0, s, a, pl);
+  else hipLaunchKernelGGL(conv1_kernel<float>, grid, block, 0, s, a, pl);
   return hipGetLastError();
 }
 

@@ -15,9 +15,9 @@
 // swizzled by the row index so that 16 lanes reading 16 rows at one chunk
 // hit distinct banks.
 //
-// Operand fragments: one 16-byte chunk per lane and operand.  For bf16 this
-// is one v_mfma_f32_16x16x32_bf16 (lane l supplies row l%16, k = 8*(l/16)..+7
-// of the 32-wide step).  For fp32 it is four v_mfma_f32_16x16x4_f32, the e-th
+// Operand fragments: one 16-byte chunk per lane and operand.  For bf16 and
+// fp16 this is one v_mfma_f32_16x16x32_{bf16,f16} (lane l supplies row l%16,
+// k = 8*(l/16)..+7 of the 32-wide step).  For fp32 it is four v_mfma_f32_16x16x4_f32, the e-th
 // one taking element e of every lane's chunk; as both operands use the same
 // assignment of k to (lane group, element), the sum over k is unchanged.
 #include "common.h"
@@ -30,21 +30,9 @@ namespace {
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 template <typename T>
-__device__ __forceinline__ void mma_chunk(f32x4& acc, const uint4& a, const uint4& b);
-
-template <>
-__device__ __forceinline__ void mma_chunk<bf16_t>(f32x4& acc, const uint4& a, const uint4& b) {
-  bf16x8 av = __builtin_bit_cast(bf16x8, a);
-  bf16x8 bv = __builtin_bit_cast(bf16x8, b);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ void mma_chunk<float>(f32x4& acc, const uint4& a, const uint4& b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+__device__ __forceinline__ void mma_chunk(f32x4& acc, const uint4& a, const uint4& b) {
+  if constexpr (sizeof(T) == 4) mma_f32x4(acc, a, b);
+  else mma16(acc, a, b, T{});
 }
 
 // Per-row state of the convolution gather.
@@ -245,9 +233,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             ((T*)a.C)[(int64_t)row * a.ldc + col] = Elem<T>::from_f(gelu_f(v));
           } else if constexpr (EPI == EPI_GELU_SPLIT) {
             const float gv = gelu_f(v);
-            const bf16_t hi = f2bf(gv);
-            const bf16_t lo = f2bf(gv - bf2f(hi));
-            bf16_t* C = (bf16_t*)a.C;
+            const T hi = Elem<T>::from_f(gv);
+            const T lo = Elem<T>::from_f(gv - Elem<T>::to_f(hi));
+            T* C = (T*)a.C;
             C[(int64_t)row * a.ldc + col] = hi;
             C[(int64_t)row * a.ldc + a.N + col] = lo;
           } else if constexpr (EPI == EPI_RESID) {
@@ -319,9 +307,13 @@ hipError_t by_epi(const GemmArgs& a, int epi, hipStream_t s) {
 hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStream_t s) {
   // the convolutions always end in bias + GELU
   if (conv && epi != EPI_GELU) return hipErrorInvalidValue;
-  if (dtype == 1) {
+  if (dtype == DT_BF16) {
     if (conv) return pick_tile<bf16_t, EPI_GELU, true>(a, s);
     return by_epi<bf16_t, false>(a, epi, s);
+  }
+  if (dtype == DT_F16) {
+    if (conv) return pick_tile<f16_t, EPI_GELU, true>(a, s);
+    return by_epi<f16_t, false>(a, epi, s);
   }
   if (conv) return pick_tile<float, EPI_GELU, true>(a, s);
   return by_epi<float, false>(a, epi, s);

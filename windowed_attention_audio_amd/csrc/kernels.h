@@ -7,6 +7,9 @@
 
 namespace mt {
 
+// Element type of matrix operands (same codes as mt_dtype).
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
 // ---------------------------------------------------------------- tables
 // Copies n 32-bit words from host memory into device memory through kernel
 // arguments (graph-capturable, no host buffer needs to outlive the call).
@@ -38,9 +41,9 @@ struct Conv1Args {
   int64_t total_T1;
   const float* w;            // [C][9] (tap = df*3 + dt)
   const float* b;            // [C]
-  void* out;                 // [sum T1][64][C] channels-last, bf16 or f32
+  void* out;                 // [sum T1][64][C] channels-last, element type dtype
   int C;
-  int bf16;
+  int dtype;
 };
 hipError_t launch_conv1(const Conv1Args& a, hipStream_t s);
 
@@ -49,7 +52,7 @@ enum Epi : int {
   EPI_F32 = 0,         // C (fp32) = acc (+ bias)
   EPI_ACT = 1,         // C (T) = acc + bias
   EPI_GELU = 2,        // C (T) = GELU(acc + bias)
-  EPI_GELU_SPLIT = 3,  // C (bf16) [row][col] = hi, [row][N + col] = lo of GELU(acc + bias)
+  EPI_GELU_SPLIT = 3,  // C (16-bit) [row][col] = hi, [row][N + col] = lo of GELU(acc + bias)
   EPI_RESID = 4,       // C (fp32) += acc + bias
   EPI_PE = 5,          // C (fp32) = acc + sinusoid(position of row, col)
   EPI_SWIGLU = 6,      // C (T) [row][f] = SiLU(gate) * up (gate/up interleaved by 16)
@@ -75,15 +78,15 @@ struct GemmArgs {
   int64_t out_seq_stride;  // EPI_OUT padded: rows per sequence (0 = packed)
 };
 
-// dtype: 0 = fp32 operands, 1 = bf16 operands.  conv: gather A as a 3x3
-// stride-2 convolution input.
+// dtype: DT_F32, DT_BF16 or DT_F16 operands (fp32 accumulation in every
+// case).  conv: gather A as a 3x3 stride-2 convolution input.
 hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStream_t s);
 
 // ---------------------------------------------------------------- LayerNorm
-// out = LN(x) * g + b per row of D fp32 values.  mode 0: T = fp32, 1: bf16,
-// 2: bf16 hi/lo split written as [row][2D].
+// out = LN(x) * g + b per row of D fp32 values, written as dtype (DT_*);
+// split: 16-bit hi/lo pair written as [row][2D] (hi | lo).
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D,
-                            float eps, int mode, hipStream_t s);
+                            float eps, int dtype, bool split, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -109,13 +112,14 @@ hipError_t launch_zero_pad_rows(float* out, const int32_t* cu_rows, int nseq, in
                                 int D, hipStream_t s);
 hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int32_t* cu_rows,
                             int nseq, int64_t stride, hipStream_t s);
-// Weight repacking (fp32 masters -> kernel layouts).
+// Weight repacking (fp32 masters -> kernel layouts); dtype selects the
+// destination element type (DT_*).
 hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
-                          int64_t dst_col0, int bf16, hipStream_t s);
-hipError_t launch_pack_conv(const float* w, void* dst, int C, int bf16, hipStream_t s);
-hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int bf16,
+                          int64_t dst_col0, int dtype, hipStream_t s);
+hipError_t launch_pack_conv(const float* w, void* dst, int C, int dtype, hipStream_t s);
+hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int dtype,
                                 hipStream_t s);
-hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int bf16,
+hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int dtype,
                               hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 

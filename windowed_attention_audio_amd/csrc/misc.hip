@@ -76,59 +76,60 @@ __global__ void copy_rows_kernel(const float* __restrict__ x, float* __restrict_
   for (int c = threadIdx.x; c < D; c += blockDim.x) out[orow * D + c] = x[(int64_t)row * D + c];
 }
 
-__device__ __forceinline__ void put(void* dst, int64_t i, float v, int bf16) {
-  if (bf16) ((bf16_t*)dst)[i] = f2bf(v);
+__device__ __forceinline__ void put(void* dst, int64_t i, float v, int dtype) {
+  if (dtype == DT_BF16) ((bf16_t*)dst)[i] = f2bf(v);
+  else if (dtype == DT_F16) ((f16_t*)dst)[i] = f2h(v);
   else ((float*)dst)[i] = v;
 }
 
 // dst[r * dst_ld + col0 + c] = src[r * cols + c]
 __global__ void convert_kernel(const float* __restrict__ src, void* dst, int64_t rows, int64_t cols,
-                               int64_t dst_ld, int64_t col0, int bf16) {
+                               int64_t dst_ld, int64_t col0, int dtype) {
   const int64_t n = rows * cols;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / cols, c = i - r * cols;
-    put(dst, r * dst_ld + col0 + c, src[i], bf16);
+    put(dst, r * dst_ld + col0 + c, src[i], dtype);
   }
 }
 
 // conv [C][C][3][3] -> [C][9C], column (df * 3 + dt) * C + ci
-__global__ void pack_conv_kernel(const float* __restrict__ w, void* dst, int C, int bf16) {
+__global__ void pack_conv_kernel(const float* __restrict__ w, void* dst, int C, int dtype) {
   const int64_t n = (int64_t)C * C * 9;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t co = i / (9LL * C);
     const int64_t rem = i - co * 9LL * C;
     const int tap = (int)(rem / C), ci = (int)(rem - (int64_t)tap * C);
-    put(dst, i, w[((co * C + ci) * 9) + tap], bf16);
+    put(dst, i, w[((co * C + ci) * 9) + tap], dtype);
   }
 }
 
 // conv_out [D][C*F] (column c*F + f) -> [D][F*C] (column f*C + c), matching the
 // channels-last [t][f][c] output of the last convolution.
 __global__ void pack_conv_out_kernel(const float* __restrict__ w, void* dst, int D, int C, int F,
-                                     int bf16) {
+                                     int dtype) {
   const int64_t n = (int64_t)D * C * F;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t d = i / ((int64_t)C * F);
     const int rem = (int)(i - d * C * F);
     const int f = rem / C, c = rem - f * C;
-    put(dst, i, w[d * C * F + (int64_t)c * F + f], bf16);
+    put(dst, i, w[d * C * F + (int64_t)c * F + f], dtype);
   }
 }
 
 // gate/up [A][O] -> [2A][O], rows interleaved in blocks of 16 (16 gate rows,
 // then the 16 up rows of the same features).
 __global__ void pack_swiglu_kernel(const float* __restrict__ gate, const float* __restrict__ up,
-                                   void* dst, int A, int O, int bf16) {
+                                   void* dst, int A, int O, int dtype) {
   const int64_t n = 2LL * A * O;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / O, c = i - r * O;
     const int64_t p = r >> 5, q = r & 31;
     const float v = q < 16 ? gate[(p * 16 + q) * O + c] : up[(p * 16 + q - 16) * O + c];
-    put(dst, i, v, bf16);
+    put(dst, i, v, dtype);
   }
 }
 
@@ -187,28 +188,28 @@ hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int3
 }
 
 hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
-                          int64_t dst_col0, int bf16, hipStream_t s) {
+                          int64_t dst_col0, int dtype, hipStream_t s) {
   hipLaunchKernelGGL(convert_kernel, grid_for(rows * cols), dim3(256), 0, s, src, dst, rows, cols,
-                     dst_ld, dst_col0, bf16);
+                     dst_ld, dst_col0, dtype);
   return hipGetLastError();
 }
 
-hipError_t launch_pack_conv(const float* w, void* dst, int C, int bf16, hipStream_t s) {
-  hipLaunchKernelGGL(pack_conv_kernel, grid_for(9LL * C * C), dim3(256), 0, s, w, dst, C, bf16);
+hipError_t launch_pack_conv(const float* w, void* dst, int C, int dtype, hipStream_t s) {
+  hipLaunchKernelGGL(pack_conv_kernel, grid_for(9LL * C * C), dim3(256), 0, s, w, dst, C, dtype);
   return hipGetLastError();
 }
 
-hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int bf16,
+hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int dtype,
                                 hipStream_t s) {
   hipLaunchKernelGGL(pack_conv_out_kernel, grid_for((int64_t)D * C * F), dim3(256), 0, s, w, dst, D,
-                     C, F, bf16);
+                     C, F, dtype);
   return hipGetLastError();
 }
 
-hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int bf16,
+hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int dtype,
                               hipStream_t s) {
   hipLaunchKernelGGL(pack_swiglu_kernel, grid_for(2LL * A * O), dim3(256), 0, s, gate, up, dst, A,
-                     O, bf16);
+                     O, dtype);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int VEC, int MODE>
+template <int VEC, typename T, bool SPLIT>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ g,
                                                         const float* __restrict__ b,
@@ -55,21 +55,20 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     y.y = (v[i].y - mean) * rstd * gg.y + bb.y;
     y.z = (v[i].z - mean) * rstd * gg.z + bb.z;
     y.w = (v[i].w - mean) * rstd * gg.w + bb.w;
-    if constexpr (MODE == 0) {
+    if constexpr (sizeof(T) == 4) {
       ((float4*)out)[(int64_t)row * (D / 4) + c4] = y;
     } else {
-      const bf16_t h0 = f2bf(y.x), h1 = f2bf(y.y), h2 = f2bf(y.z), h3 = f2bf(y.w);
-      uint2 hi;
-      hi.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      hi.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-      if constexpr (MODE == 1) {
+      const T h0 = Elem<T>::from_f(y.x), h1 = Elem<T>::from_f(y.y);
+      const T h2 = Elem<T>::from_f(y.z), h3 = Elem<T>::from_f(y.w);
+      const uint2 hi = make_uint2(pack2(h0, h1), pack2(h2, h3));
+      if constexpr (!SPLIT) {
         ((uint2*)out)[(int64_t)row * (D / 4) + c4] = hi;
       } else {
-        const bf16_t l0 = f2bf(y.x - bf2f(h0)), l1 = f2bf(y.y - bf2f(h1));
-        const bf16_t l2 = f2bf(y.z - bf2f(h2)), l3 = f2bf(y.w - bf2f(h3));
-        uint2 lo;
-        lo.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        lo.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+        const T l0 = Elem<T>::from_f(y.x - Elem<T>::to_f(h0));
+        const T l1 = Elem<T>::from_f(y.y - Elem<T>::to_f(h1));
+        const T l2 = Elem<T>::from_f(y.z - Elem<T>::to_f(h2));
+        const T l3 = Elem<T>::from_f(y.w - Elem<T>::to_f(h3));
+        const uint2 lo = make_uint2(pack2(l0, l1), pack2(l2, l3));
         ((uint2*)out)[(int64_t)row * (D / 2) + c4] = hi;
         ((uint2*)out)[(int64_t)row * (D / 2) + D / 4 + c4] = lo;
       }
@@ -77,30 +76,39 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   }
 }
 
+template <int VEC, typename T, bool SPLIT>
+hipError_t ln_run(const float* x, const float* g, const float* b, void* out, int M, float eps,
+                  hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL((layernorm_kernel<VEC, T, SPLIT>), dim3((M + 3) / 4), dim3(256), 0, s, x, g, b,
+                     out, M, eps);
+  return hipGetLastError();
+}
+
 template <int VEC>
 hipError_t ln_mode(const float* x, const float* g, const float* b, void* out, int M, float eps,
-                   int mode, hipStream_t s) {
-  const dim3 grid((M + 3) / 4), block(256);
-  if (M == 0) return hipSuccess;
-  if (mode == 0) hipLaunchKernelGGL((layernorm_kernel<VEC, 0>), grid, block, 0, s, x, g, b, out, M, eps);
-  else if (mode == 1) hipLaunchKernelGGL((layernorm_kernel<VEC, 1>), grid, block, 0, s, x, g, b, out, M, eps);
-  else hipLaunchKernelGGL((layernorm_kernel<VEC, 2>), grid, block, 0, s, x, g, b, out, M, eps);
-  return hipGetLastError();
+                   int dtype, bool split, hipStream_t s) {
+  if (dtype == DT_F32) return split ? hipErrorInvalidValue : ln_run<VEC, float, false>(x, g, b, out, M, eps, s);
+  if (dtype == DT_BF16)
+    return split ? ln_run<VEC, bf16_t, true>(x, g, b, out, M, eps, s)
+                 : ln_run<VEC, bf16_t, false>(x, g, b, out, M, eps, s);
+  return split ? ln_run<VEC, f16_t, true>(x, g, b, out, M, eps, s)
+               : ln_run<VEC, f16_t, false>(x, g, b, out, M, eps, s);
 }
 
 }  // namespace
 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D,
-                            float eps, int mode, hipStream_t s) {
+                            float eps, int dtype, bool split, hipStream_t s) {
   switch (D / 256) {
-    case 1: return ln_mode<1>(x, g, b, out, M, eps, mode, s);
-    case 2: return ln_mode<2>(x, g, b, out, M, eps, mode, s);
-    case 3: return ln_mode<3>(x, g, b, out, M, eps, mode, s);
-    case 4: return ln_mode<4>(x, g, b, out, M, eps, mode, s);
-    case 5: return ln_mode<5>(x, g, b, out, M, eps, mode, s);
-    case 6: return ln_mode<6>(x, g, b, out, M, eps, mode, s);
-    case 7: return ln_mode<7>(x, g, b, out, M, eps, mode, s);
-    case 8: return ln_mode<8>(x, g, b, out, M, eps, mode, s);
+    case 1: return ln_mode<1>(x, g, b, out, M, eps, dtype, split, s);
+    case 2: return ln_mode<2>(x, g, b, out, M, eps, dtype, split, s);
+    case 3: return ln_mode<3>(x, g, b, out, M, eps, dtype, split, s);
+    case 4: return ln_mode<4>(x, g, b, out, M, eps, dtype, split, s);
+    case 5: return ln_mode<5>(x, g, b, out, M, eps, dtype, split, s);
+    case 6: return ln_mode<6>(x, g, b, out, M, eps, dtype, split, s);
+    case 7: return ln_mode<7>(x, g, b, out, M, eps, dtype, split, s);
+    case 8: return ln_mode<8>(x, g, b, out, M, eps, dtype, split, s);
     default: return hipErrorInvalidValue;
   }
 }
