@@ -174,6 +174,7 @@ struct PackedLayout {
   };
   std::vector<L> layers;
   size_t lnp_g, lnp_b, wp1, bp1, wp2, bp2, wgu, wd;
+  size_t zeros;  // 256 bytes of zeros read by out-of-range matrix loads
   size_t bytes;
 };
 
@@ -239,6 +240,7 @@ PackedLayout packed_layout(const mt_encoder_config& c) {
   p.bp2 = k.take(O * 4);
   p.wgu = A ? k.take(2 * A * O * es) : 0;
   p.wd = A ? k.take(O * A * es) : 0;
+  p.zeros = k.take(256);
   p.bytes = k.off;
   return p;
 }
@@ -268,6 +270,7 @@ struct mt_encoder {
   std::vector<Layer> layers;
   const float *lnp_g, *lnp_b, *bp1, *bp2;
   const void *wp1, *wp2, *wgu, *wd;
+  const void* zeros;
 };
 
 namespace {
@@ -515,6 +518,8 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
     HIP_TRY(launch_convert(next(), P + L.wd, O, A, A, 0, bf, s), "pack adapter down");
   }
 
+  HIP_TRY(launch_fill_i32((int*)(P + L.zeros), 0, 64, s), "zero block");
+
   mt_encoder* e = new mt_encoder();
   e->cfg = c;
   e->dt = bf;  // DT_* code
@@ -551,6 +556,7 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
   e->bp2 = (const float*)(P + L.bp2);
   e->wgu = A ? P + L.wgu : nullptr;
   e->wd = A ? P + L.wd : nullptr;
+  e->zeros = P + L.zeros;
   *out = e;
   return MT_OK;
 }
@@ -638,6 +644,13 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
   void* ffn = w + p.o_ffn;
   void* ybuf = w + p.o_y;
   void* ahid = w + p.o_ahid;
+
+  auto gemm = [&](const void* A_, int64_t lda, const void* B_, int64_t ldb, int M_, int N_, int K_,
+                  const float* bias, void* C_, int64_t ldc) {
+    GemmArgs g_ = ::gemm(A_, lda, B_, ldb, M_, N_, K_, bias, C_, ldc);
+    g_.zeros = enc->zeros;
+    return g_;
+  };
 
   // ---- front-end
   Conv1Args c1;

@@ -23,7 +23,9 @@ namespace mt {
 
 namespace {
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// K rows: chunk c of key row r at chunk slot c ^ (r & 7) (conflict-free reads of
+// 16 consecutive rows at one chunk)
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // position of key kv inside a V^T row (bf16: permuted within 32-key blocks)
 template <typename T>

@@ -27,7 +27,13 @@ namespace mt {
 
 namespace {
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Chunk swizzle: chunk c of row r is stored at chunk slot c ^ (r & 7).  A
+// 16-byte fragment read (16 consecutive rows at one chunk, four chunk
+// groups) then runs at the LDS's full 256 bytes per clock; measured with the
+// LDS bank-conflict counter, the unswizzled layout costs 4x and a swizzle
+// that also folds in bit 3 of the row still 2x.  It depends only on r % 8,
+// so fragments of 16-row tiles are a base address plus constant offsets.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 template <typename T>
 __device__ __forceinline__ void mma_chunk(f32x4& acc, const uint4& a, const uint4& b) {
@@ -42,6 +48,109 @@ struct ConvRow {
   int f0;            // 2 * f_out - 1
   int Tin;           // input time rows of the sequence
 };
+
+// Fused epilogue for accumulators of C^T tiles (the products are issued as
+// B * A^T): acc[i][j][e] holds C[rbase + 16 i][cbase + 16 j + e], i.e. four
+// consecutive columns of one row, so every store is 8 (16-bit) or 16 (fp32)
+// bytes.  rbase = first row of the lane, cbase = its first column.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float v0, float v1, float v2, float v3) {
+  if constexpr (sizeof(T) == 4) {
+    *(float4*)p = make_float4(v0, v1, v2, v3);
+  } else {
+    typedef Elem<T> E;
+    *(uint2*)p = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
+  }
+}
+
+template <typename T, int EPI, int MI, int NI>
+__device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI], const int rbase,
+                                          const int cbase) {
+  float4 bias[NI];
+  double tau[EPI == EPI_PE ? NI * 4 : 1];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int col = cbase + 16 * j;
+    bias[j] = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (EPI == EPI_PE) {
+      const int half = a.N / 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = col + e;
+        const int jj = c < half ? c : c - half;
+        // timescale 10000^(-jj / (half - 1))
+        tau[4 * j + e] = exp(-(double)jj * 9.2103403719761836 / (double)(half - 1));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = rbase + 16 * i;
+    if (row >= a.M) continue;
+    int64_t orow = row;
+    int pos = 0;
+    if constexpr (EPI == EPI_PE || EPI == EPI_OUT) {
+      if (EPI == EPI_PE || a.out_seq_stride > 0) {
+        const int sq = find_seq(a.cu_rows, a.nseq, row);
+        pos = row - a.cu_rows[sq];
+        if (EPI == EPI_OUT) orow = (int64_t)sq * a.out_seq_stride + pos;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int col = cbase + 16 * j;
+      if (col >= a.N) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        if (j & 1) continue;  // tile j holds gate, tile j + 1 up, of the same 16 features
+        const int feat = (col - (col & 15)) / 2 + (col & 15);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = silu_f(acc[i][j][e]) * acc[i][j + 1][e];
+        store4((T*)a.C + (int64_t)row * a.ldc + feat, o[0], o[1], o[2], o[3]);
+        continue;
+      } else {
+        const float v0 = acc[i][j][0] + bias[j].x, v1 = acc[i][j][1] + bias[j].y;
+        const float v2 = acc[i][j][2] + bias[j].z, v3 = acc[i][j][3] + bias[j].w;
+        if constexpr (EPI == EPI_F32) {
+          store4((float*)a.C + (int64_t)row * a.ldc + col, v0, v1, v2, v3);
+        } else if constexpr (EPI == EPI_ACT) {
+          store4((T*)a.C + (int64_t)row * a.ldc + col, v0, v1, v2, v3);
+        } else if constexpr (EPI == EPI_GELU) {
+          store4((T*)a.C + (int64_t)row * a.ldc + col, gelu_f(v0), gelu_f(v1), gelu_f(v2), gelu_f(v3));
+        } else if constexpr (EPI == EPI_GELU_SPLIT) {
+          const float g4[4] = {gelu_f(v0), gelu_f(v1), gelu_f(v2), gelu_f(v3)};
+          float lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lo[e] = g4[e] - Elem<T>::to_f(Elem<T>::from_f(g4[e]));
+          T* C = (T*)a.C + (int64_t)row * a.ldc;
+          store4(C + col, g4[0], g4[1], g4[2], g4[3]);
+          store4(C + a.N + col, lo[0], lo[1], lo[2], lo[3]);
+        } else if constexpr (EPI == EPI_RESID) {
+          float4* R = (float4*)((float*)a.C + (int64_t)row * a.ldc + col);
+          float4 r = *R;
+          r.x += v0;
+          r.y += v1;
+          r.z += v2;
+          r.w += v3;
+          *R = r;
+        } else if constexpr (EPI == EPI_PE) {
+          const int half = a.N / 2;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            double ang = (double)pos * tau[4 * j + e];
+            ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+            const float fa = (float)ang;
+            o[e] = acc[i][j][e] + (col + e < half ? sinf(fa) : cosf(fa));
+          }
+          store4((float*)a.C + (int64_t)row * a.ldc + col, o[0], o[1], o[2], o[3]);
+        } else if constexpr (EPI == EPI_OUT) {
+          store4((float*)a.C + orow * a.ldc + col, v0, v1, v2, v3);
+        }
+      }
+    }
+  }
+}
 
 template <typename T, int BM, int BN, int EPI, bool CONV>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
@@ -185,85 +294,240 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) mma_chunk<T>(acc[i][j], af[i], bfr[j]);
+        for (int j = 0; j < NI; ++j) mma_chunk<T>(acc[i][j], bfr[j], af[i]);  // C^T tile
     }
     if (kb + 1 < nkb) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds C[4g + e][l16] of every 16 x 16 tile
-  const int rbase = m0 + wm * WTM + 4 * g;
-  const int cbase = n0 + wn * WTN + l16;
-  if constexpr (EPI == EPI_SWIGLU) {
-    T* C = (T*)a.C;
+  // ---- epilogue: lane holds C[l16][4g + e] of every 16 x 16 tile
+  epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
+}
+
+
+// ---------------------------------------------------------------------------
+// 16-bit operands: WM x WN wavefronts, BM x BN tile, K slices of 64 copied
+// global -> LDS by the matrix-load DMA (global_load_lds_dwordx4: lane j of a
+// wavefront writes bytes [16 j, 16 j + 16) of a 1 KB LDS block), two LDS
+// stages.  The slice for kb + 1 is in flight while slice kb feeds the matrix
+// cores; each wavefront waits only for its own earlier loads (vmcnt) before
+// the barrier that publishes a stage.  Loads that fall outside the matrices
+// (row or K tails, convolution padding) read a 16-byte block of zeros.
+// Rows of a stage: A rows [0, BM), then B rows [BM, BM + BN); 128 bytes each,
+// chunk c of row r stored at chunk slot c ^ swz(r).
+
+__device__ __forceinline__ void wait_vm(int n) {
+  // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding)
+  switch (n) {
+#define MT_WAITVM(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); break;
+    MT_WAITVM(0) MT_WAITVM(1) MT_WAITVM(2) MT_WAITVM(3) MT_WAITVM(4) MT_WAITVM(5) MT_WAITVM(6)
+    MT_WAITVM(7) MT_WAITVM(8) MT_WAITVM(9) MT_WAITVM(10) MT_WAITVM(11) MT_WAITVM(12)
+    MT_WAITVM(13) MT_WAITVM(14) MT_WAITVM(15) MT_WAITVM(16)
+#undef MT_WAITVM
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <typename T, int BM, int BN, int WM, int WN, int NST, int EPI, bool CONV>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_lds_kernel(GemmArgs a) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 16, NI = WTN / 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int NBLK = ROWS / 8;               // 1 KB blocks per stage
+  constexpr int BPW = (NBLK + NW - 1) / NW;    // blocks per wavefront (the last may be idle)
+  static_assert(sizeof(T) == 2, "16-bit operands only");
+  static_assert(BM % 16 == 0 && BN % 16 == 0 && ROWS % 8 == 0, "tile shape");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be 16-aligned");
+  static_assert(EPI != EPI_SWIGLU || (WTN % 32) == 0, "SwiGLU pairs need 32-column wave tiles");
+  static_assert(BPW <= 16, "too many loads per wavefront");
+  static_assert(NST == 2, "two LDS stages");
+
+  __shared__ uint4 st0[ROWS * 8];
+  __shared__ uint4 st1[ROWS * 8];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
+  const int m0 = bm * BM, n0 = bn * BN;
+  const char* zeros = (const char*)a.zeros;
+
+  // ---- load plan.  Block blk (8 rows x 8 chunks) is loaded by wavefront
+  // blk % NW; lane j of it fills LDS row 8 blk + j / 8, chunk slot j % 8.  So
+  // this lane's rows are r0 + RPI * i (i = 0 .. BPW-1), and since swz depends
+  // only on r % 16 it loads the same logical chunk c in all of them.
+  constexpr int RPI = NW * 8;                  // rows per load round
+  constexpr int AI = BM / RPI;                 // rounds that fill A rows
+  static_assert(BM % RPI == 0, "A rows must fill whole load rounds");
+  const int r0 = wave * 8 + (lane >> 3);
+  const int c = (lane & 7) ^ swz(r0);
+  const int64_t ldab = a.lda * (int64_t)sizeof(T), ldbb = a.ldb * (int64_t)sizeof(T);
+  const char* a_base = (const char*)a.A + (int64_t)(m0 + r0) * ldab + c * 16;
+  const char* b_base = (const char*)a.B + (int64_t)(n0 + r0) * ldbb + c * 16;
+  const int64_t a_step = RPI * ldab, b_step = RPI * ldbb;
+  uint32_t a_ok = 0, b_ok = 0;  // bit i: row of load round i inside the matrix
 #pragma unroll
-    for (int j = 0; j < NI; j += 2) {
-      const int colg = cbase + j * 16;  // gate column (its pair: + 16)
-      if (colg >= a.N) continue;
-      const int feat = (colg - l16) / 2 + l16;
+  for (int i = 0; i < BPW; ++i) {
+    if (m0 + r0 + RPI * i < a.M) a_ok |= 1u << i;
+    if (n0 + r0 + RPI * i < a.N) b_ok |= 1u << i;
+  }
+  int nblk = 0;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < BPW; ++i) nblk += (wave + i * NW < NBLK) ? 1 : 0;
+
+  ConvRow cr[CONV ? AI : 1];
+  int ctap = 0, cch = c * 8;  // (tap, channel) of this lane's chunk in the current slice
+  if constexpr (CONV) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rbase + i * 16 + e;
-          if (row < a.M) {
-            const float gv = acc[i][j][e], uv = acc[i][j + 1][e];
-            C[(int64_t)row * a.ldc + feat] = Elem<T>::from_f(silu_f(gv) * uv);
-          }
-        }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int col = cbase + j * 16;
-      if (col >= a.N) continue;
-      const float bias = a.bias ? a.bias[col] : 0.f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rbase + i * 16 + e;
-          if (row >= a.M) continue;
-          const float v = acc[i][j][e] + bias;
-          if constexpr (EPI == EPI_F32) {
-            ((float*)a.C)[(int64_t)row * a.ldc + col] = v;
-          } else if constexpr (EPI == EPI_ACT) {
-            ((T*)a.C)[(int64_t)row * a.ldc + col] = Elem<T>::from_f(v);
-          } else if constexpr (EPI == EPI_GELU) {
-            ((T*)a.C)[(int64_t)row * a.ldc + col] = Elem<T>::from_f(gelu_f(v));
-          } else if constexpr (EPI == EPI_GELU_SPLIT) {
-            const float gv = gelu_f(v);
-            const T hi = Elem<T>::from_f(gv);
-            const T lo = Elem<T>::from_f(gv - Elem<T>::to_f(hi));
-            T* C = (T*)a.C;
-            C[(int64_t)row * a.ldc + col] = hi;
-            C[(int64_t)row * a.ldc + a.N + col] = lo;
-          } else if constexpr (EPI == EPI_RESID) {
-            float* R = (float*)a.C;
-            R[(int64_t)row * a.ldc + col] += v;
-          } else if constexpr (EPI == EPI_PE) {
-            const int sq = find_seq(a.cu_rows, a.nseq, row);
-            const int pos = row - a.cu_rows[sq];
-            const int half = a.N / 2;
-            const int jj = col < half ? col : col - half;
-            // timescale 10000^(-jj/(half-1)); angle reduced mod 2 pi in double
-            const double ts = exp(-(double)jj * 9.2103403719761836 / (double)(half - 1));
-            double ang = (double)pos * ts;
-            ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-            const float fa = (float)ang;
-            const float pe = col < half ? sinf(fa) : cosf(fa);
-            ((float*)a.C)[(int64_t)row * a.ldc + col] = acc[i][j][e] + pe;
-          } else if constexpr (EPI == EPI_OUT) {
-            int64_t orow = row;
-            if (a.out_seq_stride > 0) {
-              const int sq = find_seq(a.cu_rows, a.nseq, row);
-              orow = (int64_t)sq * a.out_seq_stride + (row - a.cu_rows[sq]);
-            }
-            ((float*)a.C)[orow * a.ldc + col] = v;
-          }
-        }
+    for (int i = 0; i < AI; ++i) {
+      const int m = m0 + r0 + RPI * i;
+      const bool ok = m < a.M;
+      const int mm = ok ? m : 0;
+      const int t_glob = mm / a.conv_Fout;
+      const int fo = mm - t_glob * a.conv_Fout;
+      const int sq = find_seq(a.cu_out, a.nseq, t_glob);
+      const int tl = t_glob - a.cu_out[sq];
+      const int tin_base = a.cu_in[sq];
+      cr[i].base = (const char*)a.A + (int64_t)tin_base * a.conv_Fin * a.conv_C * (int64_t)sizeof(T);
+      cr[i].t0 = ok ? 2 * tl - 1 : -(1 << 28);  // rows past M never pass the time test
+      cr[i].f0 = 2 * fo - 1;
+      cr[i].Tin = a.cu_in[sq + 1] - tin_base;
     }
   }
+
+  auto issue = [&](uint4* stage, int kb) {
+    const bool kok = kb * 64 + c * 8 < a.K;
+    int df = 0, dt = 0;
+    if constexpr (CONV) {
+      df = ctap / 3;
+      dt = ctap - 3 * df;
+    }
+    const char* pa = a_base + kb * 128;
+    const char* pb = b_base + kb * 128;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave + i * NW;
+      if (i * NW >= NBLK) break;  // no wavefront has this round
+      const char* p = zeros;
+      if (i < AI) {
+        if constexpr (CONV) {
+          const int t = cr[i].t0 + dt, f = cr[i].f0 + df;
+          if (kok && t >= 0 && t < cr[i].Tin && f >= 0 && f < a.conv_Fin)
+            p = cr[i].base + (((int64_t)t * a.conv_Fin + f) * a.conv_C + cch) * (int64_t)sizeof(T);
+        } else {
+          p = (kok && ((a_ok >> i) & 1)) ? pa : zeros;
+          pa += a_step;
+        }
+      } else {
+        p = (kok && ((b_ok >> (i - AI)) & 1)) ? pb : zeros;
+        pb += b_step;
+      }
+      if (blk < NBLK)
+        __builtin_amdgcn_global_load_lds((const void*)p, (lds_ptr_t)(stage + blk * 64), 16, 0, 0);
+    }
+    if constexpr (CONV) {
+      cch += 64;
+      while (cch >= a.conv_C) { cch -= a.conv_C; ++ctap; }
+    }
+  };
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- main loop.  A 64-wide K slice is two 32-wide MFMA steps; their
+  // operand fragments alternate between two register sets so that the LDS
+  // reads of one step overlap the matrix-core work of the other.  One barrier
+  // per slice publishes the next slice (all wavefronts' DMA landed) and
+  // retires the slice whose stage is refilled next.
+  const int g = lane >> 4, l16 = lane & 15;
+  uint4 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+  auto ldfrag = [&](const uint4* stage, int s2, uint4 (&fa)[MI], uint4 (&fb)[NI]) {
+    const int cc = 4 * s2 + g;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * WTM + i * 16 + l16;
+      fa[i] = stage[r * 8 + (cc ^ swz(r))];
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = BM + wn * WTN + j * 16 + l16;
+      fb[j] = stage[r * 8 + (cc ^ swz(r))];
+    }
+  };
+  // MFMAs of rows [i0, i1) of the wave tile
+  auto mma = [&](const uint4 (&fa)[MI], const uint4 (&fb)[NI], int i0, int i1) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (i < i0 || i >= i1) continue;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) mma16(acc[i][j], fb[j], fa[i], T{});  // C^T tile
+    }
+  };
+
+  // Two LDS stages: slice kb lives in stage kb % 2 and slice kb + 2 is loaded
+  // while slice kb + 1 is consumed.  The slice count is padded to an even
+  // number (a slice past K loads zeros and adds nothing) and the last slice
+  // is peeled off, so the loop body has no branch that touches the
+  // accumulators (the register allocator keeps them in place).  Phases are
+  // pinned with sched_barrier: the compiler would otherwise wait for all
+  // outstanding LDS reads before the first MFMA of a phase and hoist the DMA
+  // address arithmetic in front of the matrix-core work.
+  constexpr int MH = MI / 2;
+  const int nkb = ((a.K + 127) / 128) * 2;
+  auto step = [&](int kb, const uint4* CUR, const uint4* NXT) {  // kb + 1 < nkb
+    mma(fa0, fb0, 0, MH);              // k-step 0 of slice kb (read during the last phase)
+    __builtin_amdgcn_sched_barrier(0);
+    ldfrag(CUR, 1, fa1, fb1);          // k-step 1 of slice kb, behind the MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0, MH, MI);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm(0);                        // this wavefront's DMA of slice kb+1 has landed
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0): reads of CUR done
+    __builtin_amdgcn_s_barrier();      // every wavefront's has; CUR is no longer read
+    __builtin_amdgcn_sched_barrier(0);
+    ldfrag(NXT, 0, fa0, fb0);          // k-step 0 of slice kb+1
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1, 0, MH);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 2 < nkb) issue((uint4*)CUR, kb + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1, MH, MI);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue(st0, 0);
+  issue(st1, 1);
+  wait_vm(nblk);
+  __builtin_amdgcn_s_barrier();
+  ldfrag(st0, 0, fa0, fb0);
+  // unrolled by two so that every LDS access names its stage array: the
+  // compiler then sees that reads of one stage do not alias DMA into another
+  for (int kb = 0; kb < nkb - 2; kb += 2) {
+    step(kb, st0, st1);
+    step(kb + 1, st1, st0);
+  }
+  step(nkb - 2, st0, st1);
+  ldfrag(st1, 1, fa1, fb1);            // last slice
+  mma(fa0, fb0, 0, MI);
+  mma(fa1, fb1, 0, MI);
+
+  epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int NST, int EPI, bool CONV>
+hipError_t run_lds(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WM, WN, NST, EPI, CONV>), dim3(tiles),
+                     dim3(WM * WN * 64), 0, s, a);
+  return hipGetLastError();
 }
 
 template <typename T, int BM, int BN, int EPI, bool CONV>
@@ -276,6 +540,14 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
 
 template <typename T, int EPI, bool CONV>
 hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // 128-row tiles, four wavefronts of 64 x 64 (x 80): two workgroups per
+    // CU (64 / 72 KB of LDS each), so one's DMA wait overlaps the other's
+    // matrix work.  (Measured on the encoder's shapes: 620-780 TFLOP/s.)
+    // The convolutions keep the register-staged kernel below: its gather
+    // measured faster (2.6 ms vs 3.3 ms for the 16 x 30 s conv2).
+    if constexpr (!CONV) return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
+  }
   if constexpr (CONV) {
     // output channels 480 = 3 x 160
     if (a.N % 160 == 0) return run<T, 128, 160, EPI, CONV>(a, s);

@@ -76,6 +76,7 @@ struct GemmArgs {
   // row -> sequence position (EPI_PE, EPI_OUT)
   const int32_t* cu_rows;  // [nseq+1]
   int64_t out_seq_stride;  // EPI_OUT padded: rows per sequence (0 = packed)
+  const void* zeros;       // >= 16 bytes of zeros (device), read by out-of-range loads
 };
 
 // dtype: DT_F32, DT_BF16 or DT_F16 operands (fp32 accumulation in every
