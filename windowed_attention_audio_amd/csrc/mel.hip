@@ -2,7 +2,8 @@
 // Architecture table, Audio row; gotcha list: the trailing STFT frame is
 // dropped, so a clip of n samples gives floor(n / 160) frames).
 //
-// Pass 1 (mel_frames_kernel): one workgroup per 16 consecutive frames.
+// Pass 1 (mel_frames_kernel): one workgroup of 128 threads per 8 consecutive
+// frames (42 KB of LDS: three workgroups per CU).
 //   load    each frame is 400 samples centred on 160 t, the clip mirrored at
 //           both ends (reflect padding by 200, edge sample not repeated),
 //           times a periodic Hann window; reads of neighbouring frames are
@@ -29,13 +30,14 @@ namespace mt {
 
 namespace {
 
-constexpr int FPB = 16;  // frames per workgroup
+constexpr int FPB = 8;   // frames per workgroup
+constexpr int NTH = 128; // threads per workgroup (FPB x 16 in step B)
 
 __device__ __forceinline__ double2 cmul(double2 a, double2 b) {
   return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 
-__global__ __launch_bounds__(256) void mel_frames_kernel(MelArgs a) {
+__global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
   __shared__ float xs[FPB][400];       // raw frame samples, later |X|^2 [FPB][201]
   __shared__ double2 ys[FPB][25][9];   // step-A output, k1 = 0..8
   __shared__ float fmax_s[FPB];
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void mel_frames_kernel(MelArgs a) {
   __syncthreads();
 
   // ---- load (the window is applied in double in step A)
-  for (int idx = tid; idx < FPB * 400; idx += 256) {
+  for (int idx = tid; idx < FPB * 400; idx += NTH) {
     const int f = idx / 400, j = idx - f * 400;
     const int sq = fseq_s[f];
     float v = 0.f;
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) void mel_frames_kernel(MelArgs a) {
   __syncthreads();
 
   // ---- step A: (frame, n2) -> 16-point real DFT over n1 of the windowed frame
-  for (int task = tid; task < FPB * 25; task += 256) {
+  for (int task = tid; task < FPB * 25; task += NTH) {
     const int f = task / 25, n2 = task - f * 25;
     double x[16];
 #pragma unroll
@@ -99,17 +101,23 @@ __global__ __launch_bounds__(256) void mel_frames_kernel(MelArgs a) {
       if (k1 > 8) v.y = -v.y;  // real input: Y[16 - k1] = conj(Y[k1])
       y[n2] = cmul(v, c_tw[n2 * k1]);
     }
-    const int nk2 = k1 <= 8 ? 13 : 12;
-    for (int k2 = 0; k2 < nk2; ++k2) {
-      double re = 0.0, im = 0.0;
+    // all 13 outputs at once (13 independent accumulator pairs, compile-time
+    // twiddles); k1 > 8 has only 12 bins <= 200
+    double re[13], im[13];
 #pragma unroll
-      for (int n2 = 0; n2 < 25; ++n2) {
+    for (int k2 = 0; k2 < 13; ++k2) re[k2] = im[k2] = 0.0;
+#pragma unroll
+    for (int n2 = 0; n2 < 25; ++n2) {
+#pragma unroll
+      for (int k2 = 0; k2 < 13; ++k2) {
         const double2 w = c_tw[(16 * n2 * k2) % 400];
-        re = fma(y[n2].x, w.x, fma(-y[n2].y, w.y, re));
-        im = fma(y[n2].x, w.y, fma(y[n2].y, w.x, im));
+        re[k2] = fma(y[n2].x, w.x, fma(-y[n2].y, w.y, re[k2]));
+        im[k2] = fma(y[n2].x, w.y, fma(y[n2].y, w.x, im[k2]));
       }
-      xs[f][k1 + 16 * k2] = (float)(re * re + im * im);  // power, bins 0..200
     }
+#pragma unroll
+    for (int k2 = 0; k2 < 13; ++k2)
+      if (k1 + 16 * k2 <= 200) xs[f][k1 + 16 * k2] = (float)(re[k2] * re[k2] + im[k2] * im[k2]);
   }
   __syncthreads();
 
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(256) void mel_frames_kernel(MelArgs a) {
 hipError_t launch_mel(const MelArgs& a, hipStream_t s) {
   if (a.total_frames == 0) return hipSuccess;
   const int64_t blocks = (a.total_frames + FPB - 1) / FPB;
-  hipLaunchKernelGGL(mel_frames_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mel_frames_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
   return hipGetLastError();
 }
 
