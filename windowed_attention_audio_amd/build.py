@@ -66,7 +66,7 @@ def build(verbose=False):
                 print(msg)
     objs = [o for o, _ in results]
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("linking libmt.so failed:\n" + r.stdout + r.stderr)

@@ -530,6 +530,223 @@ hipError_t run_lds(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// Epilogue through LDS for 16-bit outputs (bias, optional GELU).  Written
+// straight from the MFMA layout, each store instruction of a wavefront
+// touches 16 rows x 32 bytes, and with every CU in its epilogue at once the
+// partial-line writes, not the math, set the pace (measured ~7.7 us per
+// 256 x 256 tile).  Instead each wavefront parks its converted fragments in
+// LDS (rows 0-127 of the tile in stage 0, 128-255 in stage 1; 16-byte
+// chunks XOR-swizzled by row), and the workgroup then writes whole rows,
+// 16 bytes per lane, so each instruction covers full 128-byte lines.
+template <typename T, int EPI, int BN, int MI, int NI>
+__device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[MI][NI], uint4* st0,
+                                                uint4* st1, int m0, int n0, int wm, int wn) {
+  static_assert(EPI == EPI_ACT || EPI == EPI_GELU, "16-bit outputs");
+  static_assert(MI * 16 == 128, "one LDS stage per 128 rows");
+  constexpr int WTN = NI * 16;
+  constexpr int CPR = BN / 8;  // 16-byte chunks per output row
+  static_assert(CPR % 8 == 0, "swizzle groups");
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  uint4* half = wm ? st1 : st0;
+  char* hb = (char*)half;
+  __syncthreads();  // every wavefront is done reading operand fragments
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int col = n0 + wn * WTN + 16 * j + 4 * g;
+    const float4 b = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int q = (wn * WTN + 16 * j + 4 * g) >> 3;  // chunk of the 4 values
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = 16 * i + l16;
+      float v0 = acc[i][j][0] + b.x, v1 = acc[i][j][1] + b.y, v2 = acc[i][j][2] + b.z,
+            v3 = acc[i][j][3] + b.w;
+      if constexpr (EPI == EPI_GELU) {
+        v0 = gelu_f(v0);
+        v1 = gelu_f(v1);
+        v2 = gelu_f(v2);
+        v3 = gelu_f(v3);
+      }
+      typedef Elem<T> E;
+      const uint2 w = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
+      *(uint2*)(hb + r * (BN * 2) + ((q ^ (r & 7)) << 4) + ((g & 1) << 3)) = w;
+    }
+  }
+  __syncthreads();
+  // 128 rows x CPR chunks per stage, 512 threads
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const char* src = (const char*)(h ? st1 : st0);
+#pragma unroll
+    for (int it = 0; it < 128 * CPR / 512; ++it) {
+      const int t = it * 512 + threadIdx.x;
+      const int r = t / CPR, q = t % CPR;
+      const int row = m0 + 128 * h + r, col = n0 + 8 * q;
+      const uint4 v = *(const uint4*)(src + r * (BN * 2) + ((q ^ (r & 7)) << 4));
+      if (row < a.M && col < a.N) *(uint4*)((T*)a.C + (int64_t)row * a.ldc + col) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large tiles: 256 x BN (BN = 256, 192 or 128), eight wavefronts of
+// 128 x BN/4, one workgroup per CU (two wavefronts per SIMD).
+//
+// Why: with 128 x 128 tiles the per-CU vector-memory path that feeds the
+// LDS (one 1 KB global_load_lds per 16-plus cycles) is busy for ~1.75 cycles
+// per matrix-core cycle, so the tile, not the matrix cores, sets the pace.
+// A 256 x 256 tile moves half the bytes per FLOP.  The accumulators
+// (128 per lane at BN = 256) stay in AGPRs; A fragments are single-buffered
+// and refilled row by row right behind the MFMAs that last read them, B
+// fragments are double-buffered across K steps, and the second wavefront on
+// each SIMD covers the LDS latency the first one waits on.
+template <typename T, int BN, int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
+  constexpr int BM = 256, WM = 2, WN = 4, NW = 8;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 16, NI = WTN / 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int NBLK = ROWS / 8;  // 1 KB blocks per stage
+  constexpr int BPW = NBLK / NW;  // blocks per wavefront
+  constexpr int RPI = NW * 8;     // rows per load round
+  constexpr int AI = BM / RPI;    // rounds that load A rows
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  static_assert(MI == 8, "eight 16-row fragments per wavefront");
+  static_assert(NBLK % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "load plan");
+  static_assert(WTN % 16 == 0, "wave tile");
+  static_assert(EPI != EPI_SWIGLU || (WTN % 32) == 0, "SwiGLU pairs need 32-column wave tiles");
+
+  __shared__ uint4 st0[ROWS * 8];
+  __shared__ uint4 st1[ROWS * 8];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
+  const int m0 = bm * BM, n0 = bn * BN;
+
+  // DMA plan: block (wave + NW i) holds LDS rows r0 + RPI i; rows < BM are
+  // A rows, the rest B rows.  Lane j fills chunk slot j % 8 of its row with
+  // logical chunk c (the slot XOR the row's swizzle, the same for all i).
+  // Loads go through buffer descriptors, one per round i, based at row
+  // RPI i of the operand and sized to the rows that remain, so rows past M
+  // or N read as zeros and a single offset register serves every round.  K
+  // is a multiple of 128 (checked by the caller): no slice runs past a row's
+  // end.  32-bit offsets: the caller also checks that each operand spans
+  // less than 2 GiB.
+  const int r0 = wave * 8 + (lane >> 3);
+  const int c = (lane & 7) ^ swz(r0);
+  const int ldab = a.lda * (int)sizeof(T), ldbb = a.ldb * (int)sizeof(T);
+  const int va = (m0 + r0) * ldab + c * 16;
+  const int vb = (n0 + r0) * ldbb + c * 16;
+  auto issue = [&](uint4* stage, int kb) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const bool isa = i < AI;
+      const int row = (isa ? i : i - AI) * RPI;
+      const int rows = (isa ? a.M : a.N) - row;
+      const int ld = isa ? ldab : ldbb;
+      const char* base = (const char*)(isa ? a.A : a.B) + (int64_t)row * ld;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows > 0 ? rows * ld : 0, 0x00020000),
+          (lds_ptr_t)(stage + (wave + i * NW) * 64), 16, isa ? va : vb, kb * 128, 0, 0);
+    }
+  };
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int g = lane >> 4, l16 = lane & 15;
+  const int sw = swz(l16);
+  // fragment of K step s (chunk 4 s + g) of tile row r: r % 8 == l16 % 8
+  auto a_idx = [&](int i, int s) { return (wm * WTM + i * 16 + l16) * 8 + ((4 * s + g) ^ sw); };
+  auto b_idx = [&](int j, int s) { return (BM + wn * WTN + j * 16 + l16) * 8 + ((4 * s + g) ^ sw); };
+
+  uint4 fa[MI];
+  uint4 fb0[NI], fb1[NI];
+
+  // K step s of the slice in S with B fragments FB: MFMAs row by row, each
+  // row's A fragment reloaded from (SN, sn) right after its last use, and
+  // the next step's B fragments read into FBN halfway through.
+  auto kstep = [&](const uint4 (&FB)[NI], uint4 (&FBN)[NI], const uint4* SN, int sn, bool more) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) mma16(acc[i][j], FB[j], fa[i], T{});  // C^T tile
+      if (more) {
+        fa[i] = SN[a_idx(i, sn)];
+        if (i == MI / 2 - 1) {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) FBN[j] = SN[b_idx(j, sn)];
+        }
+      }
+    }
+    // Interleave: each row's MFMAs, then that row's reload (left alone, the
+    // scheduler batches every read after every MFMA, all wavefronts of the
+    // workgroup do so in step, and the LDS reads stop overlapping the MFMAs).
+    if (more) {
+#define MT_ROW(NREAD)                                    \
+  __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);    \
+  __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+      MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1 + NI) MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1)
+#undef MT_ROW
+    }
+  };
+  // The barrier that hands slice kb+1 over and frees the stage of slice kb
+  // for slice kb+2: every read of that stage has been issued by now.
+  auto handover = [&](uint4* CUR, bool refill, int kb) {
+    wait_vm(0);  // this wavefront's DMA of slice kb+1 has landed
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0): reads done
+    __builtin_amdgcn_s_barrier();
+    if (refill) issue(CUR, kb + 2);
+  };
+
+  const int nkb = a.K / 64;  // even
+  issue(st0, 0);
+  issue(st1, 1);
+  wait_vm(BPW);
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < MI; ++i) fa[i] = st0[a_idx(i, 0)];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) fb0[j] = st0[b_idx(j, 0)];
+
+  // Slices kb (stage 0) and kb+1 (stage 1) per iteration; inside the loop
+  // slices kb+2 and kb+3 exist, so the body has no branch.  The last two
+  // slices are peeled.
+  for (int kb = 0; kb < nkb - 2; kb += 2) {
+    kstep(fb0, fb1, st0, 1, true);
+    handover(st0, true, kb);
+    kstep(fb1, fb0, st1, 0, true);
+    kstep(fb0, fb1, st1, 1, true);
+    handover(st1, true, kb + 1);
+    kstep(fb1, fb0, st0, 0, true);
+  }
+  kstep(fb0, fb1, st0, 1, true);
+  handover(st0, false, nkb - 2);
+  kstep(fb1, fb0, st1, 0, true);
+  kstep(fb0, fb1, st1, 1, true);
+  kstep(fb1, fb0, st1, 0, false);
+
+  if constexpr (EPI == EPI_ACT || EPI == EPI_GELU)
+    epilogue_staged<T, EPI, BN, MI, NI>(a, acc, st0, st1, m0, n0, wm, wn);
+  else
+    epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
+}
+
+template <typename T, int BN, int EPI>
+hipError_t run_w8(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_w8_kernel<T, BN, EPI>), dim3(tiles), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int BM, int BN, int EPI, bool CONV>
 hipError_t run(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -546,7 +763,29 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
     // matrix work.  (Measured on the encoder's shapes: 620-780 TFLOP/s.)
     // The convolutions keep the register-staged kernel below: its gather
     // measured faster (2.6 ms vs 3.3 ms for the 16 x 30 s conv2).
-    if constexpr (!CONV) return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
+    if constexpr (!CONV) {
+      // Wide outputs: 256-row tiles where K allows them (whole 128-wide K
+      // pairs, operands addressable with 32-bit offsets), 256 or 192 wide by
+      // how full the last round of tiles leaves the CUs (measured at
+      // M = 6000: N = 5120 -> 256 x 256, 855 TFLOP/s; N = 3840 -> 256 x 192,
+      // 793 TFLOP/s; 128 x 128: 670 / 651).  Narrow outputs (N = 1280: too
+      // few wide tiles to fill 256 CUs): 256 x 128 tiles of eight 64 x 64
+      // wavefronts (778 TFLOP/s at K = 5120 against 756 for 128 x 128).
+      const bool w8 = a.K % 128 == 0 && (int64_t)a.M * a.lda * 2 < (1ll << 31) &&
+                      (int64_t)a.N * a.ldb * 2 < (1ll << 31);
+      if (w8 && a.N >= 2048) {
+        if constexpr (EPI != EPI_SWIGLU) {
+          const int tm = (a.M + 255) / 256;
+          const int t256 = tm * ((a.N + 255) / 256), t192 = tm * ((a.N + 191) / 192);
+          const double e256 = t256 / (256.0 * ((t256 + 255) / 256));
+          const double e192 = t192 / (256.0 * ((t192 + 255) / 256));
+          if (e192 > 1.15 * e256) return run_w8<T, 192, EPI>(a, s);
+        }
+        return run_w8<T, 256, EPI>(a, s);
+      }
+      if (a.M >= 2048) return run_lds<T, 256, 128, 4, 2, 2, EPI, CONV>(a, s);
+      return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
+    }
   }
   if constexpr (CONV) {
     // output channels 480 = 3 x 160
