@@ -194,6 +194,195 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
   }
 }
 
+// 16-bit operands, same algorithm with a different staging:
+//  * K and V of the (window, head) go to LDS by buffer loads straight into
+//    LDS (no trip through registers, no transposing stores).  The buffer
+//    descriptor spans exactly the window's w rows, so rows >= w read as
+//    zeros.  Both are kept row-major (128 bytes per key), 16-byte chunk c of
+//    key row r at chunk slot c ^ (r & 7).
+//  * V^T fragments for O^T = V^T P^T come from transposing LDS reads
+//    (ds_read_b64_tr_b16).  Within each 16-lane group G, element j of lane i
+//    of that read is element i & 3 of the 8-byte vector addressed by lane
+//    4 j + (i >> 2) of the same group.  So to give lane (d, g) the keys
+//    32 u + 4 g + e (and + 16) of dimension d -- the order in which the P
+//    fragment holds its probabilities -- lane (g, s) addresses key row
+//    kc 64 + 32 u + 4 g + (s >> 2) (+ 16), columns 16 nd + 4 (s & 3) .. + 3.
+//  * each wavefront's Q fragments are read from global memory before the
+//    wait for the staging, one query group ahead.
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr4_t* tr_ptr_t;
+typedef __attribute__((address_space(3))) void* lds_vptr_t;
+
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void wattn16_kernel(AttnArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  constexpr int HD = 64, CPR = 8;  // 8 chunks of 8 elements per 128-byte row
+  extern __shared__ uint4 smem[];
+  const int wpad = a.wpad;
+  uint4* Ks = smem;               // [wpad][8] chunks
+  uint4* Vs = smem + wpad * CPR;  // [wpad][8] chunks
+
+  const int win = blockIdx.x;
+  const int head = blockIdx.y;
+  const int sq = find_seq(a.cu_win, a.nseq, win);
+  const int kwin = win - a.cu_win[sq];
+  const int N = a.cu_rows[sq + 1] - a.cu_rows[sq];
+  const int s0 = a.cu_rows[sq] + kwin * a.window;
+  const int w = min(a.window, N - kwin * a.window);
+  const int ldb = 3 * a.D * (int)sizeof(T);  // bytes per qkv row
+  const char* base = (const char*)a.qkv + (int64_t)s0 * ldb;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // ---- DMA: 1 KB blocks of 8 rows; blocks [0, wpad/8) are K, the rest V
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, w * ldb, 0x00020000);
+    const int nb = wpad / 8;
+    const int r8 = lane >> 3, slot = lane & 7;
+    for (int b = wave; b < 2 * nb; b += 4) {
+      const bool isv = b >= nb;
+      const int r = 8 * (isv ? b - nb : b) + r8;
+      const int c = slot ^ (r & 7);
+      const int col = (isv ? 2 : 1) * a.D + head * HD + c * 8;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr_t)(smem + b * 64), 16,
+                                               r * ldb + col * (int)sizeof(T), 0, 0, 0);
+    }
+  }
+
+  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+  const int nqg = (w + 15) >> 4;
+  const int nkc = (w + 63) >> 6;
+  const T* Qg = (const T*)base + head * HD;
+  const int ldq = 3 * a.D;
+
+  auto load_q = [&](int qg, uint4 (&qf)[2]) {
+    const int q = qg * 16 + l16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      qf[s] = make_uint4(0, 0, 0, 0);
+      if (qg < nqg && q < w) qf[s] = *(const uint4*)(Qg + (int64_t)q * ldq + (4 * s + g) * 8);
+    }
+  };
+  uint4 qn[2];
+  load_q(wave, qn);
+
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's DMA and Q loads
+  __syncthreads();
+
+  for (int qg = wave; qg < nqg; qg += 4) {
+    const int q = qg * 16 + l16;  // this lane's query row (window-local)
+    uint4 qf[2] = {qn[0], qn[1]};
+    load_q(qg + 4, qn);  // next group, in flight during this one
+    float m_run = -INFINITY, l_part = 0.f;
+    f32x4 o[4];
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kc = 0; kc < nkc; ++kc) {
+      f32x4 st[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int kvr = kc * 64 + t * 16 + l16;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint4 kf = Ks[kvr * CPR + ((4 * s + g) ^ (kvr & 7))];
+          mma16(st[t], kf, qf[s], T{});
+        }
+      }
+      // lane holds S^T[kv = kc*64 + 16t + 4g + e][q]; scale, mask, row max
+      float cmax = -INFINITY;
+      if (kc * 64 + 64 <= w) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            st[t][e] *= sl2;
+            cmax = fmaxf(cmax, st[t][e]);
+          }
+      } else {  // last, partial chunk: keys >= w drop out
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kv = kc * 64 + t * 16 + 4 * g + e;
+            const float v = kv < w ? st[t][e] * sl2 : -INFINITY;
+            st[t][e] = v;
+            cmax = fmaxf(cmax, v);
+          }
+      }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2f(st[t][e] - m_new);
+          st[t][e] = p;
+          psum += p;
+        }
+      l_part = l_part * alpha + psum;
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
+
+      // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]
+      typedef Elem<T> E;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint4 pf;
+        pf.x = pack2(E::from_f(st[2 * u][0]), E::from_f(st[2 * u][1]));
+        pf.y = pack2(E::from_f(st[2 * u][2]), E::from_f(st[2 * u][3]));
+        pf.z = pack2(E::from_f(st[2 * u + 1][0]), E::from_f(st[2 * u + 1][1]));
+        pf.w = pack2(E::from_f(st[2 * u + 1][2]), E::from_f(st[2 * u + 1][3]));
+        const int r1 = kc * 64 + 32 * u + 4 * g + (l16 >> 2), r2 = r1 + 16;
+#pragma unroll
+        for (int nd = 0; nd < 4; ++nd) {
+          const int c = 2 * nd + ((l16 & 3) >> 1), half = (l16 & 1) * 8;  // bytes within chunk
+          const tr4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (tr_ptr_t)((char*)(Vs + r1 * CPR + (c ^ (r1 & 7))) + half));
+          const tr4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (tr_ptr_t)((char*)(Vs + r2 * CPR + (c ^ (r2 & 7))) + half));
+          const uint2 w1 = __builtin_bit_cast(uint2, v1), w2 = __builtin_bit_cast(uint2, v2);
+          mma16(o[nd], make_uint4(w1.x, w1.y, w2.x, w2.y), pf, T{});
+        }
+      }
+    }
+    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (q < w) {
+      T* orow = (T*)a.out + (int64_t)(s0 + q) * a.D + head * HD;
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) {
+        const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
+        typedef Elem<T> E;
+        uint2 pk;
+        pk.x = pack2(E::from_f(o[nd][0] * inv), E::from_f(o[nd][1] * inv));
+        pk.y = pack2(E::from_f(o[nd][2] * inv), E::from_f(o[nd][3] * inv));
+        *(uint2*)(orow + d0) = pk;
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t run_attn16(const AttnArgs& a, hipStream_t s) {
+  if (a.n_windows == 0) return hipSuccess;
+  const size_t lds = (size_t)a.wpad * 2 * 128;  // K and V, 128 bytes per key each
+  hipError_t e = hipFuncSetAttribute((const void*)wattn16_kernel<T>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(wattn16_kernel<T>, dim3(a.n_windows, a.n_heads), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t run_attn(const AttnArgs& a, hipStream_t s) {
   if (a.n_windows == 0) return hipSuccess;
@@ -208,8 +397,8 @@ hipError_t run_attn(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
-  if (dtype == DT_BF16) return run_attn<bf16_t>(a, s);
-  if (dtype == DT_F16) return run_attn<f16_t>(a, s);
+  if (dtype == DT_BF16) return run_attn16<bf16_t>(a, s);
+  if (dtype == DT_F16) return run_attn16<f16_t>(a, s);
   return run_attn<float>(a, s);
 }
 
