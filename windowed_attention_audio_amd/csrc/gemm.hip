@@ -543,14 +543,16 @@ template <typename T, int EPI, int BN, int MI, int NI>
 __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[MI][NI], uint4* st0,
                                                 uint4* st1, int m0, int n0, int wm, int wn) {
   static_assert(EPI == EPI_ACT || EPI == EPI_GELU, "16-bit outputs");
-  static_assert(MI * 16 == 128, "one LDS stage per 128 rows");
-  constexpr int WTN = NI * 16;
+  static_assert(MI == 8 || MI == 4, "wave tiles of 128 or 64 rows");
+  constexpr int WTM = MI * 16, WTN = NI * 16;
+  constexpr int WPS = 128 / WTM;  // wavefront rows per LDS stage
   constexpr int CPR = BN / 8;  // 16-byte chunks per output row
   static_assert(CPR % 8 == 0, "swizzle groups");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, l16 = lane & 15;
-  uint4* half = wm ? st1 : st0;
+  uint4* half = wm / WPS ? st1 : st0;
   char* hb = (char*)half;
+  const int rw = (wm % WPS) * WTM;  // first row of this wavefront inside its stage
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -559,7 +561,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
     const int q = (wn * WTN + 16 * j + 4 * g) >> 3;  // chunk of the 4 values
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int r = 16 * i + l16;
+      const int r = rw + 16 * i + l16;
       float v0 = acc[i][j][0] + b.x, v1 = acc[i][j][1] + b.y, v2 = acc[i][j][2] + b.z,
             v3 = acc[i][j][3] + b.w;
       if constexpr (EPI == EPI_GELU) {
@@ -601,9 +603,9 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
 // and refilled row by row right behind the MFMAs that last read them, B
 // fragments are double-buffered across K steps, and the second wavefront on
 // each SIMD covers the LDS latency the first one waits on.
-template <typename T, int BN, int EPI>
+template <typename T, int BN, int WM, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
-  constexpr int BM = 256, WM = 2, WN = 4, NW = 8;
+  constexpr int BM = 256, NW = 8, WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 16, NI = WTN / 16;
   constexpr int ROWS = BM + BN;
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   constexpr int RPI = NW * 8;     // rows per load round
   constexpr int AI = BM / RPI;    // rounds that load A rows
   static_assert(sizeof(T) == 2, "16-bit operands");
-  static_assert(MI == 8, "eight 16-row fragments per wavefront");
+  static_assert(MI == 8 || MI == 4, "128- or 64-row wave tiles");
   static_assert(NBLK % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "load plan");
   static_assert(WTN % 16 == 0, "wave tile");
   static_assert(EPI != EPI_SWIGLU || (WTN % 32) == 0, "SwiGLU pairs need 32-column wave tiles");
@@ -693,7 +695,11 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
 #define MT_ROW(NREAD)                                    \
   __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);    \
   __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-      MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1 + NI) MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1)
+      if constexpr (MI == 8) {
+        MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1 + NI) MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1)
+      } else {
+        MT_ROW(1) MT_ROW(1 + NI) MT_ROW(1) MT_ROW(1)
+      }
 #undef MT_ROW
     }
   };
@@ -739,11 +745,11 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
     epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
 }
 
-template <typename T, int BN, int EPI>
+template <typename T, int BN, int EPI, int WM = 2>
 hipError_t run_w8(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_w8_kernel<T, BN, EPI>), dim3(tiles), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((gemm_w8_kernel<T, BN, WM, EPI>), dim3(tiles), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -769,8 +775,10 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
       // how full the last round of tiles leaves the CUs (measured at
       // M = 6000: N = 5120 -> 256 x 256, 855 TFLOP/s; N = 3840 -> 256 x 192,
       // 793 TFLOP/s; 128 x 128: 670 / 651).  Narrow outputs (N = 1280: too
-      // few wide tiles to fill 256 CUs): 256 x 128 tiles of eight 64 x 64
-      // wavefronts (778 TFLOP/s at K = 5120 against 756 for 128 x 128).
+      // few wide tiles to fill 256 CUs): the same kernel with 256 x 128
+      // tiles of eight 64 x 64 wavefronts (K = 5120: 847 TFLOP/s with a
+      // 16-bit epilogue, 730 with the fp32 residual add, against 752 / 622
+      // for 128 x 128; K = 1280: 740 / 595 against 617 / 541).
       const bool w8 = a.K % 128 == 0 && (int64_t)a.M * a.lda * 2 < (1ll << 31) &&
                       (int64_t)a.N * a.ldb * 2 < (1ll << 31);
       if (w8 && a.N >= 2048) {
@@ -783,6 +791,7 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
         }
         return run_w8<T, 256, EPI>(a, s);
       }
+      if (w8 && a.M >= 2048) return run_w8<T, 128, EPI, 4>(a, s);
       if (a.M >= 2048) return run_lds<T, 256, 128, 4, 2, 2, EPI, CONV>(a, s);
       return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
     }
