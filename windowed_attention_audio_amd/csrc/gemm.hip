@@ -547,7 +547,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
   constexpr int WTM = MI * 16, WTN = NI * 16;
   constexpr int WPS = 128 / WTM;  // wavefront rows per LDS stage
   constexpr int CPR = BN / 8;  // 16-byte chunks per output row
-  static_assert(CPR % 8 == 0, "swizzle groups");
+  static_assert(CPR % 4 == 0, "swizzle groups");
+  constexpr int SWM = CPR % 8 == 0 ? 7 : 3;  // chunks are swizzled within aligned groups
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, l16 = lane & 15;
   uint4* half = wm / WPS ? st1 : st0;
@@ -572,7 +573,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
       }
       typedef Elem<T> E;
       const uint2 w = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
-      *(uint2*)(hb + r * (BN * 2) + ((q ^ (r & 7)) << 4) + ((g & 1) << 3)) = w;
+      *(uint2*)(hb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }
   }
   __syncthreads();
@@ -585,7 +586,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
       const int t = it * 512 + threadIdx.x;
       const int r = t / CPR, q = t % CPR;
       const int row = m0 + 128 * h + r, col = n0 + 8 * q;
-      const uint4 v = *(const uint4*)(src + r * (BN * 2) + ((q ^ (r & 7)) << 4));
+      const uint4 v = *(const uint4*)(src + r * (BN * 2) + ((q ^ (r & SWM)) << 4));
       if (row < a.M && col < a.N) *(uint4*)((T*)a.C + (int64_t)row * a.ldc + col) = v;
     }
   }
@@ -603,19 +604,21 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
 // and refilled row by row right behind the MFMAs that last read them, B
 // fragments are double-buffered across K steps, and the second wavefront on
 // each SIMD covers the LDS latency the first one waits on.
-template <typename T, int BN, int WM, int EPI>
+template <typename T, int BN, int WM, int EPI, bool CONV>
 __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   constexpr int BM = 256, NW = 8, WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 16, NI = WTN / 16;
-  constexpr int ROWS = BM + BN;
+  constexpr int RPI = NW * 8;     // rows per load round
+  constexpr int BNP = (BN + RPI - 1) / RPI * RPI;  // B rows loaded (the rest of the
+                                                   // last round: next tile's, unused)
+  constexpr int ROWS = BM + BNP;
   constexpr int NBLK = ROWS / 8;  // 1 KB blocks per stage
   constexpr int BPW = NBLK / NW;  // blocks per wavefront
-  constexpr int RPI = NW * 8;     // rows per load round
   constexpr int AI = BM / RPI;    // rounds that load A rows
   static_assert(sizeof(T) == 2, "16-bit operands");
   static_assert(MI == 8 || MI == 4, "128- or 64-row wave tiles");
-  static_assert(NBLK % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "load plan");
+  static_assert(NBLK % NW == 0 && BM % RPI == 0, "load plan");
   static_assert(WTN % 16 == 0, "wave tile");
   static_assert(EPI != EPI_SWIGLU || (WTN % 32) == 0, "SwiGLU pairs need 32-column wave tiles");
 
@@ -626,7 +629,19 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (a.N + BN - 1) / BN;
-  const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
+  // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin;
+  // for narrow outputs (few N tiles per row of A) and the convolutions,
+  // renumber so that each XCD runs a contiguous range of tiles (row-major:
+  // the N tiles of one row of A, then the next row) and the A rows -- and,
+  // for the convolution, the overlapping input rows -- stay in one L2
+  // (measured: conv2 2.31 -> 2.19 ms, fc2 3.46 -> 3.30, o 1.21 -> 1.16 per
+  // 16 x 30 s step; the wide GEMMs did not gain).
+  int tile = blockIdx.x;
+  if (CONV || BN < 192) {
+    const int nt = gridDim.x, q = nt / 8, r = nt % 8, x = tile % 8, idx = tile / 8;
+    tile = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
+  }
+  const int bm = tile / tiles_n, bn = tile % tiles_n;
   const int m0 = bm * BM, n0 = bn * BN;
 
   // DMA plan: block (wave + NW i) holds LDS rows r0 + RPI i; rows < BM are
@@ -643,10 +658,69 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   const int ldab = a.lda * (int)sizeof(T), ldbb = a.ldb * (int)sizeof(T);
   const int va = (m0 + r0) * ldab + c * 16;
   const int vb = (n0 + r0) * ldbb + c * 16;
+
+  // Implicit-GEMM convolution (3x3, stride 2, padding 1, channels-last
+  // input [t][f][C]): A row m is output position (t, f) = (m / Fout, m %
+  // Fout) of its sequence and A column k is tap k / C (= 3 df + dt), channel
+  // k % C.  C is a multiple of 8, so each lane's 16-byte chunk lies inside one
+  // tap; lanes of one K slice may straddle two.  One descriptor per
+  // workgroup, based at the first input time row the tile can touch and
+  // ending at the end of the input; a tap outside the sequence or the
+  // frequency range, and k >= K in the last slice, get an offset past the
+  // end and read zeros.
+  int cv_off[CONV ? AI : 1];        // input position (2t, 2f) of the row, bytes from the base
+  uint32_t cv_ok[CONV ? AI : 1];    // bit dt: time tap dt inside; bit 3 + df: frequency tap df inside
+  const char* cv_base = nullptr;
+  int cv_bytes = 0;
+  if constexpr (CONV) {
+    const int pos_b = a.conv_C * (int)sizeof(T);  // bytes per input position
+    const int tg0 = m0 / a.conv_Fout;
+    const int sq0 = find_seq(a.cu_out, a.nseq, tg0);
+    const int t_base = a.cu_in[sq0] + max(2 * (tg0 - a.cu_out[sq0]) - 1, 0);
+    const int64_t row_b = (int64_t)a.conv_Fin * pos_b;
+    cv_base = (const char*)a.A + t_base * row_b;
+    const int64_t left = ((int64_t)a.cu_in[a.nseq] - t_base) * row_b;
+    cv_bytes = (int)min(left, (int64_t)0x7fffffff);
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int m = m0 + r0 + RPI * i;
+      cv_off[i] = 0;
+      cv_ok[i] = 0;
+      if (m < a.M) {
+        const int tg = m / a.conv_Fout, f2 = m - tg * a.conv_Fout;
+        const int sq = find_seq(a.cu_out, a.nseq, tg);
+        const int t2 = tg - a.cu_out[sq], Tin = a.cu_in[sq + 1] - a.cu_in[sq];
+        cv_off[i] = (int)((((int64_t)a.cu_in[sq] + 2 * t2 - t_base) * a.conv_Fin + 2 * f2) * pos_b);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          if (2 * t2 + d - 1 >= 0 && 2 * t2 + d - 1 < Tin) cv_ok[i] |= 1u << d;
+          if (2 * f2 + d - 1 >= 0 && 2 * f2 + d - 1 < a.conv_Fin) cv_ok[i] |= 8u << d;
+        }
+      }
+    }
+  }
+
   auto issue = [&](uint4* stage, int kb) {
+    int cdelta = 0;
+    uint32_t need = 0;
+    if constexpr (CONV) {
+      const int k = kb * 64 + c * 8;  // first column of this lane's chunk
+      const int tap = k / a.conv_C, ch = k - tap * a.conv_C;
+      const int df = tap / 3, dt = tap - 3 * df;
+      cdelta = ((dt - 1) * a.conv_Fin + (df - 1)) * a.conv_C * (int)sizeof(T) + ch * (int)sizeof(T);
+      need = k < a.K ? (1u << dt) | (8u << df) : 0xffffffffu;  // past K: never satisfied
+    }
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const bool isa = i < AI;
+      if (CONV && isa) {
+        const uint32_t voff = (cv_ok[CONV ? i : 0] & need) == need ? (uint32_t)(cv_off[CONV ? i : 0] + cdelta)
+                                                                   : 0x80000000u;  // past any descriptor
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            __builtin_amdgcn_make_buffer_rsrc((void*)cv_base, (short)0, cv_bytes, 0x00020000),
+            (lds_ptr_t)(stage + (wave + i * NW) * 64), 16, (int)voff, 0, 0, 0);
+        continue;
+      }
       const int row = (isa ? i : i - AI) * RPI;
       const int rows = (isa ? a.M : a.N) - row;
       const int ld = isa ? ldab : ldbb;
@@ -712,7 +786,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
     if (refill) issue(CUR, kb + 2);
   };
 
-  const int nkb = a.K / 64;  // even
+  const int nkb = CONV ? (a.K + 127) / 128 * 2 : a.K / 64;  // even; conv pads with zero slices
   issue(st0, 0);
   issue(st1, 1);
   wait_vm(BPW);
@@ -739,17 +813,18 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   kstep(fb0, fb1, st1, 1, true);
   kstep(fb1, fb0, st1, 0, false);
 
+  static_assert(128 * BN * 2 <= ROWS * 128, "staged output fits a stage");
   if constexpr (EPI == EPI_ACT || EPI == EPI_GELU)
     epilogue_staged<T, EPI, BN, MI, NI>(a, acc, st0, st1, m0, n0, wm, wn);
   else
     epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
 }
 
-template <typename T, int BN, int EPI, int WM = 2>
+template <typename T, int BN, int EPI, int WM = 2, bool CONV = false>
 hipError_t run_w8(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_w8_kernel<T, BN, WM, EPI>), dim3(tiles), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((gemm_w8_kernel<T, BN, WM, EPI, CONV>), dim3(tiles), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -764,11 +839,13 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
 template <typename T, int EPI, bool CONV>
 hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    // 128-row tiles, four wavefronts of 64 x 64 (x 80): two workgroups per
-    // CU (64 / 72 KB of LDS each), so one's DMA wait overlaps the other's
-    // matrix work.  (Measured on the encoder's shapes: 620-780 TFLOP/s.)
-    // The convolutions keep the register-staged kernel below: its gather
-    // measured faster (2.6 ms vs 3.3 ms for the 16 x 30 s conv2).
+    // Convolutions: the eight-wavefront kernel with the tap gather, 256 x 160
+    // tiles of 64 x 80 wavefronts (480 output channels = 3 tiles; the
+    // 256 x 256 variant spills with the gather's per-row state).
+    if constexpr (CONV) {
+      if (a.conv_C % 8 == 0 && (int64_t)a.N * a.ldb * 2 < (1ll << 31))
+        return run_w8<T, 160, EPI, 4, true>(a, s);
+    }
     if constexpr (!CONV) {
       // Wide outputs: 256-row tiles where K allows them (whole 128-wide K
       // pairs, operands addressable with 32-bit offsets), 256 or 192 wide by
