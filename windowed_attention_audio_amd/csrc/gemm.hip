@@ -536,11 +536,75 @@ hipError_t run_lds(const GemmArgs& a, hipStream_t s) {
 // touches 16 rows x 32 bytes, and with every CU in its epilogue at once the
 // partial-line writes, not the math, set the pace (measured ~7.7 us per
 // 256 x 256 tile).  Instead each wavefront parks its converted fragments in
+// LDS -- rows 64 q .. 64 q + 63 of the tile in stage q, 16-byte chunks
+// XOR-swizzled by row -- and the workgroup then writes whole rows, 16 bytes
+// per lane, so each instruction covers full 128-byte lines.
+template <typename T, int EPI, int BN, int MI, int NI>
+__device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)[MI][NI], uint4* st0,
+                                                uint4* st1, uint4* st2, uint4* st3, int m0, int n0,
+                                                int wm, int wn) {
+  auto stage = [&](int q) { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
+  static_assert(EPI == EPI_ACT || EPI == EPI_GELU, "16-bit outputs");
+  static_assert(MI == 8 || MI == 4, "wave tiles of 128 or 64 rows");
+  constexpr int WTM = MI * 16, WTN = NI * 16;
+  constexpr int CPR = BN / 8;  // 16-byte chunks per output row
+  static_assert(CPR % 4 == 0, "swizzle groups");
+  constexpr int SWM = CPR % 8 == 0 ? 7 : 3;  // chunks are swizzled within aligned groups
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  __syncthreads();  // every wavefront is done reading operand fragments
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int R = wm * WTM + 16 * i;  // first tile row of fragment row i
+    char* qb = (char*)stage(R >> 6);
+    const int r = (R & 63) + l16;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int col = n0 + wn * WTN + 16 * j + 4 * g;
+      const float4 b = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int q = (wn * WTN + 16 * j + 4 * g) >> 3;  // chunk of the 4 values
+      float v0 = acc[i][j][0] + b.x, v1 = acc[i][j][1] + b.y, v2 = acc[i][j][2] + b.z,
+            v3 = acc[i][j][3] + b.w;
+      if constexpr (EPI == EPI_GELU) {
+        v0 = gelu_f(v0);
+        v1 = gelu_f(v1);
+        v2 = gelu_f(v2);
+        v3 = gelu_f(v3);
+      }
+      typedef Elem<T> E;
+      const uint2 w = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
+      *(uint2*)(qb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
+    }
+  }
+  __syncthreads();
+  // 64 rows x CPR chunks per stage, 512 threads
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const char* src = (const char*)stage(h);
+#pragma unroll
+    for (int it = 0; it < (64 * CPR + 511) / 512; ++it) {
+      const int t = it * 512 + threadIdx.x;
+      if (t < 64 * CPR) {
+        const int r = t / CPR, q = t % CPR;
+        const int row = m0 + 64 * h + r, col = n0 + 8 * q;
+        const uint4 v = *(const uint4*)(src + r * (BN * 2) + ((q ^ (r & SWM)) << 4));
+        if (row < a.M && col < a.N) *(uint4*)((T*)a.C + (int64_t)row * a.ldc + col) = v;
+      }
+    }
+  }
+}
+
+// Epilogue through LDS for 16-bit outputs (bias, optional GELU), two-stage
+// variant (rows 0-127 of the tile in stage 0, 128-255 in stage 1).  Written
+// straight from the MFMA layout, each store instruction of a wavefront
+// touches 16 rows x 32 bytes, and with every CU in its epilogue at once the
+// partial-line writes, not the math, set the pace (measured ~7.7 us per
+// 256 x 256 tile).  Instead each wavefront parks its converted fragments in
 // LDS (rows 0-127 of the tile in stage 0, 128-255 in stage 1; 16-byte
 // chunks XOR-swizzled by row), and the workgroup then writes whole rows,
 // 16 bytes per lane, so each instruction covers full 128-byte lines.
 template <typename T, int EPI, int BN, int MI, int NI>
-__device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[MI][NI], uint4* st0,
+__device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)[MI][NI], uint4* st0,
                                                 uint4* st1, int m0, int n0, int wm, int wn) {
   static_assert(EPI == EPI_ACT || EPI == EPI_GELU, "16-bit outputs");
   static_assert(MI == 8 || MI == 4, "wave tiles of 128 or 64 rows");
@@ -815,7 +879,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
 
   static_assert(128 * BN * 2 <= ROWS * 128, "staged output fits a stage");
   if constexpr (EPI == EPI_ACT || EPI == EPI_GELU)
-    epilogue_staged<T, EPI, BN, MI, NI>(a, acc, st0, st1, m0, n0, wm, wn);
+    epilogue_staged2<T, EPI, BN, MI, NI>(a, acc, st0, st1, m0, n0, wm, wn);
   else
     epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
 }
@@ -825,6 +889,264 @@ hipError_t run_w8(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_w8_kernel<T, BN, WM, EPI, CONV>), dim3(tiles), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The same 256-row eight-wavefront design with K in slices of 32 (one MFMA
+// K step) through four LDS stages, for the narrow outputs (N tiles of 128
+// or 160: o-proj, fc2, the convolutions).  A slice's DMA is issued three
+// steps before its fragments are read (global loads under full load take
+// ~2 us, more than the ~1.5 us the two-stage pipeline of 64-wide slices
+// gives them); the price is a barrier every K step instead of every two,
+// which the wide tiles (32 MFMAs per wavefront per step) did not recover:
+// measured per 16 x 30 s step, conv2 2.19 -> 1.98 ms, fc2 3.27 -> 3.08 ms,
+// but fc1 3.09 -> 3.34 and qkv 2.05 -> 2.37, so those keep two stages.
+// Rows are 64 bytes (4 chunks, chunk slot c ^ ((r >> 2) & 3)), so a
+// slice's DMA is issued three steps before its fragments are read: global
+// loads under full load take ~2 us, more than the 1.5 us that a two-stage
+// pipeline of 64-wide slices left them.
+template <typename T, int BN, int WM, int EPI, bool CONV>
+__global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
+  constexpr int BM = 256, NW = 8, WN = NW / WM;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 16, NI = WTN / 16;
+  constexpr int RPB = 16;                          // rows per 1 KB block (64-byte rows)
+  constexpr int RPI = NW * RPB;                    // rows per load round
+  constexpr int AI = BM / RPI;                     // rounds that load A rows
+  constexpr int BNP = (BN + RPB - 1) / RPB * RPB;  // B rows loaded
+  constexpr int NBLK = (BM + BNP) / RPB;           // 1 KB blocks of operands per stage
+  constexpr int BPW = (NBLK + NW - 1) / NW;        // blocks per wavefront (the last
+                                                   // round's spare ones load zeros)
+  constexpr int SROWS = BPW * NW * RPB;            // rows per stage
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  static_assert(MI == 8 || MI == 4, "128- or 64-row wave tiles");
+  static_assert(BM % RPI == 0, "load plan");
+  static_assert(WTN % 16 == 0, "wave tile");
+  static_assert(EPI != EPI_SWIGLU || (WTN % 32) == 0, "SwiGLU pairs need 32-column wave tiles");
+  static_assert(64 * BN * 2 <= SROWS * 64, "a quarter of the staged output fits a stage");
+
+  __shared__ uint4 st0[SROWS * 4];
+  __shared__ uint4 st1[SROWS * 4];
+  __shared__ uint4 st2[SROWS * 4];
+  __shared__ uint4 st3[SROWS * 4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin;
+  // for narrow outputs (few N tiles per row of A) and the convolutions,
+  // renumber so that each XCD runs a contiguous range of tiles (row-major:
+  // the N tiles of one row of A, then the next row) and the A rows -- and,
+  // for the convolution, the overlapping input rows -- stay in one L2
+  // (measured: conv2 2.31 -> 2.19 ms, fc2 3.46 -> 3.30, o 1.21 -> 1.16 per
+  // 16 x 30 s step; the wide GEMMs did not gain).
+  int tile = blockIdx.x;
+  if (CONV || BN < 192) {
+    const int nt = gridDim.x, q = nt / 8, r = nt % 8, x = tile % 8, idx = tile / 8;
+    tile = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
+  }
+  const int bm = tile / tiles_n, bn = tile % tiles_n;
+  const int m0 = bm * BM, n0 = bn * BN;
+
+  // DMA plan: block (wave + NW i) of a stage holds LDS rows r0 + RPI i
+  // (64-byte rows, 4 chunks of 8 elements); rows < BM are A rows, the next
+  // BNP are B rows, the rest (spare blocks) receive zeros.  Lane j fills chunk
+  // slot j % 4 of its row with logical chunk c = slot ^ swz(row), swz(r) =
+  // (r >> 2) & 3, the same for all i; a 16-row fragment read of one chunk is
+  // then conflict-free.  Loads go through buffer descriptors, one per round,
+  // based at row RPI i of the operand and sized to the rows that remain, so
+  // rows past M or N read as zeros and one offset register serves every
+  // round.  K is a multiple of 128 (checked by the caller): no slice runs
+  // past a row's end.  32-bit offsets: the caller also checks that each
+  // operand spans less than 2 GiB.
+  const int r0 = wave * RPB + (lane >> 2);
+  const int c = (lane & 3) ^ ((r0 >> 2) & 3);
+  const int ldab = a.lda * (int)sizeof(T), ldbb = a.ldb * (int)sizeof(T);
+  const int va = (m0 + r0) * ldab + c * 16;
+  const int vb = (n0 + r0) * ldbb + c * 16;
+
+  // Implicit-GEMM convolution (3x3, stride 2, padding 1, channels-last
+  // input [t][f][C]): A row m is output position (t, f) = (m / Fout, m %
+  // Fout) of its sequence and A column k is tap k / C (= 3 df + dt), channel
+  // k % C.  C is a multiple of 8, so each lane's 16-byte chunk lies inside one
+  // tap; lanes of one K slice may straddle two.  One descriptor per
+  // workgroup, based at the first input time row the tile can touch and
+  // ending at the end of the input; a tap outside the sequence or the
+  // frequency range, and k >= K in the last slices, get an offset past the
+  // end and read zeros.
+  int cv_off[CONV ? AI : 1];        // input position (2t, 2f) of the row, bytes from the base
+  uint32_t cv_ok[CONV ? AI : 1];    // bit dt: time tap dt inside; bit 3 + df: frequency tap df inside
+  const char* cv_base = nullptr;
+  int cv_bytes = 0;
+  if constexpr (CONV) {
+    const int pos_b = a.conv_C * (int)sizeof(T);  // bytes per input position
+    const int tg0 = m0 / a.conv_Fout;
+    const int sq0 = find_seq(a.cu_out, a.nseq, tg0);
+    const int t_base = a.cu_in[sq0] + max(2 * (tg0 - a.cu_out[sq0]) - 1, 0);
+    const int64_t row_b = (int64_t)a.conv_Fin * pos_b;
+    cv_base = (const char*)a.A + t_base * row_b;
+    const int64_t left = ((int64_t)a.cu_in[a.nseq] - t_base) * row_b;
+    cv_bytes = (int)min(left, (int64_t)0x7fffffff);
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int m = m0 + r0 + RPI * i;
+      cv_off[i] = 0;
+      cv_ok[i] = 0;
+      if (m < a.M) {
+        const int tg = m / a.conv_Fout, f2 = m - tg * a.conv_Fout;
+        const int sq = find_seq(a.cu_out, a.nseq, tg);
+        const int t2 = tg - a.cu_out[sq], Tin = a.cu_in[sq + 1] - a.cu_in[sq];
+        cv_off[i] = (int)((((int64_t)a.cu_in[sq] + 2 * t2 - t_base) * a.conv_Fin + 2 * f2) * pos_b);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          if (2 * t2 + d - 1 >= 0 && 2 * t2 + d - 1 < Tin) cv_ok[i] |= 1u << d;
+          if (2 * f2 + d - 1 >= 0 && 2 * f2 + d - 1 < a.conv_Fin) cv_ok[i] |= 8u << d;
+        }
+      }
+    }
+  }
+
+  auto issue = [&](uint4* stage, int kb) {
+    int cdelta = 0;
+    uint32_t need = 0;
+    if constexpr (CONV) {
+      const int k = kb * 32 + c * 8;  // first column of this lane's chunk
+      const int tap = k / a.conv_C, ch = k - tap * a.conv_C;
+      const int df = tap / 3, dt = tap - 3 * df;
+      cdelta = ((dt - 1) * a.conv_Fin + (df - 1)) * a.conv_C * (int)sizeof(T) + ch * (int)sizeof(T);
+      need = k < a.K ? (1u << dt) | (8u << df) : 0xffffffffu;  // past K: never satisfied
+    }
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const lds_ptr_t dst = (lds_ptr_t)(stage + (wave + i * NW) * 64);
+      if (i < AI) {
+        if constexpr (CONV) {
+          const uint32_t voff = (cv_ok[i] & need) == need ? (uint32_t)(cv_off[i] + cdelta)
+                                                          : 0x80000000u;  // past any descriptor
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              __builtin_amdgcn_make_buffer_rsrc((void*)cv_base, (short)0, cv_bytes, 0x00020000), dst, 16,
+              (int)voff, 0, 0, 0);
+        } else {
+          const int rows = a.M - i * RPI;
+          const char* base = (const char*)a.A + (int64_t)(i * RPI) * ldab;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows > 0 ? rows * ldab : 0, 0x00020000),
+              dst, 16, va, kb * 64, 0, 0);
+        }
+      } else {
+        // B rounds; blocks past the B rows (spare ones of the last round)
+        // get an empty descriptor and load zeros
+        const int row = (i - AI) * RPI;
+        const int rows = (wave + i * NW) * RPB < BM + BNP ? a.N - row : 0;
+        const char* base = (const char*)a.B + (int64_t)row * ldbb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows > 0 ? rows * ldbb : 0, 0x00020000),
+            dst, 16, vb, kb * 64, 0, 0);
+      }
+    }
+  };
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int g = lane >> 4, l16 = lane & 15;
+  const int sw = (l16 >> 2) & 3;
+  // fragment of chunk g of tile row r (r % 16 == l16): index r * 4 + (g ^ swz(r))
+  auto a_idx = [&](int i) { return (wm * WTM + i * 16 + l16) * 4 + (g ^ sw); };
+  auto b_idx = [&](int j) { return (BM + wn * WTN + j * 16 + l16) * 4 + (g ^ sw); };
+
+  uint4 fa[MI];
+  uint4 fb0[NI], fb1[NI];
+
+  // One K step with B fragments FB: MFMAs row by row, each row's A fragment
+  // reloaded from SN (the next slice's stage) right after its last use, and
+  // the next step's B fragments read into FBN halfway through.
+  auto kstep = [&](const uint4 (&FB)[NI], uint4 (&FBN)[NI], const uint4* SN, bool more) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) mma16(acc[i][j], FB[j], fa[i], T{});  // C^T tile
+      if (more) {
+        fa[i] = SN[a_idx(i)];
+        if (i == MI / 2 - 1) {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) FBN[j] = SN[b_idx(j)];
+        }
+      }
+    }
+    // Interleave: each row's MFMAs, then that row's reload (left alone, the
+    // scheduler batches every read after every MFMA, all wavefronts of the
+    // workgroup do so in step, and the LDS reads stop overlapping the MFMAs).
+    if (more) {
+#define MT_ROW(NREAD)                                    \
+  __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);    \
+  __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+      if constexpr (MI == 8) {
+        MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1 + NI) MT_ROW(1) MT_ROW(1) MT_ROW(1) MT_ROW(1)
+      } else {
+        MT_ROW(1) MT_ROW(1 + NI) MT_ROW(1) MT_ROW(1)
+      }
+#undef MT_ROW
+    }
+  };
+  // Before step s (slice s in stage s % 4): slice s + 1 has landed for every
+  // wavefront (own DMA: at most the BPW loads of slice s + 2 still in flight;
+  // everyone's: the barrier), and every wavefront is past step s - 1, so no
+  // one still reads the stage of slice s - 1: it takes slice s + 3.
+  auto handover = [&](uint4* FREE, bool refill, int s, int newer) {
+    wait_vm(newer);
+    __builtin_amdgcn_s_barrier();
+    if (refill) issue(FREE, s + 3);
+  };
+
+  const int nkb = CONV ? (a.K + 127) / 128 * 4 : a.K / 32;  // a multiple of 4; conv: zero slices
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  wait_vm(2 * BPW);
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < MI; ++i) fa[i] = st0[a_idx(i)];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) fb0[j] = st0[b_idx(j)];
+
+  // Four steps per iteration (stages 0-3); inside the loop slices s + 3 all
+  // exist, so the body has no branch.  The last four steps are peeled.
+  for (int s = 0; s < nkb - 4; s += 4) {
+    handover(st3, true, s, BPW);
+    kstep(fb0, fb1, st1, true);
+    handover(st0, true, s + 1, BPW);
+    kstep(fb1, fb0, st2, true);
+    handover(st1, true, s + 2, BPW);
+    kstep(fb0, fb1, st3, true);
+    handover(st2, true, s + 3, BPW);
+    kstep(fb1, fb0, st0, true);
+  }
+  handover(st3, true, nkb - 4, BPW);
+  kstep(fb0, fb1, st1, true);
+  handover(st0, false, nkb - 3, BPW);
+  kstep(fb1, fb0, st2, true);
+  handover(st1, false, nkb - 2, 0);
+  kstep(fb0, fb1, st3, true);
+  kstep(fb1, fb0, st0, false);
+
+  if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
+    epilogue_staged4<T, EPI, BN, MI, NI>(a, acc, st0, st1, st2, st3, m0, n0, wm, wn);
+  } else {
+    epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
+  }
+}
+
+template <typename T, int BN, int EPI, int WM = 2, bool CONV = false>
+hipError_t run_w8q(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_w8q_kernel<T, BN, WM, EPI, CONV>), dim3(tiles), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -839,12 +1161,12 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
 template <typename T, int EPI, bool CONV>
 hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    // Convolutions: the eight-wavefront kernel with the tap gather, 256 x 160
-    // tiles of 64 x 80 wavefronts (480 output channels = 3 tiles; the
-    // 256 x 256 variant spills with the gather's per-row state).
+    // Convolutions: the four-stage eight-wavefront kernel with the tap
+    // gather, 256 x 160 tiles of 64 x 80 wavefronts (480 output channels =
+    // 3 tiles; the 256 x 256 variant spills with the gather's per-row state).
     if constexpr (CONV) {
       if (a.conv_C % 8 == 0 && (int64_t)a.N * a.ldb * 2 < (1ll << 31))
-        return run_w8<T, 160, EPI, 4, true>(a, s);
+        return run_w8q<T, 160, EPI, 4, true>(a, s);
     }
     if constexpr (!CONV) {
       // Wide outputs: 256-row tiles where K allows them (whole 128-wide K
@@ -852,10 +1174,11 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
       // how full the last round of tiles leaves the CUs (measured at
       // M = 6000: N = 5120 -> 256 x 256, 855 TFLOP/s; N = 3840 -> 256 x 192,
       // 793 TFLOP/s; 128 x 128: 670 / 651).  Narrow outputs (N = 1280: too
-      // few wide tiles to fill 256 CUs): the same kernel with 256 x 128
-      // tiles of eight 64 x 64 wavefronts (K = 5120: 847 TFLOP/s with a
-      // 16-bit epilogue, 730 with the fp32 residual add, against 752 / 622
-      // for 128 x 128; K = 1280: 740 / 595 against 617 / 541).
+      // few wide tiles to fill 256 CUs): the four-stage kernel with 256 x 128
+      // tiles of eight 64 x 64 wavefronts (two-stage variant, standalone:
+      // K = 5120: 847 TFLOP/s with a 16-bit epilogue, 730 with the fp32
+      // residual add, against 752 / 622 for 128 x 128; K = 1280: 740 / 595
+      // against 617 / 541; four stages gained another ~6 % on fc2).
       const bool w8 = a.K % 128 == 0 && (int64_t)a.M * a.lda * 2 < (1ll << 31) &&
                       (int64_t)a.N * a.ldb * 2 < (1ll << 31);
       if (w8 && a.N >= 2048) {
@@ -868,7 +1191,7 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
         }
         return run_w8<T, 256, EPI>(a, s);
       }
-      if (w8 && a.M >= 2048) return run_w8<T, 128, EPI, 4>(a, s);
+      if (w8 && a.M >= 2048) return run_w8q<T, 128, EPI, 4>(a, s);
       if (a.M >= 2048) return run_lds<T, 256, 128, 4, 2, 2, EPI, CONV>(a, s);
       return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
     }
