@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="before the steps, copy 256 MiB device-to-device once (a kernel of known "
+                         "traffic, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -127,6 +130,14 @@ def main():
     def step():
         W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream)
         W.mt_encode(enc, mel, lens_T, window, out=out, ws=ws_enc, stream=stream)
+
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -693,19 +693,22 @@ __global__ __launch_bounds__(512, 1) void gemm_w8_kernel(GemmArgs a) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (a.N + BN - 1) / BN;
-  // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin;
-  // for narrow outputs (few N tiles per row of A) and the convolutions,
-  // renumber so that each XCD runs a contiguous range of tiles (row-major:
-  // the N tiles of one row of A, then the next row) and the A rows -- and,
-  // for the convolution, the overlapping input rows -- stay in one L2
-  // (measured: conv2 2.31 -> 2.19 ms, fc2 3.46 -> 3.30, o 1.21 -> 1.16 per
-  // 16 x 30 s step; the wide GEMMs did not gain).
+  // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin.
+  // Renumber so that each XCD runs a contiguous range of tiles, ordered in
+  // groups of 4 rows of A: the ~32 tiles an XCD runs at once then cover
+  // about 4 A rows x 8 B columns of tiles, whose K slices its L2 shares,
+  // instead of ~13 x 5 (fc1, counters: 197 MB fetched from the fabric per
+  // launch before, for 28.5 MB of operands).
   int tile = blockIdx.x;
-  if (CONV || BN < 192) {
+  {
     const int nt = gridDim.x, q = nt / 8, r = nt % 8, x = tile % 8, idx = tile / 8;
     tile = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
   }
-  const int bm = tile / tiles_n, bn = tile % tiles_n;
+  constexpr int GM = 4;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int grp = tile / (GM * tiles_n), gw = tile - grp * (GM * tiles_n);
+  const int grows = min(GM, tiles_m - grp * GM);
+  const int bm = grp * GM + gw % grows, bn = gw / grows;
   const int m0 = bm * BM, n0 = bn * BN;
 
   // DMA plan: block (wave + NW i) holds LDS rows r0 + RPI i; rows < BM are
