@@ -30,6 +30,32 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
+# HBM traffic of one fc1 launch, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# then WRITE_SIZE) of `bench.py --steps 2 --warmup 1 --copy-probe`, each
+# scaled by what the same counter read for the probe's 256 MiB device copy
+# (see profiles/fc1_16x30s_traffic.md).  Keyed by a hash of the GEMM kernel
+# sources: after any change to them the figure is stale and reported as null.
+FC1_TRAFFIC = {
+    "30ca5247b9378827": {"fetch_KiB": 70450, "write_KiB": 73440,
+                         "fetch_scale": 262144 / 131094.4, "write_scale": 262144 / 262144.0},
+}
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "windowed_attention_audio_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def fc1_traffic_bytes():
+    t = FC1_TRAFFIC.get(gemm_source_hash())
+    if t is None:
+        return None
+    return round(1024 * (t["fetch_KiB"] * t["fetch_scale"] + t["write_KiB"] * t["write_scale"]))
+
 
 def algorithmic_flops(geom, lens_T, window):
     """Multiply-add count x 2 of one forward pass (excluding the log-mel)."""
@@ -202,7 +228,10 @@ def main():
                                % (M, geom["d_ffn"], geom["d_model"]),
                      "bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fc1_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_launch_ms": round(fc1_avg, 5), "launches": fc1_n},
+                     "traffic": fc1_traffic_bytes(), "avg_launch_ms": round(fc1_avg, 5),
+                     "launches": fc1_n,
+                     "algorithmic_bytes": 2 * (M * geom["d_model"] + geom["d_ffn"] * geom["d_model"]
+                                               + M * geom["d_ffn"])},
     }
     if breakdown:
         res["breakdown_ms_per_step"] = breakdown
