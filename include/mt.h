@@ -156,9 +156,12 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* we
 
 void mt_encoder_destroy(mt_encoder* enc);
 
-/* Largest window (encoder frames) the attention kernel keeps on chip.  A
- * larger `window` is accepted when no sequence is longer than this (the
- * attention is then the same as with window = the longest sequence). */
+/* Largest window (encoder frames) whose keys the attention kernel keeps on
+ * chip.  16-bit encoders accept any window: longer windows (up to window >=
+ * every sequence, i.e. full attention) stream their keys through LDS.  fp32
+ * encoders accept a larger `window` only when no sequence is longer than
+ * this (the attention is then the same as with window = the longest
+ * sequence); otherwise mt_encode returns MT_ERR_UNSUPPORTED. */
 int32_t mt_max_window(void);
 
 /* Workspace bytes for mt_encode on this batch and window. */

@@ -183,8 +183,13 @@ def test_rejections(model):
     import torch
     import windowed_attention_audio_amd as W
     mel = torch.zeros((3000, 128), device="cuda")
+    # fp32 encoders keep every window's keys on chip: 375 frames > 256 is refused
+    geom1 = dict(FULL, n_layers=1)
+    names = [n for n, _ in synth.weight_names(geom1)]
+    w32 = synth.make_weights(geom1, bf16=False)
+    m32 = GpuModel(geom1, "f32", {n: w32[n] for n in names})
     with pytest.raises(W.MtError) as e:
-        W.mt_encode(model.enc, mel, [3000], 300)  # 375 frames > on-chip window
+        W.mt_encode(m32.enc, mel, [3000], 300)
     assert e.value.status == W.MT_ERR_UNSUPPORTED
     with pytest.raises(W.MtError) as e:
         W.mt_encode(model.enc, mel, [3000], 0)
@@ -196,3 +201,32 @@ def test_rejections(model):
     with pytest.raises(W.MtError) as e:
         W.mt_logmel(torch.zeros(200, device="cuda"), [200])
     assert e.value.status == W.MT_ERR_INVALID_ARG
+
+
+def test_long_windows_30s(model, P64):
+    # windows longer than the 256 frames kept on chip stream their keys:
+    # W = 300 (windows of 300 and 75) and W >= N (full attention, 375 frames)
+    w = synth.workload(1)
+    mel = OL.log_mel(synth.make_clips(w)[0])
+    for W in (300, 1000):
+        say(f"30 s clip, W = {W}")
+        got = model.encode([mel], W)
+        ref = OE.encode_clip(mel, P64, FULL, W)
+        m = assert_bf16_rows(got, ref, what=f"W={W}")
+        say(f"  min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def test_long_windows_varlen_one_layer():
+    # one layer with random LayerNorm parameters, a packed batch whose clips are
+    # shorter than, equal to and longer than the window; W = 600 and 2000
+    geom = dict(FULL, n_layers=1)
+    wts = synth.make_weights(geom, bf16=True, ln_random=True)
+    model1 = GpuModel(geom, "f16", wts)
+    P = OE.as_f64(wts)
+    mels = _mels(11, [6000, 77, 4801, 2100])
+    N = [OE.encoder_frames(m.shape[0]) for m in mels]
+    for W in (600, 2000):
+        got = split_rows(model1.encode(mels, W), N)
+        for g, m in zip(got, mels):
+            ref = OE.encode_clip(m.astype(np.float64), P, geom, W)
+            assert_bf16_rows(g, ref, what=f"1 layer W={W} T={m.shape[0]}")

@@ -309,10 +309,10 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
     cuW[i + 1] = (int32_t)p.n_windows;
   }
   const int64_t weff = std::min<int64_t>(window, p.maxN);
-  if (weff > MAX_WINDOW)
+  if (weff > MAX_WINDOW && enc->dt == DT_F32)
     return fail(MT_ERR_UNSUPPORTED, "mt_encode: window %d over sequences of up to %lld frames "
-                "exceeds the on-chip maximum %d", window, (long long)p.maxN, MAX_WINDOW);
-  p.wpad = (int)((weff + 63) / 64 * 64);  // whole key chunks of 64 stay on chip
+                "exceeds the fp32 on-chip maximum %d", window, (long long)p.maxN, MAX_WINDOW);
+  p.wpad = (int)((weff + 63) / 64 * 64);  // whole key chunks of 64 (on chip up to MAX_WINDOW)
   p.out_stride = mb->layout == MT_PADDED ? half_up(half_up(half_up(mb->max_len))) : 0;
 
   const size_t es = enc->es;

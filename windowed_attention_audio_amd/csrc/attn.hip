@@ -213,6 +213,89 @@ typedef short tr4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) tr4_t* tr_ptr_t;
 typedef __attribute__((address_space(3))) void* lds_vptr_t;
 
+// One chunk of 64 keys for one 16-query group: S^T = K Q^T (lane = query
+// l16), scale, mask keys >= w, online-softmax update, O^T += V^T P^T.  K and
+// V rows r0 .. r0 + 63 of the LDS arrays hold keys kv0 .. kv0 + 63; 16-byte
+// chunk c of a row sits at slot c ^ (row & 7) (r0 is a multiple of 64).
+template <typename T>
+__device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, int r0, int kv0, int w,
+                                             const uint4 (&qf)[2], float& m_run, float& l_part,
+                                             f32x4 (&o)[4], int g, int l16) {
+  constexpr int CPR = 8;
+  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+  f32x4 st[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kvr = r0 + t * 16 + l16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 kf = Ks[kvr * CPR + ((4 * s + g) ^ (kvr & 7))];
+      mma16(st[t], kf, qf[s], T{});
+    }
+  }
+  // lane holds S^T[kv = kv0 + 16t + 4g + e][q]; scale, mask, row max
+  float cmax = -INFINITY;
+  if (kv0 + 64 <= w) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st[t][e] *= sl2;
+        cmax = fmaxf(cmax, st[t][e]);
+      }
+  } else {  // last, partial chunk: keys >= w drop out
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kv = kv0 + t * 16 + 4 * g + e;
+        const float v = kv < w ? st[t][e] * sl2 : -INFINITY;
+        st[t][e] = v;
+        cmax = fmaxf(cmax, v);
+      }
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  const float m_new = fmaxf(m_run, cmax);
+  const float alpha = exp2f(m_run - m_new);
+  m_run = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = exp2f(st[t][e] - m_new);
+      st[t][e] = p;
+      psum += p;
+    }
+  l_part = l_part * alpha + psum;
+#pragma unroll
+  for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
+
+  // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]
+  typedef Elem<T> E;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    uint4 pf;
+    pf.x = pack2(E::from_f(st[2 * u][0]), E::from_f(st[2 * u][1]));
+    pf.y = pack2(E::from_f(st[2 * u][2]), E::from_f(st[2 * u][3]));
+    pf.z = pack2(E::from_f(st[2 * u + 1][0]), E::from_f(st[2 * u + 1][1]));
+    pf.w = pack2(E::from_f(st[2 * u + 1][2]), E::from_f(st[2 * u + 1][3]));
+    const int r1 = r0 + 32 * u + 4 * g + (l16 >> 2), r2 = r1 + 16;
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd) {
+      const int c = 2 * nd + ((l16 & 3) >> 1), half = (l16 & 1) * 8;  // bytes within chunk
+      const tr4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (tr_ptr_t)((char*)(Vs + r1 * CPR + (c ^ (r1 & 7))) + half));
+      const tr4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (tr_ptr_t)((char*)(Vs + r2 * CPR + (c ^ (r2 & 7))) + half));
+      const uint2 w1 = __builtin_bit_cast(uint2, v1), w2 = __builtin_bit_cast(uint2, v2);
+      mma16(o[nd], make_uint4(w1.x, w1.y, w2.x, w2.y), pf, T{});
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void wattn16_kernel(AttnArgs a) {
   static_assert(sizeof(T) == 2, "16-bit operands");
@@ -252,7 +335,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void w
     }
   }
 
-  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
   const int nqg = (w + 15) >> 4;
   const int nkc = (w + 63) >> 6;
   const T* Qg = (const T*)base + head * HD;
@@ -281,79 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void w
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = 0; kc < nkc; ++kc) {
-      f32x4 st[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int kvr = kc * 64 + t * 16 + l16;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint4 kf = Ks[kvr * CPR + ((4 * s + g) ^ (kvr & 7))];
-          mma16(st[t], kf, qf[s], T{});
-        }
-      }
-      // lane holds S^T[kv = kc*64 + 16t + 4g + e][q]; scale, mask, row max
-      float cmax = -INFINITY;
-      if (kc * 64 + 64 <= w) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            st[t][e] *= sl2;
-            cmax = fmaxf(cmax, st[t][e]);
-          }
-      } else {  // last, partial chunk: keys >= w drop out
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int kv = kc * 64 + t * 16 + 4 * g + e;
-            const float v = kv < w ? st[t][e] * sl2 : -INFINITY;
-            st[t][e] = v;
-            cmax = fmaxf(cmax, v);
-          }
-      }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(st[t][e] - m_new);
-          st[t][e] = p;
-          psum += p;
-        }
-      l_part = l_part * alpha + psum;
-#pragma unroll
-      for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
-
-      // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]
-      typedef Elem<T> E;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint4 pf;
-        pf.x = pack2(E::from_f(st[2 * u][0]), E::from_f(st[2 * u][1]));
-        pf.y = pack2(E::from_f(st[2 * u][2]), E::from_f(st[2 * u][3]));
-        pf.z = pack2(E::from_f(st[2 * u + 1][0]), E::from_f(st[2 * u + 1][1]));
-        pf.w = pack2(E::from_f(st[2 * u + 1][2]), E::from_f(st[2 * u + 1][3]));
-        const int r1 = kc * 64 + 32 * u + 4 * g + (l16 >> 2), r2 = r1 + 16;
-#pragma unroll
-        for (int nd = 0; nd < 4; ++nd) {
-          const int c = 2 * nd + ((l16 & 3) >> 1), half = (l16 & 1) * 8;  // bytes within chunk
-          const tr4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (tr_ptr_t)((char*)(Vs + r1 * CPR + (c ^ (r1 & 7))) + half));
-          const tr4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (tr_ptr_t)((char*)(Vs + r2 * CPR + (c ^ (r2 & 7))) + half));
-          const uint2 w1 = __builtin_bit_cast(uint2, v1), w2 = __builtin_bit_cast(uint2, v2);
-          mma16(o[nd], make_uint4(w1.x, w1.y, w2.x, w2.y), pf, T{});
-        }
-      }
-    }
+    for (int kc = 0; kc < nkc; ++kc) attn_chunk16<T>(Ks, Vs, kc * 64, kc * 64, w, qf, m_run, l_part, o, g, l16);
     float l_tot = l_part + __shfl_xor(l_part, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     const float inv = 1.0f / l_tot;
@@ -383,6 +393,115 @@ hipError_t run_attn16(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Windows longer than the on-chip maximum (any W; W >= N is full attention
+// over each sequence): one workgroup per (window, block of 64 queries,
+// head), 16 queries per wavefront, and the window's keys stream through LDS
+// in tiles of 64 (K and V, 16 KB per stage, four stages: each tile's DMA is
+// issued three tiles ahead; tiles past the window read zeros, so every
+// wavefront issues the same loads).  Same per-chunk math as above.
+template <typename T>
+__global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) {
+  static_assert(sizeof(T) == 2, "16-bit operands");
+  constexpr int HD = 64, CPR = 8;
+  __shared__ uint4 k0[64 * CPR], k1[64 * CPR], k2[64 * CPR], k3[64 * CPR];
+  __shared__ uint4 v0[64 * CPR], v1[64 * CPR], v2[64 * CPR], v3[64 * CPR];
+
+  const int win = blockIdx.x / qblocks, qb = blockIdx.x - win * qblocks;
+  const int head = blockIdx.y;
+  const int sq = find_seq(a.cu_win, a.nseq, win);
+  const int kwin = win - a.cu_win[sq];
+  const int N = a.cu_rows[sq + 1] - a.cu_rows[sq];
+  const int s0 = a.cu_rows[sq] + kwin * a.window;
+  const int w = min(a.window, N - kwin * a.window);
+  if (qb * 64 >= w) return;  // the whole workgroup: before any barrier
+
+  const int ldb = 3 * a.D * (int)sizeof(T);  // bytes per qkv row
+  const char* base = (const char*)a.qkv + (int64_t)s0 * ldb;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, w * ldb, 0x00020000);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int nkt = (w + 63) >> 6;
+
+  // query group of this wavefront (may lie past w in the last block)
+  const int q = qb * 64 + wave * 16 + l16;
+  const bool active = qb * 64 + wave * 16 < w;
+  uint4 qf[2];
+  {
+    const T* Qg = (const T*)base + head * HD;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      qf[s] = make_uint4(0, 0, 0, 0);
+      if (q < w) qf[s] = *(const uint4*)(Qg + (int64_t)q * (3 * a.D) + (4 * s + g) * 8);
+    }
+  }
+
+  // tile kt into (K, V): 16 blocks of 8 rows, four per wavefront
+  auto issue = [&](int kt, uint4* K, uint4* V) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave + 4 * i;
+      const bool isv = b >= 8;
+      const int r = 8 * (isv ? b - 8 : b) + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      const int col = (isv ? 2 : 1) * a.D + head * HD + c * 8;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr_t)((isv ? V + (b - 8) * 64 : K + b * 64)), 16,
+                                               (kt * 64 + r) * ldb + col * (int)sizeof(T), 0, 0, 0);
+    }
+  };
+
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, k0, v0);
+  issue(1, k1, v1);
+  issue(2, k2, v2);
+  // Step kt: this wavefront's DMA of tile kt has landed (the 8 loads of the
+  // next two tiles may be in flight), everyone's has (barrier), and no one
+  // reads the stage of tile kt - 1 any more: it takes tile kt + 3.
+  auto step = [&](int kt, uint4* K, uint4* V, uint4* FK, uint4* FV) {
+    __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8) | ((8 >> 4) << 14));  // vmcnt(8)
+    __syncthreads();
+    issue(kt + 3, FK, FV);
+    if (active) attn_chunk16<T>(K, V, 0, kt * 64, w, qf, m_run, l_part, o, g, l16);
+  };
+  for (int kt = 0; kt < nkt; kt += 4) {
+    step(kt, k0, v0, k3, v3);
+    if (kt + 1 < nkt) step(kt + 1, k1, v1, k0, v0);
+    if (kt + 2 < nkt) step(kt + 2, k2, v2, k1, v1);
+    if (kt + 3 < nkt) step(kt + 3, k3, v3, k2, v2);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the loads of tiles past the window
+
+  if (active && q < w) {
+    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv = 1.0f / l_tot;
+    T* orow = (T*)a.out + (int64_t)(s0 + q) * a.D + head * HD;
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd) {
+      const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
+      typedef Elem<T> E;
+      uint2 pk;
+      pk.x = pack2(E::from_f(o[nd][0] * inv), E::from_f(o[nd][1] * inv));
+      pk.y = pack2(E::from_f(o[nd][2] * inv), E::from_f(o[nd][3] * inv));
+      *(uint2*)(orow + d0) = pk;
+    }
+  }
+}
+
+template <typename T>
+hipError_t run_attn16s(const AttnArgs& a, hipStream_t s) {
+  if (a.n_windows == 0) return hipSuccess;
+  const int qblocks = (a.wpad + 63) / 64;
+  hipLaunchKernelGGL(wattn16s_kernel<T>, dim3(a.n_windows * qblocks, a.n_heads), dim3(256), 0, s, a,
+                     qblocks);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t run_attn(const AttnArgs& a, hipStream_t s) {
   if (a.n_windows == 0) return hipSuccess;
@@ -397,8 +516,11 @@ hipError_t run_attn(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s) {
-  if (dtype == DT_BF16) return run_attn16<bf16_t>(a, s);
-  if (dtype == DT_F16) return run_attn16<f16_t>(a, s);
+  // keys of a window stay on chip up to 256 (LDS per workgroup 2 x 32 KB);
+  // longer windows stream them
+  if (dtype == DT_BF16) return a.wpad <= 256 ? run_attn16<bf16_t>(a, s) : run_attn16s<bf16_t>(a, s);
+  if (dtype == DT_F16) return a.wpad <= 256 ? run_attn16<f16_t>(a, s) : run_attn16s<f16_t>(a, s);
+  if (a.wpad > 256) return hipErrorInvalidValue;  // fp32: on-chip windows only
   return run_attn<float>(a, s);
 }
 

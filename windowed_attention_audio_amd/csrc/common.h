@@ -24,23 +24,23 @@ __device__ __forceinline__ uint32_t pack2(T a, T b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// erf after Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
-// erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
-// t = 1 / (1 + p |x|), odd in x; |error| <= 1.5e-7 (about 6e-7 with fp32
-// reciprocal and exp2).  About a dozen instructions, no branches.
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  const float poly =
-      fmaf(fmaf(fmaf(fmaf(1.061405429f, t, -1.453152027f), t, 1.421413741f), t, -0.284496736f), t,
-           0.254829592f) * t;
-  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
-  return copysignf(fmaf(-poly, e, 1.0f), x);
-}
-
-// GELU with the erf form, 0.5 x (1 + erf(x / sqrt 2)); |error| below 5e-7.
+// GELU with the erf form, x Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2.
+// erfc after Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z),
+// z >= 0, |error| <= 1.5e-7.  With z = |x| / sqrt 2 and the coefficients
+// halved, h = erfc(z) / 2 is the tail mass of the normal law beyond |x|:
+// Phi(x) = 1 - h for x >= 0 and h for x < 0, so GELU = x - x h or x h.
+// Written so for few instructions (it runs on every element of conv1-3 and
+// fc1): one reciprocal, one exp2, nine other ops; |error| below 3.5e-7
+// (float32, measured against the exact erf form on [-12, 12]).
 __device__ __forceinline__ float gelu_f(float x) {
-  return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752440f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164190f, fabsf(x), 1.0f));  // p / sqrt 2
+  const float P =
+      t * fmaf(fmaf(fmaf(fmaf(0.5307027145f, t, -0.726576013f), t, 0.7107068705f), t, -0.142248368f),
+               t, 0.127414796f);
+  const float h = P * __builtin_amdgcn_exp2f(x * x * -0.72134752044f);  // exp(-x^2 / 2)
+  const float xh = x * h;
+  return x < 0.f ? xh : x - xh;
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
