@@ -106,6 +106,56 @@ def cpu_baseline(clip, weights, geom, window, min_seconds=10.0, max_clips=4):
                       f"full encoder in NumPy float64, {el:.1f} s wall"}
 
 
+def stream_measure(W, enc, synth, torch, np, chunks=(8, 32), reps=4):
+    """mt_encode_stream on the 10-minute stream (window 104) with chunk_windows
+    windows per chunk, against mt_logmel + mt_encode of the whole stream: time
+    per encode and workspace bytes."""
+    wl = synth.workload(3)
+    wav = synth.make_clips(wl)[0]
+    n = len(wav)
+    dwav = torch.from_numpy(wav).cuda()
+    T = W.mt_mel_frames(n)
+    N = W.mt_encoder_frames(T)
+    out = torch.empty((N, enc.d_out), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {"workload": wl.name, "audio_s": n / 16000.0}
+    for cw in chunks:
+        nb = W.mt_encode_stream_workspace_size(enc, n, wl.window, cw)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: W.mt_encode_stream(enc, dwav, wl.window, cw, out=out, ws=ws,
+                                              stream=stream))
+        res[f"chunk{cw}"] = {"ms": round(ms, 3), "audio_s_per_s": round(n / 16000.0 / (ms * 1e-3), 1),
+                             "workspace_bytes": nb}
+        del ws
+    mel = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+    ws_m = torch.empty(W.mt_logmel_workspace_size([n]), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty(W.mt_encode_workspace_size(enc, [T], wl.window), dtype=torch.uint8,
+                       device="cuda")
+
+    def whole():
+        W.mt_logmel(dwav, [n], mel=mel, ws=ws_m, stream=stream)
+        W.mt_encode(enc, mel, [T], wl.window, out=out, ws=ws_e, stream=stream)
+
+    ms = timed(whole)
+    res["whole"] = {"ms": round(ms, 3), "audio_s_per_s": round(n / 16000.0 / (ms * 1e-3), 1),
+                    "workspace_bytes": ws_m.numel() + ws_e.numel() + mel.numel() * 4}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +164,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the bounded-memory stream measurement (10-minute stream)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before the steps, copy 256 MiB device-to-device once (a kernel of known "
                          "traffic, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -235,6 +287,8 @@ def main():
     }
     if breakdown:
         res["breakdown_ms_per_step"] = breakdown
+    if not args.no_stream:
+        res["stream_10min"] = stream_measure(W, enc, synth, torch, np)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(clips[0], weights, geom, window)
     print(json.dumps(res), flush=True)

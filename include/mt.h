@@ -182,6 +182,24 @@ mt_status mt_encode_workspace_size(const mt_encoder* enc, const mt_batch* mel_b,
 mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel_b,
                     int32_t window, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Bounded-memory encode of one long stream (model card "MOSS-Transcribe-
+ * preview-2B-GGUF", Architecture table; the windows make encoder frames
+ * independent beyond the convolutions' receptive field of 15 mel frames).
+ *   wav            device fp32 [n_samples], one stream, n_samples >= 201.
+ *   window         W >= 1 as in mt_encode.
+ *   chunk_windows  windows encoded per chunk (>= 1): the workspace holds one
+ *                  chunk's activations and does not grow with the stream.
+ *   out            device fp32 [N, d], N = mt_encoder_frames(mt_mel_frames(n)).
+ * Two passes over the waveform: the stream's log-mel maximum first (the
+ * normalisation needs it), then each chunk's mel frames with their receptive
+ * field (8 frames before, none after) and the encoder.  The result equals
+ * mt_logmel + mt_encode of the whole stream with the same window. */
+mt_status mt_encode_stream_workspace_size(const mt_encoder* enc, int64_t n_samples, int32_t window,
+                                          int32_t chunk_windows, size_t* bytes);
+mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_samples,
+                           int32_t window, int32_t chunk_windows, float* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 
 /* Stage timer.  Arms timing of one stage of mt_logmel / mt_encode, named

@@ -230,3 +230,54 @@ def test_long_windows_varlen_one_layer():
         for g, m in zip(got, mels):
             ref = OE.encode_clip(m.astype(np.float64), P, geom, W)
             assert_bf16_rows(g, ref, what=f"1 layer W={W} T={m.shape[0]}")
+
+
+def _full_stream(model, wav, W):
+    mel = gpu_logmel([wav])
+    return model.encode([mel], W)
+
+
+def test_stream_chunked_equals_whole(model):
+    # mt_encode_stream (bounded workspace, chunk by chunk) against mt_logmel +
+    # mt_encode of the whole 10-minute stream: bitwise equal
+    import torch
+    import windowed_attention_audio_amd as W
+    w = synth.workload(3)
+    wav = synth.make_clips(w)[0]
+    full = _full_stream(model, wav, w.window)
+    dwav = torch.from_numpy(wav).cuda()
+    for cw in (1, 5, 1000):
+        say(f"10 min stream, {cw} window(s) per chunk")
+        got = W.mt_encode_stream(model.enc, dwav, w.window, cw)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), full), f"chunk_windows={cw}"
+    # the workspace does not grow with the stream
+    n = len(wav)
+    assert (W.mt_encode_stream_workspace_size(model.enc, n, w.window, 5)
+            == W.mt_encode_stream_workspace_size(model.enc, 6 * n, w.window, 5))
+
+
+def test_stream_short_and_ragged(model):
+    import torch
+    import windowed_attention_audio_amd as W
+    rng = np.random.default_rng(12)
+    for n, Wn, cw in ((201, 104, 1), (16000, 104, 1), (16000 * 7 + 77, 3, 2), (16000 * 20 + 159, 52, 3)):
+        wav = (rng.standard_normal(n) * 0.2).astype(np.float32)
+        full = _full_stream(model, wav, Wn)
+        got = W.mt_encode_stream(model.enc, torch.from_numpy(wav).cuda(), Wn, cw).cpu().numpy()
+        assert np.array_equal(got, full), f"n={n} W={Wn} chunk_windows={cw}"
+
+
+def test_stream_rejections(model):
+    import torch
+    import windowed_attention_audio_amd as W
+    wav = torch.zeros(16000, device="cuda")
+    for args, status in (((200, 104, 1), W.MT_ERR_INVALID_ARG), ((16000, 0, 1), W.MT_ERR_INVALID_ARG),
+                         ((16000, 104, 0), W.MT_ERR_INVALID_ARG)):
+        with pytest.raises(W.MtError) as e:
+            W.mt_encode_stream_workspace_size(model.enc, *args)
+        assert e.value.status == status
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(W.MtError) as e:
+        W.mt_encode_stream(model.enc, wav, 104, 1, ws=ws)
+    assert e.value.status == W.MT_ERR_WORKSPACE

@@ -163,3 +163,10 @@ def test_library_tables_match_oracle_filterbank():
     for m, (first, w) in enumerate(rows):
         F[m, first:first + len(w)] = w
     assert np.max(np.abs(F - OL.mel_filterbank())) < 1e-12
+
+
+def test_encode_stream_rejects_null_encoder(L):
+    import ctypes as C
+    n = C.c_size_t()
+    assert L.mt_encode_stream_workspace_size(None, 16000, 104, 1, C.byref(n)) == W.MT_ERR_INVALID_ARG
+    assert L.mt_encode_stream(None, None, 16000, 104, 1, None, None, 0, None) == W.MT_ERR_INVALID_ARG

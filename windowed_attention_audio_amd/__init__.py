@@ -30,6 +30,7 @@ EXPORTS = (
     "mt_mel_frames", "mt_encoder_frames", "mt_logmel_workspace_size", "mt_logmel",
     "mt_encoder_n_weights", "mt_encoder_packed_bytes", "mt_encoder_create",
     "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
+    "mt_encode_stream_workspace_size", "mt_encode_stream",
     "mt_status_string", "mt_last_error", "mt_trace_arm", "mt_trace_collect",
 )
 
@@ -83,6 +84,10 @@ def lib():
         L.mt_encode_workspace_size.argtypes = [vp, ctypes.POINTER(Batch), ctypes.c_int32,
                                                ctypes.POINTER(c_sz)]
         L.mt_encode.argtypes = [vp, vp, ctypes.POINTER(Batch), ctypes.c_int32, vp, vp, c_sz, vp]
+        L.mt_encode_stream_workspace_size.argtypes = [vp, ctypes.c_int64, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.POINTER(c_sz)]
+        L.mt_encode_stream.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp,
+                                       vp, c_sz, vp]
         L.mt_trace_arm.argtypes = [ctypes.c_char_p, ctypes.c_int32]
         L.mt_trace_arm.restype = ctypes.c_int
         L.mt_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -92,7 +97,8 @@ def lib():
         L.mt_status_string.argtypes = [ctypes.c_int]
         L.mt_last_error.restype = ctypes.c_char_p
         for name in ("mt_logmel_workspace_size", "mt_logmel", "mt_encoder_packed_bytes",
-                     "mt_encoder_create", "mt_encode_workspace_size", "mt_encode"):
+                     "mt_encoder_create", "mt_encode_workspace_size", "mt_encode",
+                     "mt_encode_stream_workspace_size", "mt_encode_stream"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -243,6 +249,33 @@ def mt_encode(enc: Encoder, mel, lens, window, layout=MT_PACKED, out=None, ws=No
     _check(lib().mt_encode(enc.handle, ctypes.c_void_p(mel.data_ptr()), ctypes.byref(b),
                            int(window), ctypes.c_void_p(out.data_ptr()),
                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
+    return out
+
+
+def mt_encode_stream_workspace_size(enc: Encoder, n_samples, window, chunk_windows) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_encode_stream_workspace_size(enc.handle if enc is not None else None,
+                                                 int(n_samples), int(window), int(chunk_windows),
+                                                 ctypes.byref(n)))
+    return n.value
+
+
+def mt_encode_stream(enc: Encoder, wav, window, chunk_windows, out=None, ws=None, stream=None):
+    """wav: fp32 CUDA tensor [n] (one stream).  Encodes it chunk_windows
+    windows at a time with a workspace that does not grow with the stream;
+    returns fp32 [N, d], equal to mt_logmel + mt_encode over the whole stream."""
+    import torch
+    assert wav.is_cuda and wav.dtype == torch.float32 and wav.is_contiguous() and wav.dim() == 1
+    n = wav.numel()
+    N = mt_encoder_frames(mt_mel_frames(n))
+    if out is None:
+        out = torch.empty((N, enc.d_out), dtype=torch.float32, device=wav.device)
+    if ws is None:
+        nbytes = mt_encode_stream_workspace_size(enc, n, window, chunk_windows)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=wav.device)
+    _check(lib().mt_encode_stream(enc.handle, ctypes.c_void_p(wav.data_ptr()), int(n), int(window),
+                                  int(chunk_windows), ctypes.c_void_p(out.data_ptr()),
+                                  ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
     return out
 
 

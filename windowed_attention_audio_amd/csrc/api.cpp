@@ -256,7 +256,16 @@ struct EncPlan {
   int64_t sumT = 0, sumT1 = 0, sumT2 = 0, M = 0, maxN = 0, n_windows = 0, out_stride = 0;
   int wpad = 0;
   // workspace offsets
-  size_t o_words, o_rowoff, o_act1, o_act2, o_act3, o_x, o_h, o_qkv, o_att, o_ffn, o_y, o_ahid, bytes;
+  size_t o_words, o_rowoff, o_twords, o_act1, o_act2, o_act3, o_x, o_h, o_qkv, o_att, o_ffn, o_y, o_ahid,
+      bytes;
+};
+
+// One chunk of a stream (mt_encode_stream): the batch is one sequence, a
+// window of mel frames of the stream; its first `drop` encoder frames are the
+// halo (their receptive field leaves the window) and the next `keep` are
+// encoded; `pos` is the stream position of the sequence's encoder frame 0.
+struct StreamChunk {
+  int pos = 0, drop = 0, keep = 0;
 };
 
 }  // namespace
@@ -321,6 +330,7 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   Carver k;
   p.o_words = k.take(4 * p.words.size());
   p.o_rowoff = k.take(8 * (size_t)B);
+  p.o_twords = k.take(16);
   p.o_act1 = k.take((size_t)p.sumT1 * 64 * C * es);
   p.o_act2 = k.take((size_t)p.sumT2 * 32 * C * es);
   p.o_act3 = k.take(M * 16 * C * es);
@@ -359,6 +369,222 @@ GemmArgs gemm(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int
 }  // namespace
 
 // ====================================================================== C ABI
+
+namespace {
+
+// Launches the whole encoder for a planned batch (validated by the caller).
+mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, int32_t window,
+                     float* out, char* w, hipStream_t s, const StreamChunk* ch) {
+  const mt_encoder_config& c = enc->cfg;
+  const int dt = enc->dt;
+  const int B = p.B;
+  int M = (int)p.M;
+  const int C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
+
+  // tables: words (cu_T | cu_T1 | cu_T2 | cu_N | cu_win), then mel row offsets
+  HIP_TRY(upload_words((uint32_t*)(w + p.o_words), (const uint32_t*)p.words.data(),
+                       (int64_t)p.words.size(), s), "upload tables");
+  HIP_TRY(upload_words((uint32_t*)(w + p.o_rowoff), (const uint32_t*)p.mel_row_off.data(),
+                       2 * (int64_t)B, s), "upload tables");
+  const int32_t* cuT = (const int32_t*)(w + p.o_words);
+  const int32_t* cuT1 = cuT + (B + 1);
+  const int32_t* cuT2 = cuT1 + (B + 1);
+  const int32_t* cuN = cuT2 + (B + 1);
+  const int32_t* cuW = cuN + (B + 1);
+  void* act1 = w + p.o_act1;
+  void* act2 = w + p.o_act2;
+  void* act3 = w + p.o_act3;
+  float* x = (float*)(w + p.o_x);
+  void* h = w + p.o_h;
+  void* qkv = w + p.o_qkv;
+  void* att = w + p.o_att;
+  void* ffn = w + p.o_ffn;
+  void* ybuf = w + p.o_y;
+  void* ahid = w + p.o_ahid;
+
+  auto gemm = [&](const void* A_, int64_t lda, const void* B_, int64_t ldb, int M_, int N_, int K_,
+                  const float* bias, void* C_, int64_t ldc) {
+    GemmArgs g_ = ::gemm(A_, lda, B_, ldb, M_, N_, K_, bias, C_, ldc);
+    g_.zeros = enc->zeros;
+    return g_;
+  };
+
+  // ---- front-end
+  Conv1Args c1;
+  c1.mel = mel;
+  c1.mel_row_off = (const int64_t*)(w + p.o_rowoff);
+  c1.cu_T = cuT;
+  c1.cu_T1 = cuT1;
+  c1.nseq = B;
+  c1.total_T1 = p.sumT1;
+  c1.w = enc->conv1_w;
+  c1.b = enc->conv1_b;
+  c1.out = act1;
+  c1.C = C;
+  c1.dtype = dt;
+  STAGE(launch_conv1(c1, s), "conv1");
+
+  GemmArgs g = gemm(act1, 0, enc->conv2_w, 9 * C, (int)(p.sumT2 * 32), C, 9 * C, enc->conv2_b, act2, C);
+  g.conv_C = C;
+  g.conv_Fin = 64;
+  g.conv_Fout = 32;
+  g.cu_in = cuT1;
+  g.cu_out = cuT2;
+  g.nseq = B;
+  STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv2");
+  g = gemm(act2, 0, enc->conv3_w, 9 * C, (int)(p.M * 16), C, 9 * C, enc->conv3_b, act3, C);
+  g.conv_C = C;
+  g.conv_Fin = 32;
+  g.conv_Fout = 16;
+  g.cu_in = cuT2;
+  g.cu_out = cuN;
+  g.nseq = B;
+  STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv3");
+  g = gemm(act3, 16 * C, enc->conv_out_w, 16 * C, M, D, 16 * C, nullptr, x, D);
+  g.cu_rows = cuN;
+  g.nseq = B;
+  g.pos_offset = ch ? ch->pos : 0;
+  STAGE(launch_gemm(g, EPI_PE, dt, false, s), "conv_out");
+
+  // ---- tower (a stream chunk: its kept rows only, as one sequence)
+  int64_t n_windows = p.n_windows;
+  if (ch) {
+    n_windows = (ch->keep + window - 1) / window;
+    const int32_t tw[4] = {0, ch->keep, 0, (int32_t)n_windows};
+    HIP_TRY(upload_words((uint32_t*)(w + p.o_twords), (const uint32_t*)tw, 4, s), "upload tables");
+    cuN = (const int32_t*)(w + p.o_twords);
+    cuW = cuN + 2;
+    x += (size_t)ch->drop * D;
+    M = ch->keep;
+  }
+  AttnArgs aa;
+  aa.qkv = qkv;
+  aa.out = att;
+  aa.cu_rows = cuN;
+  aa.cu_win = cuW;
+  aa.nseq = ch ? 1 : B;
+  aa.n_windows = (int)n_windows;
+  aa.window = window;
+  aa.n_heads = c.n_heads;
+  aa.D = D;
+  aa.wpad = p.wpad;
+  const bool half = dt != DT_F32;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& L = enc->layers[l];
+    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, dt, false, s), "ln1");
+    STAGE(launch_gemm(gemm(h, D, L.wqkv, D, M, 3 * D, D, L.bqkv, qkv, 3 * D), EPI_ACT, dt, false, s), "qkv");
+    STAGE(launch_attention(aa, dt, s), "attn");
+    STAGE(launch_gemm(gemm(att, D, L.wo, D, M, D, D, L.bo, x, D), EPI_RESID, dt, false, s), "o");
+    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, dt, false, s), "ln2");
+    STAGE(launch_gemm(gemm(h, D, L.w1, D, M, F, D, L.b1, ffn, F), EPI_GELU, dt, false, s), "fc1");
+    STAGE(launch_gemm(gemm(ffn, F, L.w2, F, M, D, F, L.b2, x, D), EPI_RESID, dt, false, s), "fc2");
+  }
+
+  // ---- head / output
+  const int64_t stride = p.out_stride;
+  int out_d = D;
+  if (!c.with_head) {
+    STAGE(launch_copy_rows(x, out, M, D, cuN, ch ? 1 : B, stride, s), "copy_rows");
+  } else {
+    out_d = O;
+    // 16-bit operands: the head's activations enter as hi/lo pairs (K doubled)
+    const int KD = half ? 2 * D : D;
+    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt, half, s), "ln_post");
+    STAGE(launch_gemm(gemm(h, KD, enc->wp1, KD, M, D, KD, enc->bp1, ffn, KD),
+                        half ? EPI_GELU_SPLIT : EPI_GELU, dt, false, s), "proj1");
+    GemmArgs g2 = gemm(ffn, KD, enc->wp2, KD, M, O, KD, enc->bp2, A ? ybuf : (void*)out, O);
+    g2.cu_rows = cuN;
+    g2.nseq = ch ? 1 : B;
+    g2.out_seq_stride = A ? 0 : stride;
+    STAGE(launch_gemm(g2, A ? EPI_ACT : EPI_OUT, dt, false, s), "proj2");
+    if (A) {
+      STAGE(launch_gemm(gemm(ybuf, O, enc->wgu, O, M, 2 * A, O, nullptr, ahid, A), EPI_SWIGLU, dt,
+                          false, s), "adapter_gu");
+      GemmArgs g3 = gemm(ahid, A, enc->wd, A, M, O, A, nullptr, out, O);
+      g3.cu_rows = cuN;
+      g3.nseq = ch ? 1 : B;
+      g3.out_seq_stride = stride;
+      STAGE(launch_gemm(g3, EPI_OUT, dt, false, s), "adapter_down");
+    }
+  }
+  if (stride > 0) STAGE(launch_zero_pad_rows(out, cuN, ch ? 1 : B, stride, out_d, s), "zero_pad");
+  return MT_OK;
+}
+
+
+// ------------------------------------------------------------- stream plan
+// mt_encode_stream: encoder frames in chunks of chunk_windows windows.  Chunk
+// [e0, e1) needs mel frames [8 e0 - 7, 8 e1) (the receptive field of encoder
+// frame t is mel frames 8t - 7 .. 8t + 7); it is encoded from mel frames
+// [max(0, 8 e0 - 8), min(T, 8 e1)): starting on a multiple of 8 keeps the
+// stride-2 convolutions aligned with the stream's, and the one encoder frame
+// before e0 that this range yields (its receptive field leaves the range) is
+// dropped before the tower.  Every kept frame then goes through the same
+// arithmetic as in mt_logmel + mt_encode over the whole stream.
+struct StreamPlan {
+  int64_t n = 0, T = 0, N = 0, Fc = 0, Tc = 0;  // samples, mel frames, encoder frames,
+                                                // frames per chunk, largest chunk's mel frames
+  size_t off_tab = 0, off_gmax = 0, off_mel = 0, off_enc = 0, bytes = 0;
+  EncPlan enc;  // plan of the largest chunk (sizes the workspace)
+};
+
+mt_status plan_stream(const mt_encoder* enc, int64_t n_samples, int32_t window, int32_t chunk_windows,
+                      StreamPlan& sp) {
+  if (!enc) return fail(MT_ERR_INVALID_ARG, "encoder is NULL");
+  if (n_samples < 201 || n_samples > INT32_MAX)
+    return fail(MT_ERR_INVALID_ARG, "mt_encode_stream: n_samples %lld out of range [201, %d]",
+                (long long)n_samples, INT32_MAX);
+  if (window < 1) return fail(MT_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+  if (chunk_windows < 1)
+    return fail(MT_ERR_INVALID_ARG, "chunk_windows must be >= 1 (got %d)", chunk_windows);
+  sp.n = n_samples;
+  sp.T = n_samples / 160;
+  sp.N = half_up(half_up(half_up(sp.T)));
+  sp.Fc = std::min<int64_t>((int64_t)chunk_windows * window, sp.N);
+  sp.Tc = std::min<int64_t>(sp.T, 8 * sp.Fc + 8);
+  int64_t lens[1] = {sp.Tc};
+  mt_batch b;
+  b.layout = MT_PACKED;
+  b.n_seqs = 1;
+  b.len = lens;
+  b.max_len = 0;
+  mt_status st = plan_encode(enc, &b, window, sp.enc);
+  if (st != MT_OK) return st;
+  Carver k;
+  sp.off_tab = k.take(64);
+  sp.off_gmax = k.take(4);
+  sp.off_mel = k.take((size_t)sp.Tc * 128 * 4);
+  sp.off_enc = k.take(sp.enc.bytes);
+  sp.bytes = k.off;
+  return MT_OK;
+}
+
+// Mel frames [m0, m0 + nf) of the stream into mel (rows 0 .. nf - 1): tables
+// for one sequence of the stream's full length, frame offset m0.
+mt_status stream_mel(const float* wav, int64_t n, int64_t m0, int64_t nf, float* mel, char* w,
+                     const StreamPlan& sp, bool normalise, hipStream_t s) {
+  // sample_off (8) | row_off (8) | seq_len (4) | cu_frames (8)
+  uint32_t words[7] = {0, 0, 0, 0, (uint32_t)n, 0, (uint32_t)nf};
+  HIP_TRY(upload_words((uint32_t*)(w + sp.off_tab), words, 7, s), "upload tables");
+  MelArgs a;
+  a.wav = wav;
+  a.mel = mel;
+  a.seq_sample_off = (const int64_t*)(w + sp.off_tab);
+  a.seq_row_off = (const int64_t*)(w + sp.off_tab + 8);
+  a.seq_len = (const int32_t*)(w + sp.off_tab + 16);
+  a.cu_frames = (const int32_t*)(w + sp.off_tab + 20);
+  a.gmax = (int*)(w + sp.off_gmax);
+  a.nseq = 1;
+  a.total_frames = nf;
+  a.out_rows = nf;
+  a.padded = 0;
+  a.frame_off = m0;
+  STAGE(launch_mel(a, s), "mel");
+  if (normalise) STAGE(launch_mel_norm(a, nf, s), "mel_norm");
+  return MT_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -427,6 +653,7 @@ mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* w
   a.total_frames = p.total_frames;
   a.out_rows = p.out_rows;
   a.padded = wav_b->layout == MT_PADDED;
+  a.frame_off = 0;
   STAGE(launch_mel(a, s), "mel");
   STAGE(launch_mel_norm(a, p.tmax, s), "mel_norm");
   return MT_OK;
@@ -616,130 +843,71 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
   if (ws_bytes < p.bytes)
     return fail(MT_ERR_WORKSPACE, "mt_encode: workspace %zu bytes < required %zu", ws_bytes, p.bytes);
 
-  const mt_encoder_config& c = enc->cfg;
+  return run_encode(enc, p, mel, window, out, (char*)ws, (hipStream_t)stream, nullptr);
+}
+
+
+mt_status mt_encode_stream_workspace_size(const mt_encoder* enc, int64_t n_samples, int32_t window,
+                                          int32_t chunk_windows, size_t* bytes) {
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  StreamPlan sp;
+  mt_status st = plan_stream(enc, n_samples, window, chunk_windows, sp);
+  if (st != MT_OK) return st;
+  *bytes = sp.bytes;
+  return MT_OK;
+}
+
+mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_samples, int32_t window,
+                           int32_t chunk_windows, float* out, void* ws, size_t ws_bytes, void* stream) {
+  StreamPlan sp;
+  mt_status st = plan_stream(enc, n_samples, window, chunk_windows, sp);
+  if (st != MT_OK) return st;
+  if (!wav || !out || !ws) return fail(MT_ERR_INVALID_ARG, "mt_encode_stream: NULL device pointer");
+  if ((uintptr_t)ws % ALIGN || (uintptr_t)out % 16)
+    return fail(MT_ERR_INVALID_ARG, "mt_encode_stream: ws must be 256-byte and out 16-byte aligned");
+  if (ws_bytes < sp.bytes)
+    return fail(MT_ERR_WORKSPACE, "mt_encode_stream: workspace %zu bytes < required %zu", ws_bytes,
+                sp.bytes);
   hipStream_t s = (hipStream_t)stream;
-  const int dt = enc->dt;
   char* w = (char*)ws;
-  const int B = p.B;
-  const int M = (int)p.M;
-  const int C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
+  float* mel = (float*)(w + sp.off_mel);
+  const int d_out = enc->cfg.with_head ? enc->cfg.d_out : enc->cfg.d_model;
 
-  // tables: words (cu_T | cu_T1 | cu_T2 | cu_N | cu_win), then mel row offsets
-  HIP_TRY(upload_words((uint32_t*)(w + p.o_words), (const uint32_t*)p.words.data(),
-                       (int64_t)p.words.size(), s), "upload tables");
-  HIP_TRY(upload_words((uint32_t*)(w + p.o_rowoff), (const uint32_t*)p.mel_row_off.data(),
-                       2 * (int64_t)B, s), "upload tables");
-  const int32_t* cuT = (const int32_t*)(w + p.o_words);
-  const int32_t* cuT1 = cuT + (B + 1);
-  const int32_t* cuT2 = cuT1 + (B + 1);
-  const int32_t* cuN = cuT2 + (B + 1);
-  const int32_t* cuW = cuN + (B + 1);
-  void* act1 = w + p.o_act1;
-  void* act2 = w + p.o_act2;
-  void* act3 = w + p.o_act3;
-  float* x = (float*)(w + p.o_x);
-  void* h = w + p.o_h;
-  void* qkv = w + p.o_qkv;
-  void* att = w + p.o_att;
-  void* ffn = w + p.o_ffn;
-  void* ybuf = w + p.o_y;
-  void* ahid = w + p.o_ahid;
-
-  auto gemm = [&](const void* A_, int64_t lda, const void* B_, int64_t ldb, int M_, int N_, int K_,
-                  const float* bias, void* C_, int64_t ldc) {
-    GemmArgs g_ = ::gemm(A_, lda, B_, ldb, M_, N_, K_, bias, C_, ldc);
-    g_.zeros = enc->zeros;
-    return g_;
-  };
-
-  // ---- front-end
-  Conv1Args c1;
-  c1.mel = mel;
-  c1.mel_row_off = (const int64_t*)(w + p.o_rowoff);
-  c1.cu_T = cuT;
-  c1.cu_T1 = cuT1;
-  c1.nseq = B;
-  c1.total_T1 = p.sumT1;
-  c1.w = enc->conv1_w;
-  c1.b = enc->conv1_b;
-  c1.out = act1;
-  c1.C = C;
-  c1.dtype = dt;
-  STAGE(launch_conv1(c1, s), "conv1");
-
-  GemmArgs g = gemm(act1, 0, enc->conv2_w, 9 * C, (int)(p.sumT2 * 32), C, 9 * C, enc->conv2_b, act2, C);
-  g.conv_C = C;
-  g.conv_Fin = 64;
-  g.conv_Fout = 32;
-  g.cu_in = cuT1;
-  g.cu_out = cuT2;
-  g.nseq = B;
-  STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv2");
-  g = gemm(act2, 0, enc->conv3_w, 9 * C, (int)(p.M * 16), C, 9 * C, enc->conv3_b, act3, C);
-  g.conv_C = C;
-  g.conv_Fin = 32;
-  g.conv_Fout = 16;
-  g.cu_in = cuT2;
-  g.cu_out = cuN;
-  g.nseq = B;
-  STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv3");
-  g = gemm(act3, 16 * C, enc->conv_out_w, 16 * C, M, D, 16 * C, nullptr, x, D);
-  g.cu_rows = cuN;
-  g.nseq = B;
-  STAGE(launch_gemm(g, EPI_PE, dt, false, s), "conv_out");
-
-  // ---- tower
-  AttnArgs aa;
-  aa.qkv = qkv;
-  aa.out = att;
-  aa.cu_rows = cuN;
-  aa.cu_win = cuW;
-  aa.nseq = B;
-  aa.n_windows = (int)p.n_windows;
-  aa.window = window;
-  aa.n_heads = c.n_heads;
-  aa.D = D;
-  aa.wpad = p.wpad;
-  const bool half = dt != DT_F32;
-  for (int l = 0; l < c.n_layers; ++l) {
-    const Layer& L = enc->layers[l];
-    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, dt, false, s), "ln1");
-    STAGE(launch_gemm(gemm(h, D, L.wqkv, D, M, 3 * D, D, L.bqkv, qkv, 3 * D), EPI_ACT, dt, false, s), "qkv");
-    STAGE(launch_attention(aa, dt, s), "attn");
-    STAGE(launch_gemm(gemm(att, D, L.wo, D, M, D, D, L.bo, x, D), EPI_RESID, dt, false, s), "o");
-    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, dt, false, s), "ln2");
-    STAGE(launch_gemm(gemm(h, D, L.w1, D, M, F, D, L.b1, ffn, F), EPI_GELU, dt, false, s), "fc1");
-    STAGE(launch_gemm(gemm(ffn, F, L.w2, F, M, D, F, L.b2, x, D), EPI_RESID, dt, false, s), "fc2");
+  // pass 1: the stream's log-mel maximum (values discarded)
+  const float ninf = -INFINITY;
+  int key;
+  memcpy(&key, &ninf, 4);
+  key = key >= 0 ? key : key ^ 0x7fffffff;
+  HIP_TRY(launch_fill_i32((int*)(w + sp.off_gmax), key, 1, s), "fill");
+  for (int64_t m0 = 0; m0 < sp.T; m0 += sp.Tc) {
+    st = stream_mel(wav, sp.n, m0, std::min(sp.Tc, sp.T - m0), mel, w, sp, false, s);
+    if (st != MT_OK) return st;
   }
-
-  // ---- head / output
-  const int64_t stride = p.out_stride;
-  int out_d = D;
-  if (!c.with_head) {
-    STAGE(launch_copy_rows(x, out, M, D, cuN, B, stride, s), "copy_rows");
-  } else {
-    out_d = O;
-    // 16-bit operands: the head's activations enter as hi/lo pairs (K doubled)
-    const int KD = half ? 2 * D : D;
-    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt, half, s), "ln_post");
-    STAGE(launch_gemm(gemm(h, KD, enc->wp1, KD, M, D, KD, enc->bp1, ffn, KD),
-                        half ? EPI_GELU_SPLIT : EPI_GELU, dt, false, s), "proj1");
-    GemmArgs g2 = gemm(ffn, KD, enc->wp2, KD, M, O, KD, enc->bp2, A ? ybuf : (void*)out, O);
-    g2.cu_rows = cuN;
-    g2.nseq = B;
-    g2.out_seq_stride = A ? 0 : stride;
-    STAGE(launch_gemm(g2, A ? EPI_ACT : EPI_OUT, dt, false, s), "proj2");
-    if (A) {
-      STAGE(launch_gemm(gemm(ybuf, O, enc->wgu, O, M, 2 * A, O, nullptr, ahid, A), EPI_SWIGLU, dt,
-                          false, s), "adapter_gu");
-      GemmArgs g3 = gemm(ahid, A, enc->wd, A, M, O, A, nullptr, out, O);
-      g3.cu_rows = cuN;
-      g3.nseq = B;
-      g3.out_seq_stride = stride;
-      STAGE(launch_gemm(g3, EPI_OUT, dt, false, s), "adapter_down");
-    }
+  // pass 2: chunk by chunk, mel (normalised by the stream's maximum) -> encoder
+  for (int64_t e0 = 0; e0 < sp.N; e0 += sp.Fc) {
+    const int64_t e1 = std::min(sp.N, e0 + sp.Fc);
+    const int drop = e0 > 0 ? 1 : 0;
+    const int64_t m0 = std::max<int64_t>(0, 8 * e0 - 8), m1 = std::min(sp.T, 8 * e1);
+    int64_t lens[1] = {m1 - m0};
+    if (half_up(half_up(half_up(lens[0]))) != e1 - e0 + drop)
+      return fail(MT_ERR_INVALID_ARG, "mt_encode_stream: internal chunk geometry error");
+    st = stream_mel(wav, sp.n, m0, m1 - m0, mel, w, sp, true, s);
+    if (st != MT_OK) return st;
+    mt_batch b;
+    b.layout = MT_PACKED;
+    b.n_seqs = 1;
+    b.len = lens;
+    b.max_len = 0;
+    EncPlan ep;
+    st = plan_encode(enc, &b, window, ep);
+    if (st != MT_OK) return st;
+    StreamChunk ch;
+    ch.pos = (int)(e0 - drop);
+    ch.drop = drop;
+    ch.keep = (int)(e1 - e0);
+    st = run_encode(enc, ep, mel, window, out + e0 * d_out, w + sp.off_enc, s, &ch);
+    if (st != MT_OK) return st;
   }
-  if (stride > 0) STAGE(launch_zero_pad_rows(out, cuN, B, stride, out_d, s), "zero_pad");
   return MT_OK;
 }
 

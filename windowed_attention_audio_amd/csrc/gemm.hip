@@ -92,7 +92,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
     if constexpr (EPI == EPI_PE || EPI == EPI_OUT) {
       if (EPI == EPI_PE || a.out_seq_stride > 0) {
         const int sq = find_seq(a.cu_rows, a.nseq, row);
-        pos = row - a.cu_rows[sq];
+        pos = row - a.cu_rows[sq] + (EPI == EPI_PE ? a.pos_offset : 0);
         if (EPI == EPI_OUT) orow = (int64_t)sq * a.out_seq_stride + pos;
       }
     }

@@ -28,6 +28,9 @@ struct MelArgs {
   int64_t total_frames;
   int64_t out_rows;               // rows of the mel output (padded: B * Tmax)
   int padded;
+  int64_t frame_off;              // frame t of a sequence is its frame t + frame_off
+                                  // (a window of a longer stream: reflection at the
+                                  // stream's own ends, n_i = the stream's length)
 };
 hipError_t launch_mel(const MelArgs& a, hipStream_t s);
 
@@ -75,6 +78,7 @@ struct GemmArgs {
   int nseq;
   // row -> sequence position (EPI_PE, EPI_OUT)
   const int32_t* cu_rows;  // [nseq+1]
+  int pos_offset;          // EPI_PE: position of a sequence's row 0
   int64_t out_seq_stride;  // EPI_OUT padded: rows per sequence (0 = packed)
   const void* zeros;       // >= 16 bytes of zeros (device), read by out-of-range loads
 };

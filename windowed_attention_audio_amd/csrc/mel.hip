@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
     const int sq = fseq_s[f];
     float v = 0.f;
     if (sq >= 0) {
-      const int t = (int)(f0 + f) - a.cu_frames[sq];
+      const int t = (int)(f0 + f) - a.cu_frames[sq] + (int)a.frame_off;
       const int n = a.seq_len[sq];
       int q = 160 * t + j - 200;
       q = q < 0 ? -q : q;
