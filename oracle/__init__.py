@@ -10,9 +10,10 @@ Modules
   logmel   waveform -> normalised log-mel frames
   encoder  log-mel -> encoder frames (conv front-end, windowed-attention
            tower, head, optional SwiGLU adapter)
+  prompt   adapter frames spliced into the prompt's token embeddings
 
 Every function below is pinned by tests under ``tests/`` that check it against
 closed forms, invariants, brute force, or an independent library routine.
 """
 
-from . import logmel, encoder  # noqa: F401
+from . import logmel, encoder, prompt  # noqa: F401
