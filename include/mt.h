@@ -200,6 +200,27 @@ mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_sa
                            int32_t window, int32_t chunk_windows, float* out, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Prompt embedding with the audio spliced in (model card "MOSS-Transcribe-
+ * preview-2B-GGUF", Architecture table, rows Prompt and Audio injection): row
+ * i of the output is the token-embedding row of tokens[i], except that each
+ * position holding audio_token takes the next audio frame instead.
+ *   tokens       host int32 [n_tokens]; every id other than audio_token in
+ *                [0, vocab).
+ *   table        device [vocab, d], MT_F32, MT_BF16 or MT_F16 (the tied
+ *                embedding is kept at F16 by the model card); 16-byte (fp32) or
+ *                8-byte aligned rows.
+ *   audio        device fp32 [n_audio, d], n_audio = the number of
+ *                placeholders in tokens (e.g. the adapter output of one clip).
+ *   out          device fp32 [n_tokens, d].
+ *   ws           device workspace of >= mt_prompt_embed_workspace_size bytes
+ *                (the row map), 256-byte aligned.
+ * A count mismatch or an id out of range is reported before any launch. */
+mt_status mt_prompt_embed_workspace_size(int64_t n_tokens, size_t* bytes);
+mt_status mt_prompt_embed(const int32_t* tokens, int64_t n_tokens, int32_t audio_token,
+                          const void* table, int32_t table_dtype, int64_t vocab, int32_t d,
+                          const float* audio, int64_t n_audio, float* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* ---- diagnostics -------------------------------------------------------- */
 
 /* Stage timer.  Arms timing of one stage of mt_logmel / mt_encode, named

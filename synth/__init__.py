@@ -211,3 +211,17 @@ def geom_for(w: Workload, **over) -> dict:
     g["adapter_hidden"] = w.adapter_hidden
     g.update(over)
     return g
+
+
+def prompt_tokens(n_audio: int, vocab: int, audio_token: int, seed: int = 77) -> list:
+    """A synthetic prompt in the model card's ChatML shape (Architecture
+    table, row Prompt): some text tokens, a run of n_audio audio placeholders,
+    more text tokens.  Text ids are seeded draws from [0, vocab) other than
+    audio_token (no tokenizer is available; the ids only need to be valid)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def text(k):
+        t = rng.integers(0, vocab - 1, k)
+        return [int(x) + (1 if x >= audio_token else 0) for x in t]
+
+    return text(7) + [audio_token] * n_audio + text(9)

@@ -170,3 +170,20 @@ def test_encode_stream_rejects_null_encoder(L):
     n = C.c_size_t()
     assert L.mt_encode_stream_workspace_size(None, 16000, 104, 1, C.byref(n)) == W.MT_ERR_INVALID_ARG
     assert L.mt_encode_stream(None, None, 16000, 104, 1, None, None, 0, None) == W.MT_ERR_INVALID_ARG
+
+
+def test_prompt_embed_rejects_before_launch(L):
+    import ctypes as C
+    n = C.c_size_t()
+    assert L.mt_prompt_embed_workspace_size(0, C.byref(n)) == W.MT_ERR_INVALID_ARG
+    assert L.mt_prompt_embed_workspace_size(10, C.byref(n)) == W.MT_OK and n.value >= 80
+
+    def call(toks, dtype=W.MT_F16, d=8, n_audio=1, vocab=10):
+        arr = (C.c_int32 * len(toks))(*toks)
+        p = C.c_void_p(256)  # never dereferenced: validation fails first
+        return L.mt_prompt_embed(arr, len(toks), 9, p, dtype, vocab, d, p, n_audio, p, p, 1 << 20, None)
+
+    assert call([1, 9, 9]) == W.MT_ERR_INVALID_ARG          # 2 placeholders, 1 frame
+    assert call([1, 11, 9]) == W.MT_ERR_INVALID_ARG         # id outside the vocabulary
+    assert call([1, 9], dtype=7) == W.MT_ERR_INVALID_ARG    # unknown table type
+    assert call([1, 9], d=6) == W.MT_ERR_INVALID_ARG        # d not a multiple of 4

@@ -31,6 +31,7 @@ EXPORTS = (
     "mt_encoder_n_weights", "mt_encoder_packed_bytes", "mt_encoder_create",
     "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
     "mt_encode_stream_workspace_size", "mt_encode_stream",
+    "mt_prompt_embed_workspace_size", "mt_prompt_embed",
     "mt_status_string", "mt_last_error", "mt_trace_arm", "mt_trace_collect",
 )
 
@@ -88,6 +89,10 @@ def lib():
                                                       ctypes.c_int32, ctypes.POINTER(c_sz)]
         L.mt_encode_stream.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp,
                                        vp, c_sz, vp]
+        L.mt_prompt_embed_workspace_size.argtypes = [ctypes.c_int64, ctypes.POINTER(c_sz)]
+        L.mt_prompt_embed.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, ctypes.c_int32,
+                                      vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp,
+                                      ctypes.c_int64, vp, vp, c_sz, vp]
         L.mt_trace_arm.argtypes = [ctypes.c_char_p, ctypes.c_int32]
         L.mt_trace_arm.restype = ctypes.c_int
         L.mt_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -98,7 +103,8 @@ def lib():
         L.mt_last_error.restype = ctypes.c_char_p
         for name in ("mt_logmel_workspace_size", "mt_logmel", "mt_encoder_packed_bytes",
                      "mt_encoder_create", "mt_encode_workspace_size", "mt_encode",
-                     "mt_encode_stream_workspace_size", "mt_encode_stream"):
+                     "mt_encode_stream_workspace_size", "mt_encode_stream",
+                     "mt_prompt_embed_workspace_size", "mt_prompt_embed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -276,6 +282,35 @@ def mt_encode_stream(enc: Encoder, wav, window, chunk_windows, out=None, ws=None
     _check(lib().mt_encode_stream(enc.handle, ctypes.c_void_p(wav.data_ptr()), int(n), int(window),
                                   int(chunk_windows), ctypes.c_void_p(out.data_ptr()),
                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
+    return out
+
+
+def mt_prompt_embed_workspace_size(n_tokens) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_prompt_embed_workspace_size(int(n_tokens), ctypes.byref(n)))
+    return n.value
+
+
+def mt_prompt_embed(tokens, table, audio, audio_token, out=None, ws=None, stream=None):
+    """tokens: host int sequence [S]; table: CUDA tensor [vocab, d] (float32,
+    bfloat16 or float16); audio: fp32 CUDA tensor [A, d] with A = the number of
+    audio_token entries.  Returns fp32 [S, d]."""
+    import torch
+    dt = {torch.float32: MT_F32, torch.bfloat16: MT_BF16, torch.float16: MT_F16}[table.dtype]
+    assert table.is_cuda and table.is_contiguous() and table.dim() == 2
+    assert audio.is_cuda and audio.dtype == torch.float32 and audio.is_contiguous()
+    toks = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+    d = table.shape[1]
+    if out is None:
+        out = torch.empty((len(tokens), d), dtype=torch.float32, device=table.device)
+    if ws is None:
+        ws = torch.empty(mt_prompt_embed_workspace_size(len(tokens)), dtype=torch.uint8,
+                         device=table.device)
+    _check(lib().mt_prompt_embed(toks, len(tokens), int(audio_token),
+                                 ctypes.c_void_p(table.data_ptr()), dt, table.shape[0], d,
+                                 ctypes.c_void_p(audio.data_ptr()), audio.shape[0],
+                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                 ws.numel(), _stream_ptr(stream)))
     return out
 
 

@@ -911,4 +911,55 @@ mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_sa
   return MT_OK;
 }
 
+
+mt_status mt_prompt_embed_workspace_size(int64_t n_tokens, size_t* bytes) {
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  if (n_tokens < 1 || n_tokens > INT32_MAX)
+    return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: n_tokens %lld out of range", (long long)n_tokens);
+  *bytes = ((size_t)n_tokens * 8 + ALIGN - 1) / ALIGN * ALIGN;
+  return MT_OK;
+}
+
+mt_status mt_prompt_embed(const int32_t* tokens, int64_t n_tokens, int32_t audio_token, const void* table,
+                          int32_t table_dtype, int64_t vocab, int32_t d, const float* audio,
+                          int64_t n_audio, float* out, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  mt_status st = mt_prompt_embed_workspace_size(n_tokens, &need);
+  if (st != MT_OK) return st;
+  if (!tokens) return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: tokens is NULL");
+  if (table_dtype != MT_F32 && table_dtype != MT_BF16 && table_dtype != MT_F16)
+    return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: table_dtype %d unknown", table_dtype);
+  if (d < 4 || d % 4) return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: d = %d must be a positive multiple of 4", d);
+  if (vocab < 1) return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: vocab must be >= 1");
+  if (n_audio < 0) return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: n_audio < 0");
+  std::vector<int64_t> map((size_t)n_tokens);
+  int64_t k = 0;
+  for (int64_t i = 0; i < n_tokens; ++i) {
+    const int32_t t = tokens[i];
+    if (t == audio_token) {
+      map[i] = -(++k);
+    } else {
+      if (t < 0 || t >= vocab)
+        return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: tokens[%lld] = %d outside [0, %lld)",
+                    (long long)i, t, (long long)vocab);
+      map[i] = t;
+    }
+  }
+  if (k != n_audio)
+    return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: %lld audio placeholders for %lld audio frames",
+                (long long)k, (long long)n_audio);
+  if (!table || !out || !ws || (n_audio > 0 && !audio))
+    return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: NULL device pointer");
+  if ((uintptr_t)ws % ALIGN || (uintptr_t)out % 16 || (uintptr_t)audio % 16 ||
+      (uintptr_t)table % (table_dtype == MT_F32 ? 16 : 8))
+    return fail(MT_ERR_INVALID_ARG, "mt_prompt_embed: misaligned pointer");
+  if (ws_bytes < need)
+    return fail(MT_ERR_WORKSPACE, "mt_prompt_embed: workspace %zu bytes < required %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(upload_words((uint32_t*)ws, (const uint32_t*)map.data(), 2 * n_tokens, s), "upload tables");
+  const int dt = table_dtype == MT_F32 ? DT_F32 : table_dtype == MT_BF16 ? DT_BF16 : DT_F16;
+  HIP_TRY(launch_splice((const int64_t*)ws, n_tokens, table, dt, audio, out, d, s), "splice");
+  return MT_OK;
+}
+
 }  // extern "C"

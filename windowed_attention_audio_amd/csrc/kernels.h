@@ -121,6 +121,10 @@ hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int3
 // destination element type (DT_*).
 hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
                           int64_t dst_col0, int dtype, hipStream_t s);
+// Prompt embedding: out[i] = table[map[i]] (map[i] >= 0, table rows of d
+// elements of dtype) or audio[-map[i] - 1] (fp32 rows); out fp32 [rows][d].
+hipError_t launch_splice(const int64_t* map, int64_t rows, const void* table, int dtype,
+                         const float* audio, float* out, int d, hipStream_t s);
 hipError_t launch_pack_conv(const float* w, void* dst, int C, int dtype, hipStream_t s);
 hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int dtype,
                                 hipStream_t s);

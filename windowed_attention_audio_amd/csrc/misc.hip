@@ -146,6 +146,38 @@ inline dim3 grid_for(int64_t n) {
   return dim3((unsigned)b);
 }
 
+
+// Prompt embedding with the audio spliced in (model card "MOSS-Transcribe-
+// preview-2B-GGUF", Architecture table, rows Prompt and Audio injection):
+// output row i is table row map[i] (map[i] >= 0) or audio row -map[i] - 1.
+// One workgroup per row, 16-byte stores.
+__global__ void splice_kernel(const int64_t* __restrict__ map, const void* __restrict__ table,
+                              int dtype, const float* __restrict__ audio, float* __restrict__ out,
+                              int d) {
+  const int64_t row = blockIdx.x;
+  const int64_t src = map[row];
+  float4* o = (float4*)(out + row * d);
+  for (int c4 = threadIdx.x; c4 < d / 4; c4 += blockDim.x) {
+    float4 v;
+    if (src < 0) {
+      v = ((const float4*)(audio + (-src - 1) * (int64_t)d))[c4];
+    } else if (dtype == DT_F32) {
+      v = ((const float4*)((const float*)table + src * d))[c4];
+    } else {
+      const uint2 u = ((const uint2*)((const char*)table + src * d * 2))[c4];
+      const uint32_t w[4] = {u.x & 0xffffu, u.x >> 16, u.y & 0xffffu, u.y >> 16};
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (dtype == DT_BF16) f[e] = Elem<bf16_t>::to_f(__builtin_bit_cast(bf16_t, (uint16_t)w[e]));
+        else f[e] = Elem<f16_t>::to_f(__builtin_bit_cast(f16_t, (uint16_t)w[e]));
+      }
+      v = make_float4(f[0], f[1], f[2], f[3]);
+    }
+    o[c4] = v;
+  }
+}
+
 }  // namespace
 
 hipError_t upload_words(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s) {
@@ -191,6 +223,14 @@ hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t col
                           int64_t dst_col0, int dtype, hipStream_t s) {
   hipLaunchKernelGGL(convert_kernel, grid_for(rows * cols), dim3(256), 0, s, src, dst, rows, cols,
                      dst_ld, dst_col0, dtype);
+  return hipGetLastError();
+}
+
+hipError_t launch_splice(const int64_t* map, int64_t rows, const void* table, int dtype,
+                         const float* audio, float* out, int d, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(splice_kernel, dim3((unsigned)rows), dim3(256), 0, s, map, table, dtype, audio, out,
+                     d);
   return hipGetLastError();
 }
 
