@@ -10,10 +10,13 @@ Modules
   logmel   waveform -> normalised log-mel frames
   encoder  log-mel -> encoder frames (conv front-end, windowed-attention
            tower, head, optional SwiGLU adapter)
+  encoder2x  log-mel -> encoder frames of the full-attention variant with a
+             2x time-downsampling front-end (page "CrisperWhisper -> ONNX
+             (with cross-attentions)": whisper geometries)
   prompt   adapter frames spliced into the prompt's token embeddings
 
 Every function below is pinned by tests under ``tests/`` that check it against
 closed forms, invariants, brute force, or an independent library routine.
 """
 
-from . import logmel, encoder, prompt  # noqa: F401
+from . import logmel, encoder, encoder2x, prompt  # noqa: F401

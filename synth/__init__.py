@@ -53,6 +53,19 @@ FULL_GEOM = dict(
     adapter_hidden=0,
 )
 
+# The full-attention variant with the 2x conv front-end, at the two whisper
+# geometries the CrisperWhisper export page names (small: 12 layers, d 768,
+# 12 heads; large-v3: 32 layers at the tower's 32 x 1280 geometry).  FFN 4d
+# and 128 mel bins are readings (the page gives neither).
+WHISPER_SMALL_GEOM = dict(
+    frontend="conv1d_2x", n_mels=128, conv_ch=768, d_model=768, n_layers=12, n_heads=12,
+    head_dim=64, d_ffn=3072, d_out=768, adapter_hidden=0,
+)
+WHISPER_LARGE_GEOM = dict(
+    frontend="conv1d_2x", n_mels=128, conv_ch=1280, d_model=1280, n_layers=32, n_heads=20,
+    head_dim=64, d_ffn=5120, d_out=1280, adapter_hidden=0,
+)
+
 WEIGHT_SEED = 1234
 ADAPTER_SEED = 1235
 
@@ -136,12 +149,19 @@ def weight_names(geom: dict) -> list:
     D = geom["d_model"]
     H = geom["d_ffn"]
     O = geom["d_out"]
-    out = [
-        ("conv1.weight", (C, 1, 3, 3)), ("conv1.bias", (C,)),
-        ("conv2.weight", (C, C, 3, 3)), ("conv2.bias", (C,)),
-        ("conv3.weight", (C, C, 3, 3)), ("conv3.bias", (C,)),
-        ("conv_out.weight", (D, C * F8)),
-    ]
+    two_x = geom.get("frontend", "conv2d_8x") == "conv1d_2x"
+    if two_x:  # Conv1d weights are [out, in, k(time)]
+        out = [
+            ("conv1.weight", (D, geom["n_mels"], 3)), ("conv1.bias", (D,)),
+            ("conv2.weight", (D, D, 3)), ("conv2.bias", (D,)),
+        ]
+    else:
+        out = [
+            ("conv1.weight", (C, 1, 3, 3)), ("conv1.bias", (C,)),
+            ("conv2.weight", (C, C, 3, 3)), ("conv2.bias", (C,)),
+            ("conv3.weight", (C, C, 3, 3)), ("conv3.bias", (C,)),
+            ("conv_out.weight", (D, C * F8)),
+        ]
     for l in range(geom["n_layers"]):
         p = f"layers.{l}."
         out += [
@@ -154,8 +174,10 @@ def weight_names(geom: dict) -> list:
             (p + "fc1.weight", (H, D)), (p + "fc1.bias", (H,)),
             (p + "fc2.weight", (D, H)), (p + "fc2.bias", (D,)),
         ]
+    out += [("ln_post.weight", (D,)), ("ln_post.bias", (D,))]
+    if two_x:
+        return out
     out += [
-        ("ln_post.weight", (D,)), ("ln_post.bias", (D,)),
         ("proj1.weight", (D, D)), ("proj1.bias", (D,)),
         ("proj2.weight", (O, D)), ("proj2.bias", (O,)),
     ]
@@ -195,8 +217,8 @@ def make_weights(geom: dict, bf16: bool, seed: int = WEIGHT_SEED,
                     a = (0.1 * lrng.standard_normal(shape)).astype(np.float32)
             else:
                 a = (np.ones if name.endswith("weight") else np.zeros)(shape, np.float32)
-        elif name.startswith("conv") and name.endswith(".weight") and len(shape) == 4:
-            fan_in = shape[1] * shape[2] * shape[3]
+        elif name.startswith("conv") and name.endswith(".weight") and len(shape) >= 3:
+            fan_in = int(np.prod(shape[1:]))
             a = rng.standard_normal(shape, dtype=np.float32) * np.float32(1.0 / math.sqrt(fan_in))
         else:
             a = rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
