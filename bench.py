@@ -189,6 +189,69 @@ def splice_measure(W, frames, lens_T, synth, torch, np, vocab=151936, audio_toke
             "note": "includes the host-side row map upload (kernel arguments)"}
 
 
+def flops_2x(geom, lens_T):
+    """Multiply-add count x 2 of one forward pass of the 2x-front-end encoder
+    with full attention (excluding the log-mel)."""
+    D, F, L = geom["d_model"], geom["d_ffn"], geom["n_layers"]
+    tot = dict(conv1=0, conv2=0, qkv=0, attn=0, o=0, ffn=0)
+    for T in lens_T:
+        N = (T + 1) // 2
+        tot["conv1"] += 2 * T * 3 * geom["n_mels"] * D
+        tot["conv2"] += 2 * N * 3 * D * D
+        tot["qkv"] += L * 2 * N * D * 3 * D
+        tot["o"] += L * 2 * N * D * D
+        tot["ffn"] += L * 2 * 2 * N * D * F
+        tot["attn"] += L * 4 * N * N * D
+    return tot
+
+
+def measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel, steps=10, warmup=2):
+    """The full-attention encoder with the 2x conv front-end at the 32 x 1280
+    geometry (32 layers, 20 heads, FFN 5120) on the same 16 x 30 s batch: log-mel
+    + encode per step, fp16 operands."""
+    geom = synth.WHISPER_LARGE_GEOM
+    weights = synth.make_weights(geom, bf16=True)
+    dev_w = [torch.from_numpy(v).cuda() for v in weights.values()]
+    enc = W.mt_encoder_create(W.encoder_config(geom, W.MT_F16), dev_w)
+    torch.cuda.synchronize()
+    del dev_w
+    full = 1 << 30
+    M = sum(W.mt_encoder_frames_for(W.MT_FRONTEND_CONV1D_2X, t) for t in lens_T)
+    out = torch.empty((M, geom["d_model"]), dtype=torch.float32, device="cuda")
+    ws = torch.empty(W.mt_encode_workspace_size(enc, lens_T, full), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream)
+        W.mt_encode(enc, mel, lens_T, full, out=out, ws=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stages = {}
+    for st in ("mel16", "conv1", "conv2", "ln1", "qkv", "attn", "o", "ln2", "fc1", "fc2", "ln_post"):
+        W.mt_trace_arm(st, max_launches=64)
+        W.mt_trace_collect()
+        step()
+        torch.cuda.synchronize()
+        t, _ = W.mt_trace_collect()
+        stages[st] = round(t, 4)
+    W.mt_trace_arm(None)
+    fl = sum(flops_2x(geom, lens_T).values())
+    enc.close()
+    return {"workload": "16x30s_conv1d_2x_32x1280_full_attention", "encoder_frames": M,
+            "ms_per_step": round(ms, 4), "audio_s_per_s": round(sum(lens) / 16000.0 / (ms * 1e-3), 1),
+            "step_tflops": round(fl / (ms * 1e-3) / 1e12, 1), "breakdown_ms_per_step": stages}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +260,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
+    ap.add_argument("--no-2x", action="store_true",
+                    help="skip the 2x-front-end full-attention workload")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the bounded-memory stream measurement (10-minute stream)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -323,6 +388,8 @@ def main():
     if not args.no_stream:
         res["stream_10min"] = stream_measure(W, enc, synth, torch, np)
         res["prompt_splice"] = splice_measure(W, out, lens_T, synth, torch, np)
+    if not args.no_2x:
+        res["conv1d_2x_16x30s"] = measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(clips[0], weights, geom, window)
     print(json.dumps(res), flush=True)

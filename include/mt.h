@@ -73,6 +73,25 @@ typedef struct {
   int64_t max_len;
 } mt_batch;
 
+/* Front-end variants (mt_encoder_config.frontend).
+ *   MT_FRONTEND_CONV2D_8X  model card "MOSS-Transcribe-preview-2B-GGUF",
+ *       Architecture table, Conv front-end row: three 3x3 stride-2 Conv2D
+ *       (1 -> C -> C -> C channels, GELU after each) over the mel image, then
+ *       conv_out (C * 16 -> d_model) and sinusoids; windowed attention; head
+ *       ln_post -> proj1 -> GELU -> proj2 (+ optional SwiGLU adapter).
+ *   MT_FRONTEND_CONV1D_2X  the whisper geometries of page "CrisperWhisper ->
+ *       ONNX (with cross-attentions)" (sections What this exports instead and
+ *       Results: 1500 encoder frames per 30 s, full attention).  The page does
+ *       not describe the front-end; the one implemented is two 1-D
+ *       convolutions over time with kernel 3 and padding 1, the mel bins as
+ *       input channels: conv1 n_mels -> d_model stride 1, conv2 d_model ->
+ *       d_model stride 2, GELU after each, then the same sinusoids; the head
+ *       is ln_post only (d_out = d_model), no adapter; 16-bit dtypes only. */
+typedef enum {
+  MT_FRONTEND_CONV2D_8X = 0,
+  MT_FRONTEND_CONV1D_2X = 1
+} mt_frontend;
+
 /* Encoder geometry and compute type.  The production geometry is
  * {128, 480, 1280, 32, 20, 64, 5120, 2048, 0 or 8192}.  The kernels require
  * n_mels == 128, head_dim == 64, n_heads * head_dim == d_model, conv_ch a
@@ -94,6 +113,8 @@ typedef struct {
                              tower and return the fp32 residual stream
                              (d_model wide) */
   float ln_eps;           /* LayerNorm epsilon, 1e-5 */
+  int32_t frontend;       /* mt_frontend (0: the 8x Conv2D front-end).  With
+                             MT_FRONTEND_CONV1D_2X conv_ch is ignored. */
 } mt_encoder_config;
 
 typedef struct mt_encoder mt_encoder; /* opaque host handle */
@@ -107,6 +128,11 @@ int64_t mt_mel_frames(int64_t n_samples);
 /* Encoder frames for T mel frames: three stride-2 convs, ceil(ceil(ceil(T/2)/2)/2).
  * Returns -1 for T < 0. */
 int64_t mt_encoder_frames(int64_t mel_frames);
+
+/* Encoder frames for T mel frames with front-end `frontend` (mt_frontend):
+ * the 8x one as mt_encoder_frames, the 2x one ceil(T / 2).  Returns -1 for
+ * T < 0 or an unknown front-end. */
+int64_t mt_encoder_frames_for(int32_t frontend, int64_t mel_frames);
 
 /* ---- log-mel ---------------------------------------------------------- */
 
@@ -128,7 +154,8 @@ mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* w
 /* ---- encoder ---------------------------------------------------------- */
 
 /* Number of weight tensors create() expects for this geometry:
- * 7 + 16 * n_layers + 6 (+ 3 with the adapter). */
+ * 7 + 16 * n_layers + 6 (+ 3 with the adapter); with MT_FRONTEND_CONV1D_2X,
+ * 4 + 16 * n_layers + 2.  Returns -1 for an invalid configuration. */
 int32_t mt_encoder_n_weights(const mt_encoder_config* cfg);
 
 /* Bytes of the packed-weight buffer create() needs. */
@@ -146,6 +173,10 @@ mt_status mt_encoder_packed_bytes(const mt_encoder_config* cfg, size_t* bytes);
  *   proj2.weight [O,D], proj2.bias [O];
  *   adapter only: gate.weight [A,O], up.weight [A,O], down.weight [O,A].
  * Feature j of conv_out's input is conv3 channel j / 16 at frequency j % 16.
+ * MT_FRONTEND_CONV1D_2X instead: conv1.weight [D, n_mels, 3], conv1.bias [D],
+ *   conv2.weight [D, D, 3], conv2.bias [D] (torch Conv1d [out, in, k]; tap k
+ *   reads input frame stride * t + k - 1), the same 16 per layer, then
+ *   ln_post.weight, ln_post.bias.
  * `packed` (device, >= mt_encoder_packed_bytes, 256-byte aligned) receives
  * the weights in kernel layouts (rounded to nearest-even for 16-bit types);
  * it must stay alive and unchanged until mt_encoder_destroy.  The source
@@ -168,15 +199,15 @@ int32_t mt_max_window(void);
 mt_status mt_encode_workspace_size(const mt_encoder* enc, const mt_batch* mel_b, int32_t window,
                                    size_t* bytes);
 
-/* Log-mel -> encoder frames.
+/* Log-mel -> encoder frames (N_i below is mt_encoder_frames_for(frontend, T_i)).
  *   mel     device fp32, [sum T_i, n_mels] packed or [n_seqs, max_len, n_mels]
  *           padded (rows t >= T_i are not read); each T_i >= 1.
  *   window  W >= 1, in encoder frames: frames [kW, (k+1)W) of each sequence
  *           attend only to each other, in every layer.
  *   out     device fp32, packed [sum N_i, d] or padded
- *           [n_seqs, mt_encoder_frames(max_len), d] with rows >= N_i set to 0;
- *           N_i = mt_encoder_frames(T_i); d = d_out (or d_model when
- *           with_head == 0).
+ *           [n_seqs, N(max_len), d] with rows >= N_i set to 0; d = d_out (or
+ *           d_model when with_head == 0).  MT_FRONTEND_CONV1D_2X with
+ *           with_head == 1: ln_post of the residual stream, fp32.
  *   ws      device workspace of >= mt_encode_workspace_size bytes, 256-byte
  *           aligned; its contents on entry do not matter. */
 mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel_b,
@@ -193,7 +224,9 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
  * Two passes over the waveform: the stream's log-mel maximum first (the
  * normalisation needs it), then each chunk's mel frames with their receptive
  * field (8 frames before, none after) and the encoder.  The result equals
- * mt_logmel + mt_encode of the whole stream with the same window. */
+ * mt_logmel + mt_encode of the whole stream with the same window.  Only the
+ * 8x front-end streams: an MT_FRONTEND_CONV1D_2X encoder gives
+ * MT_ERR_UNSUPPORTED. */
 mt_status mt_encode_stream_workspace_size(const mt_encoder* enc, int64_t n_samples, int32_t window,
                                           int32_t chunk_windows, size_t* bytes);
 mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_samples,

@@ -187,3 +187,45 @@ def test_prompt_embed_rejects_before_launch(L):
     assert call([1, 11, 9]) == W.MT_ERR_INVALID_ARG         # id outside the vocabulary
     assert call([1, 9], dtype=7) == W.MT_ERR_INVALID_ARG    # unknown table type
     assert call([1, 9], d=6) == W.MT_ERR_INVALID_ARG        # d not a multiple of 4
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 3, 3000, 3001])
+def test_encoder_frames_for(L, T):
+    from oracle import encoder2x as OE2
+    assert W.mt_encoder_frames_for(W.MT_FRONTEND_CONV2D_8X, T) == W.mt_encoder_frames(T)
+    want = OE2.frames_2x(T) if T else 0
+    assert W.mt_encoder_frames_for(W.MT_FRONTEND_CONV1D_2X, T) == want == -(-T // 2)
+    assert W.mt_encoder_frames_for(W.MT_FRONTEND_CONV1D_2X, -1) == -1
+    assert W.mt_encoder_frames_for(5, T) == -1
+
+
+def test_config_validation_2x(L):
+    for geom in (synth.WHISPER_SMALL_GEOM, synth.WHISPER_LARGE_GEOM):
+        cfg = W.encoder_config(geom, W.MT_F16)
+        assert W.mt_encoder_n_weights(cfg) == 4 + 16 * geom["n_layers"] + 2 == \
+            len(synth.weight_names(geom))
+        # conv_ch is ignored by this front-end
+        assert W.mt_encoder_packed_bytes(W.encoder_config(dict(geom, conv_ch=1), W.MT_F16)) == \
+            W.mt_encoder_packed_bytes(cfg)
+    for over, dt, status in ((dict(), W.MT_F32, W.MT_ERR_UNSUPPORTED),
+                             (dict(adapter_hidden=1024), W.MT_BF16, W.MT_ERR_INVALID_ARG),
+                             (dict(d_out=2048), W.MT_BF16, W.MT_ERR_INVALID_ARG)):
+        cfg = W.encoder_config(dict(synth.WHISPER_SMALL_GEOM, **over), dt)
+        with pytest.raises(W.MtError) as e:
+            W.mt_encoder_packed_bytes(cfg)
+        assert e.value.status == status, over
+    cfg = W.encoder_config(synth.WHISPER_SMALL_GEOM, W.MT_BF16)
+    cfg.frontend = 9
+    with pytest.raises(W.MtError) as e:
+        W.mt_encoder_packed_bytes(cfg)
+    assert e.value.status == W.MT_ERR_INVALID_ARG
+
+
+def test_packed_bytes_2x(L):
+    geom = synth.WHISPER_SMALL_GEOM
+    names = synth.weight_names(geom)
+    n_mat = sum(int(np.prod(s)) for _, s in names if len(s) > 1)
+    n_vec = sum(int(np.prod(s)) for _, s in names if len(s) == 1)
+    b16 = W.mt_encoder_packed_bytes(W.encoder_config(geom, W.MT_BF16))
+    expect = 2 * n_mat + 4 * n_vec
+    assert expect <= b16 <= expect + 256 * (len(names) + 1)

@@ -6,6 +6,7 @@ The functions carry the names of the C entry points (include/mt.h):
 
     mt_mel_frames(n)                 floor(n / 160)
     mt_encoder_frames(T)             ceil(ceil(ceil(T / 2) / 2) / 2)
+    mt_encoder_frames_for(f, T)      the same for front-end f (2x: ceil(T / 2))
     mt_logmel(wav, lens, ...)        waveform -> normalised log-mel
     mt_encoder_create(cfg, weights)  -> Encoder (packed weights on device)
     mt_encode(enc, mel, lens, W)     log-mel -> encoder frames
@@ -25,9 +26,12 @@ LIB_PATH = os.path.join(_HERE, "libmt.so")
 MT_OK, MT_ERR_INVALID_ARG, MT_ERR_UNSUPPORTED, MT_ERR_WORKSPACE, MT_ERR_HIP = range(5)
 MT_F32, MT_BF16, MT_F16 = 0, 1, 2
 MT_PACKED, MT_PADDED = 0, 1
+MT_FRONTEND_CONV2D_8X, MT_FRONTEND_CONV1D_2X = 0, 1
+FRONTENDS = {"conv2d_8x": MT_FRONTEND_CONV2D_8X, "conv1d_2x": MT_FRONTEND_CONV1D_2X}
 
 EXPORTS = (
-    "mt_mel_frames", "mt_encoder_frames", "mt_logmel_workspace_size", "mt_logmel",
+    "mt_mel_frames", "mt_encoder_frames", "mt_encoder_frames_for", "mt_logmel_workspace_size",
+    "mt_logmel",
     "mt_encoder_n_weights", "mt_encoder_packed_bytes", "mt_encoder_create",
     "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
     "mt_encode_stream_workspace_size", "mt_encode_stream",
@@ -53,7 +57,8 @@ class EncoderConfig(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("d_ffn", ctypes.c_int32), ("d_out", ctypes.c_int32),
                 ("adapter_hidden", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("with_head", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+                ("with_head", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("frontend", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,6 +78,8 @@ def lib():
         L.mt_mel_frames.argtypes = [ctypes.c_int64]
         L.mt_encoder_frames.restype = ctypes.c_int64
         L.mt_encoder_frames.argtypes = [ctypes.c_int64]
+        L.mt_encoder_frames_for.restype = ctypes.c_int64
+        L.mt_encoder_frames_for.argtypes = [ctypes.c_int32, ctypes.c_int64]
         L.mt_logmel_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(c_sz)]
         L.mt_logmel.argtypes = [vp, ctypes.POINTER(Batch), vp, vp, c_sz, vp]
         L.mt_encoder_n_weights.argtypes = [ctypes.POINTER(EncoderConfig)]
@@ -139,6 +146,10 @@ def mt_encoder_frames(T: int) -> int:
     return lib().mt_encoder_frames(int(T))
 
 
+def mt_encoder_frames_for(frontend: int, T: int) -> int:
+    return lib().mt_encoder_frames_for(int(frontend), int(T))
+
+
 def mt_max_window() -> int:
     return lib().mt_max_window()
 
@@ -173,9 +184,11 @@ def mt_logmel(wav, lens, layout=MT_PACKED, max_len=0, mel=None, ws=None, stream=
 
 
 def encoder_config(geom: dict, dtype: int, with_head: bool = True, ln_eps: float = 1e-5):
+    """geom["frontend"]: "conv2d_8x" (default) or "conv1d_2x"."""
     return EncoderConfig(geom["n_mels"], geom["conv_ch"], geom["d_model"], geom["n_layers"],
                          geom["n_heads"], geom["head_dim"], geom["d_ffn"], geom["d_out"],
-                         geom.get("adapter_hidden", 0), dtype, 1 if with_head else 0, ln_eps)
+                         geom.get("adapter_hidden", 0), dtype, 1 if with_head else 0, ln_eps,
+                         FRONTENDS[geom.get("frontend", "conv2d_8x")])
 
 
 class Encoder:
@@ -242,10 +255,11 @@ def mt_encode(enc: Encoder, mel, lens, window, layout=MT_PACKED, out=None, ws=No
     assert mel.is_cuda and mel.dtype == torch.float32 and mel.is_contiguous()
     max_len = mel.shape[1] if layout == MT_PADDED else 0
     d = enc.d_out
+    fe = enc.cfg.frontend
     if layout == MT_PADDED:
-        shape = (len(lens), mt_encoder_frames(max_len), d)
+        shape = (len(lens), mt_encoder_frames_for(fe, max_len), d)
     else:
-        shape = (sum(mt_encoder_frames(int(t)) for t in lens), d)
+        shape = (sum(mt_encoder_frames_for(fe, int(t)) for t in lens), d)
     b = make_batch(lens, layout, max_len)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=mel.device)

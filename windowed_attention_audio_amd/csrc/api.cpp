@@ -76,6 +76,10 @@ struct TraceScope {
   }
 };
 inline int64_t half_up(int64_t x) { return (x + 1) / 2; }
+// Encoder frames of T mel frames: three stride-2 convs (8x) or one (2x).
+inline int64_t frames_of(int frontend, int64_t T) {
+  return frontend == MT_FRONTEND_CONV1D_2X ? half_up(T) : half_up(half_up(half_up(T)));
+}
 
 // Carves named regions out of one buffer.
 struct Carver {
@@ -188,15 +192,27 @@ mt_status check_config(const mt_encoder_config* c) {
   if (!(c->ln_eps > 0.f)) return fail(MT_ERR_INVALID_ARG, "ln_eps must be > 0");
   if (c->with_head != 0 && c->with_head != 1)
     return fail(MT_ERR_INVALID_ARG, "with_head must be 0 or 1");
+  if (c->frontend != MT_FRONTEND_CONV2D_8X && c->frontend != MT_FRONTEND_CONV1D_2X)
+    return fail(MT_ERR_INVALID_ARG, "frontend %d is not an mt_frontend", c->frontend);
   if (c->n_mels != 128) return fail(MT_ERR_UNSUPPORTED, "n_mels must be 128");
   if (c->head_dim != 64) return fail(MT_ERR_UNSUPPORTED, "head_dim must be 64");
   if (c->n_heads * c->head_dim != c->d_model)
     return fail(MT_ERR_UNSUPPORTED, "n_heads * head_dim must equal d_model");
   if (c->d_model % 256 || c->d_model > 2048)
     return fail(MT_ERR_UNSUPPORTED, "d_model must be a multiple of 256, at most 2048");
-  if (c->conv_ch % 32) return fail(MT_ERR_UNSUPPORTED, "conv_ch must be a multiple of 32");
   if (c->d_ffn % 64 || c->d_out % 64 || c->adapter_hidden % 64)
     return fail(MT_ERR_UNSUPPORTED, "d_ffn, d_out, adapter_hidden must be multiples of 64");
+  if (c->frontend == MT_FRONTEND_CONV1D_2X) {
+    // 1-D convolutions and a ln_post-only head; the convolutions run on the
+    // 16-bit matrix-core path only
+    if (c->dtype == MT_F32)
+      return fail(MT_ERR_UNSUPPORTED, "the 2x front-end needs MT_BF16 or MT_F16");
+    if (c->adapter_hidden) return fail(MT_ERR_INVALID_ARG, "the 2x front-end has no adapter");
+    if (c->d_out != c->d_model)
+      return fail(MT_ERR_INVALID_ARG, "the 2x front-end's output is d_model wide (d_out = d_model)");
+    return MT_OK;
+  }
+  if (c->conv_ch % 32) return fail(MT_ERR_UNSUPPORTED, "conv_ch must be a multiple of 32");
   if (c->conv_ch > 2048) return fail(MT_ERR_UNSUPPORTED, "conv_ch must be at most 2048");
   if (c->adapter_hidden && !c->with_head)
     return fail(MT_ERR_INVALID_ARG, "the adapter needs with_head = 1");
@@ -208,15 +224,24 @@ PackedLayout packed_layout(const mt_encoder_config& c) {
   const size_t es = half ? 2 : 4;
   const size_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
   const size_t KD = half ? 2 * D : D;  // hi/lo split head input
+  const bool two_x = c.frontend == MT_FRONTEND_CONV1D_2X;
   PackedLayout p;
   Carver k;
-  p.conv1_w = k.take(C * 9 * 4);
-  p.conv1_b = k.take(C * 4);
-  p.conv2_w = k.take(C * 9 * C * es);
-  p.conv2_b = k.take(C * 4);
-  p.conv3_w = k.take(C * 9 * C * es);
-  p.conv3_b = k.take(C * 4);
-  p.conv_out_w = k.take(D * 16 * C * es);
+  if (two_x) {  // conv1 [D][3 n_mels], conv2 [D][3 D], 16-bit
+    p.conv1_w = k.take(D * 3 * (size_t)c.n_mels * es);
+    p.conv1_b = k.take(D * 4);
+    p.conv2_w = k.take(D * 3 * D * es);
+    p.conv2_b = k.take(D * 4);
+    p.conv3_w = p.conv3_b = p.conv_out_w = 0;
+  } else {
+    p.conv1_w = k.take(C * 9 * 4);
+    p.conv1_b = k.take(C * 4);
+    p.conv2_w = k.take(C * 9 * C * es);
+    p.conv2_b = k.take(C * 4);
+    p.conv3_w = k.take(C * 9 * C * es);
+    p.conv3_b = k.take(C * 4);
+    p.conv_out_w = k.take(D * 16 * C * es);
+  }
   p.layers.resize(c.n_layers);
   for (auto& L : p.layers) {
     L.ln1_g = k.take(D * 4);
@@ -234,10 +259,10 @@ PackedLayout packed_layout(const mt_encoder_config& c) {
   }
   p.lnp_g = k.take(D * 4);
   p.lnp_b = k.take(D * 4);
-  p.wp1 = k.take(D * KD * es);
-  p.bp1 = k.take(D * 4);
-  p.wp2 = k.take(O * KD * es);
-  p.bp2 = k.take(O * 4);
+  p.wp1 = two_x ? 0 : k.take(D * KD * es);
+  p.bp1 = two_x ? 0 : k.take(D * 4);
+  p.wp2 = two_x ? 0 : k.take(O * KD * es);
+  p.bp2 = two_x ? 0 : k.take(O * 4);
   p.wgu = A ? k.take(2 * A * O * es) : 0;
   p.wd = A ? k.take(O * A * es) : 0;
   p.zeros = k.take(256);
@@ -246,6 +271,7 @@ PackedLayout packed_layout(const mt_encoder_config& c) {
 }
 
 int n_weights_of(const mt_encoder_config& c) {
+  if (c.frontend == MT_FRONTEND_CONV1D_2X) return 4 + 16 * c.n_layers + 2;
   return 7 + 16 * c.n_layers + 6 + (c.adapter_hidden ? 3 : 0);
 }
 
@@ -301,7 +327,9 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   for (int i = 0; i < B; ++i) {
     const int64_t T = mb->len[i];
     if (T < 1) return fail(MT_ERR_INVALID_ARG, "mt_encode: len[%d] must be >= 1 mel frame", i);
-    const int64_t T1 = half_up(T), T2 = half_up(T1), N = half_up(T2);
+    const bool two_x = c.frontend == MT_FRONTEND_CONV1D_2X;
+    // 2x: T1 is conv1's output (stride 1), T2 unused
+    const int64_t T1 = two_x ? T : half_up(T), T2 = two_x ? 0 : half_up(T1), N = frames_of(c.frontend, T);
     p.mel_row_off[i] = mb->layout == MT_PADDED ? (int64_t)i * mb->max_len : p.sumT;
     p.sumT += T;
     p.sumT1 += T1;
@@ -322,7 +350,7 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
     return fail(MT_ERR_UNSUPPORTED, "mt_encode: window %d over sequences of up to %lld frames "
                 "exceeds the fp32 on-chip maximum %d", window, (long long)p.maxN, MAX_WINDOW);
   p.wpad = (int)((weff + 63) / 64 * 64);  // whole key chunks of 64 (on chip up to MAX_WINDOW)
-  p.out_stride = mb->layout == MT_PADDED ? half_up(half_up(half_up(mb->max_len))) : 0;
+  p.out_stride = mb->layout == MT_PADDED ? frames_of(c.frontend, mb->max_len) : 0;
 
   const size_t es = enc->es;
   const size_t C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
@@ -331,12 +359,18 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   p.o_words = k.take(4 * p.words.size());
   p.o_rowoff = k.take(8 * (size_t)B);
   p.o_twords = k.take(16);
-  p.o_act1 = k.take((size_t)p.sumT1 * 64 * C * es);
-  p.o_act2 = k.take((size_t)p.sumT2 * 32 * C * es);
-  p.o_act3 = k.take(M * 16 * C * es);
+  if (c.frontend == MT_FRONTEND_CONV1D_2X) {
+    p.o_act1 = k.take((size_t)p.sumT * D * es);                  // conv1 output [T][D]
+    p.o_act2 = k.take((size_t)p.sumT * (size_t)c.n_mels * es);  // 16-bit log-mel [T][n_mels]
+    p.o_act3 = k.take(0);
+  } else {
+    p.o_act1 = k.take((size_t)p.sumT1 * 64 * C * es);
+    p.o_act2 = k.take((size_t)p.sumT2 * 32 * C * es);
+    p.o_act3 = k.take(M * 16 * C * es);
+  }
   p.o_x = k.take(M * D * 4);
   size_t hb = M * D * es;
-  if (c.with_head && enc->dt != DT_F32) hb = std::max(hb, M * 2 * D * 2);
+  if (c.with_head && enc->dt != DT_F32) hb = std::max(hb, M * 2 * D * 2);  // hi/lo, or fp32 ln_post
   p.o_h = k.take(hb);
   p.o_qkv = k.take(M * 3 * D * es);
   p.o_att = k.take(M * D * es);
@@ -410,6 +444,33 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   };
 
   // ---- front-end
+  if (c.frontend == MT_FRONTEND_CONV1D_2X) {
+    // 16-bit log-mel rows, packed; conv1 (stride 1) -> GELU; conv2 (stride
+    // 2) -> GELU -> + sinusoids into the fp32 residual stream
+    STAGE(launch_rows_to_half(mel, (const int64_t*)(w + p.o_rowoff), cuT, B, p.sumT, c.n_mels, act2, dt,
+                              s), "mel16");
+    GemmArgs g = gemm(act2, 0, enc->conv1_w, 3 * c.n_mels, (int)p.sumT, D, 3 * c.n_mels, enc->conv1_b,
+                      act1, D);
+    g.conv_C = c.n_mels;
+    g.conv_Fin = 1;
+    g.conv_Fout = 1;
+    g.conv_kind = CONV_1D_S1;
+    g.cu_in = cuT;
+    g.cu_out = cuT;
+    g.nseq = B;
+    STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv1");
+    g = gemm(act1, 0, enc->conv2_w, 3 * D, M, D, 3 * D, enc->conv2_b, x, D);
+    g.conv_C = D;
+    g.conv_Fin = 1;
+    g.conv_Fout = 1;
+    g.conv_kind = CONV_1D_S2;
+    g.cu_in = cuT;
+    g.cu_out = cuN;
+    g.nseq = B;
+    g.cu_rows = cuN;
+    g.pos_offset = 0;
+    STAGE(launch_gemm(g, EPI_GELU_PE, dt, true, s), "conv2");
+  } else {
   Conv1Args c1;
   c1.mel = mel;
   c1.mel_row_off = (const int64_t*)(w + p.o_rowoff);
@@ -445,6 +506,7 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   g.nseq = B;
   g.pos_offset = ch ? ch->pos : 0;
   STAGE(launch_gemm(g, EPI_PE, dt, false, s), "conv_out");
+  }
 
   // ---- tower (a stream chunk: its kept rows only, as one sequence)
   int64_t n_windows = p.n_windows;
@@ -485,6 +547,10 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   int out_d = D;
   if (!c.with_head) {
     STAGE(launch_copy_rows(x, out, M, D, cuN, ch ? 1 : B, stride, s), "copy_rows");
+  } else if (c.frontend == MT_FRONTEND_CONV1D_2X) {
+    float* y = (float*)h;  // ln_post in fp32, then into the output layout
+    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, y, M, D, c.ln_eps, DT_F32, false, s), "ln_post");
+    STAGE(launch_copy_rows(y, out, M, D, cuN, B, stride, s), "copy_rows");
   } else {
     out_d = O;
     // 16-bit operands: the head's activations enter as hi/lo pairs (K doubled)
@@ -531,6 +597,8 @@ struct StreamPlan {
 mt_status plan_stream(const mt_encoder* enc, int64_t n_samples, int32_t window, int32_t chunk_windows,
                       StreamPlan& sp) {
   if (!enc) return fail(MT_ERR_INVALID_ARG, "encoder is NULL");
+  if (enc->cfg.frontend != MT_FRONTEND_CONV2D_8X)
+    return fail(MT_ERR_UNSUPPORTED, "mt_encode_stream: only the 8x (Conv2D) front-end streams");
   if (n_samples < 201 || n_samples > INT32_MAX)
     return fail(MT_ERR_INVALID_ARG, "mt_encode_stream: n_samples %lld out of range [201, %d]",
                 (long long)n_samples, INT32_MAX);
@@ -591,6 +659,11 @@ extern "C" {
 int64_t mt_mel_frames(int64_t n) { return n < 0 ? -1 : n / HOP; }
 
 int64_t mt_encoder_frames(int64_t T) { return T < 0 ? -1 : half_up(half_up(half_up(T))); }
+
+int64_t mt_encoder_frames_for(int32_t frontend, int64_t T) {
+  if (T < 0 || (frontend != MT_FRONTEND_CONV2D_8X && frontend != MT_FRONTEND_CONV1D_2X)) return -1;
+  return frames_of(frontend, T);
+}
 
 int32_t mt_max_window(void) { return MAX_WINDOW; }
 
@@ -698,13 +771,21 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
   const size_t es = half ? 2 : 4;
   int wi = 0;
   auto next = [&]() { return wts[wi++]; };
-  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_w), C * 9, s), "pack conv1");
-  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_b), C, s), "pack conv1 bias");
-  HIP_TRY(launch_pack_conv(next(), P + L.conv2_w, (int)C, bf, s), "pack conv2");
-  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv2_b), C, s), "pack conv2 bias");
-  HIP_TRY(launch_pack_conv(next(), P + L.conv3_w, (int)C, bf, s), "pack conv3");
-  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv3_b), C, s), "pack conv3 bias");
-  HIP_TRY(launch_pack_conv_out(next(), P + L.conv_out_w, (int)D, (int)C, 16, bf, s), "pack conv_out");
+  const bool two_x = c.frontend == MT_FRONTEND_CONV1D_2X;
+  if (two_x) {
+    HIP_TRY(launch_pack_conv1d(next(), P + L.conv1_w, (int)D, c.n_mels, bf, s), "pack conv1");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_b), D, s), "pack conv1 bias");
+    HIP_TRY(launch_pack_conv1d(next(), P + L.conv2_w, (int)D, (int)D, bf, s), "pack conv2");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv2_b), D, s), "pack conv2 bias");
+  } else {
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_w), C * 9, s), "pack conv1");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv1_b), C, s), "pack conv1 bias");
+    HIP_TRY(launch_pack_conv(next(), P + L.conv2_w, (int)C, bf, s), "pack conv2");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv2_b), C, s), "pack conv2 bias");
+    HIP_TRY(launch_pack_conv(next(), P + L.conv3_w, (int)C, bf, s), "pack conv3");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + L.conv3_b), C, s), "pack conv3 bias");
+    HIP_TRY(launch_pack_conv_out(next(), P + L.conv_out_w, (int)D, (int)C, 16, bf, s), "pack conv_out");
+  }
   for (int l = 0; l < c.n_layers; ++l) {
     const auto& Ll = L.layers[l];
     HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.ln1_g), D, s), "pack ln1");
@@ -726,6 +807,7 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.lnp_g), D, s), "pack ln_post");
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.lnp_b), D, s), "pack ln_post");
   const int64_t KD = half ? 2 * D : D;
+  if (!two_x) {
   {
     const float* w = next();
     HIP_TRY(launch_convert(w, P + L.wp1, D, D, KD, 0, bf, s), "pack proj1");
@@ -738,6 +820,7 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
     if (half) HIP_TRY(launch_convert(w, P + L.wp2, O, D, KD, D, bf, s), "pack proj2");
   }
   HIP_TRY(launch_copy_f32(next(), (float*)(P + L.bp2), O, s), "pack proj2 bias");
+  }
   if (A) {
     const float* g = next();
     const float* u = next();
@@ -751,13 +834,13 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
   e->cfg = c;
   e->dt = bf;  // DT_* code
   e->es = es;
-  e->conv1_w = (const float*)(P + L.conv1_w);
+  e->conv1_w = (const float*)(P + L.conv1_w);  // 2x: 16-bit [D][3 n_mels]
   e->conv1_b = (const float*)(P + L.conv1_b);
   e->conv2_w = P + L.conv2_w;
   e->conv2_b = (const float*)(P + L.conv2_b);
-  e->conv3_w = P + L.conv3_w;
-  e->conv3_b = (const float*)(P + L.conv3_b);
-  e->conv_out_w = P + L.conv_out_w;
+  e->conv3_w = two_x ? nullptr : P + L.conv3_w;
+  e->conv3_b = two_x ? nullptr : (const float*)(P + L.conv3_b);
+  e->conv_out_w = two_x ? nullptr : P + L.conv_out_w;
   e->layers.resize(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     const auto& Ll = L.layers[l];
@@ -777,10 +860,10 @@ mt_status mt_encoder_create(const mt_encoder_config* cfg, const float* const* wt
   }
   e->lnp_g = (const float*)(P + L.lnp_g);
   e->lnp_b = (const float*)(P + L.lnp_b);
-  e->wp1 = P + L.wp1;
-  e->bp1 = (const float*)(P + L.bp1);
-  e->wp2 = P + L.wp2;
-  e->bp2 = (const float*)(P + L.bp2);
+  e->wp1 = two_x ? nullptr : P + L.wp1;
+  e->bp1 = two_x ? nullptr : (const float*)(P + L.bp1);
+  e->wp2 = two_x ? nullptr : P + L.wp2;
+  e->bp2 = two_x ? nullptr : (const float*)(P + L.bp2);
   e->wgu = A ? P + L.wgu : nullptr;
   e->wd = A ? P + L.wd : nullptr;
   e->zeros = P + L.zeros;

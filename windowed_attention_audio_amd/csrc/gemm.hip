@@ -67,12 +67,13 @@ template <typename T, int EPI, int MI, int NI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI], const int rbase,
                                           const int cbase) {
   float4 bias[NI];
-  double tau[EPI == EPI_PE ? NI * 4 : 1];
+  constexpr bool PE = EPI == EPI_PE || EPI == EPI_GELU_PE;
+  double tau[PE ? NI * 4 : 1];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int col = cbase + 16 * j;
     bias[j] = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (EPI == EPI_PE) {
+    if constexpr (PE) {
       const int half = a.N / 2;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -89,10 +90,10 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
     if (row >= a.M) continue;
     int64_t orow = row;
     int pos = 0;
-    if constexpr (EPI == EPI_PE || EPI == EPI_OUT) {
-      if (EPI == EPI_PE || a.out_seq_stride > 0) {
+    if constexpr (PE || EPI == EPI_OUT) {
+      if (PE || a.out_seq_stride > 0) {
         const int sq = find_seq(a.cu_rows, a.nseq, row);
-        pos = row - a.cu_rows[sq] + (EPI == EPI_PE ? a.pos_offset : 0);
+        pos = row - a.cu_rows[sq] + (PE ? a.pos_offset : 0);
         if (EPI == EPI_OUT) orow = (int64_t)sq * a.out_seq_stride + pos;
       }
     }
@@ -133,15 +134,18 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
           r.z += v2;
           r.w += v3;
           *R = r;
-        } else if constexpr (EPI == EPI_PE) {
+        } else if constexpr (PE) {
+          // EPI_PE: the bias-free conv_out plus sinusoids; EPI_GELU_PE: the
+          // last convolution's GELU(acc + bias) plus sinusoids
           const int half = a.N / 2;
+          const float v[4] = {v0, v1, v2, v3};
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             double ang = (double)pos * tau[4 * j + e];
             ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
             const float fa = (float)ang;
-            o[e] = acc[i][j][e] + (col + e < half ? sinf(fa) : cosf(fa));
+            o[e] = (EPI == EPI_GELU_PE ? gelu_f(v[e]) : acc[i][j][e]) + (col + e < half ? sinf(fa) : cosf(fa));
           }
           store4((float*)a.C + (int64_t)row * a.ldc + col, o[0], o[1], o[2], o[3]);
         } else if constexpr (EPI == EPI_OUT) {
@@ -970,16 +974,19 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
   const int va = (m0 + r0) * ldab + c * 16;
   const int vb = (n0 + r0) * ldbb + c * 16;
 
-  // Implicit-GEMM convolution (3x3, stride 2, padding 1, channels-last
-  // input [t][f][C]): A row m is output position (t, f) = (m / Fout, m %
-  // Fout) of its sequence and A column k is tap k / C (= 3 df + dt), channel
-  // k % C.  C is a multiple of 8, so each lane's 16-byte chunk lies inside one
-  // tap; lanes of one K slice may straddle two.  One descriptor per
-  // workgroup, based at the first input time row the tile can touch and
-  // ending at the end of the input; a tap outside the sequence or the
-  // frequency range, and k >= K in the last slices, get an offset past the
-  // end and read zeros.
-  int cv_off[CONV ? AI : 1];        // input position (2t, 2f) of the row, bytes from the base
+  // Implicit-GEMM convolution, channels-last input [t][f][C], padding 1.
+  // CONV_2D_S2 (3x3, stride 2): A row m is output position (t, f) = (m /
+  // Fout, m % Fout) of its sequence and A column k is tap k / C (= 3 df +
+  // dt), channel k % C.  CONV_1D_S1 / CONV_1D_S2 (3 taps over time, stride 1
+  // or 2, Fin = Fout = 1): tap k / C is dt and df is the centre.  C is a
+  // multiple of 8, so each lane's 16-byte chunk lies inside one tap; lanes of
+  // one K slice may straddle two.  One descriptor per workgroup, based at the
+  // first input time row the tile can touch and ending at the end of the
+  // input; a tap outside the sequence or the frequency range, and k >= K in
+  // the last slices, get an offset past the end and read zeros.
+  [[maybe_unused]] const bool one_d = a.conv_kind != CONV_2D_S2;
+  [[maybe_unused]] const int tstride = a.conv_kind == CONV_1D_S1 ? 1 : 2;
+  int cv_off[CONV ? AI : 1];        // input position (s t, 2f) of the row, bytes from the base
   uint32_t cv_ok[CONV ? AI : 1];    // bit dt: time tap dt inside; bit 3 + df: frequency tap df inside
   const char* cv_base = nullptr;
   int cv_bytes = 0;
@@ -987,7 +994,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
     const int pos_b = a.conv_C * (int)sizeof(T);  // bytes per input position
     const int tg0 = m0 / a.conv_Fout;
     const int sq0 = find_seq(a.cu_out, a.nseq, tg0);
-    const int t_base = a.cu_in[sq0] + max(2 * (tg0 - a.cu_out[sq0]) - 1, 0);
+    const int t_base = a.cu_in[sq0] + max(tstride * (tg0 - a.cu_out[sq0]) - 1, 0);
     const int64_t row_b = (int64_t)a.conv_Fin * pos_b;
     cv_base = (const char*)a.A + t_base * row_b;
     const int64_t left = ((int64_t)a.cu_in[a.nseq] - t_base) * row_b;
@@ -1001,10 +1008,10 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
         const int tg = m / a.conv_Fout, f2 = m - tg * a.conv_Fout;
         const int sq = find_seq(a.cu_out, a.nseq, tg);
         const int t2 = tg - a.cu_out[sq], Tin = a.cu_in[sq + 1] - a.cu_in[sq];
-        cv_off[i] = (int)((((int64_t)a.cu_in[sq] + 2 * t2 - t_base) * a.conv_Fin + 2 * f2) * pos_b);
+        cv_off[i] = (int)((((int64_t)a.cu_in[sq] + tstride * t2 - t_base) * a.conv_Fin + 2 * f2) * pos_b);
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
-          if (2 * t2 + d - 1 >= 0 && 2 * t2 + d - 1 < Tin) cv_ok[i] |= 1u << d;
+          if (tstride * t2 + d - 1 >= 0 && tstride * t2 + d - 1 < Tin) cv_ok[i] |= 1u << d;
           if (2 * f2 + d - 1 >= 0 && 2 * f2 + d - 1 < a.conv_Fin) cv_ok[i] |= 8u << d;
         }
       }
@@ -1017,7 +1024,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
     if constexpr (CONV) {
       const int k = kb * 32 + c * 8;  // first column of this lane's chunk
       const int tap = k / a.conv_C, ch = k - tap * a.conv_C;
-      const int df = tap / 3, dt = tap - 3 * df;
+      const int df = one_d ? 1 : tap / 3, dt = one_d ? tap : tap - 3 * df;
       cdelta = ((dt - 1) * a.conv_Fin + (df - 1)) * a.conv_C * (int)sizeof(T) + ch * (int)sizeof(T);
       need = k < a.K ? (1u << dt) | (8u << df) : 0xffffffffu;  // past K: never satisfied
     }
@@ -1171,6 +1178,7 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
       if (a.conv_C % 8 == 0 && (int64_t)a.N * a.ldb * 2 < (1ll << 31))
         return run_w8q<T, 160, EPI, 4, true>(a, s);
     }
+    if (CONV && a.conv_kind != CONV_2D_S2) return hipErrorInvalidValue;  // 1-D: that kernel only
     if constexpr (!CONV) {
       // Wide outputs: 256-row tiles where K allows them (whole 128-wide K
       // pairs, operands addressable with 32-bit offsets), 256 or 192 wide by
@@ -1200,6 +1208,7 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
     }
   }
   if constexpr (CONV) {
+    if (a.conv_kind != CONV_2D_S2) return hipErrorInvalidValue;  // 1-D: 16-bit operands only
     // output channels 480 = 3 x 160
     if (a.N % 160 == 0) return run<T, 128, 160, EPI, CONV>(a, s);
     return run<T, 128, 128, EPI, CONV>(a, s);
@@ -1228,17 +1237,21 @@ hipError_t by_epi(const GemmArgs& a, int epi, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStream_t s) {
-  // the convolutions always end in bias + GELU
-  if (conv && epi != EPI_GELU) return hipErrorInvalidValue;
+  // the convolutions always end in bias + GELU (then the sinusoids for the
+  // last 1-D one); no other product takes EPI_GELU_PE
+  if (conv && epi != EPI_GELU && epi != EPI_GELU_PE) return hipErrorInvalidValue;
+  if (!conv && epi == EPI_GELU_PE) return hipErrorInvalidValue;
   if (dtype == DT_BF16) {
-    if (conv) return pick_tile<bf16_t, EPI_GELU, true>(a, s);
+    if (conv) return epi == EPI_GELU ? pick_tile<bf16_t, EPI_GELU, true>(a, s)
+                                     : pick_tile<bf16_t, EPI_GELU_PE, true>(a, s);
     return by_epi<bf16_t, false>(a, epi, s);
   }
   if (dtype == DT_F16) {
-    if (conv) return pick_tile<f16_t, EPI_GELU, true>(a, s);
+    if (conv) return epi == EPI_GELU ? pick_tile<f16_t, EPI_GELU, true>(a, s)
+                                     : pick_tile<f16_t, EPI_GELU_PE, true>(a, s);
     return by_epi<f16_t, false>(a, epi, s);
   }
-  if (conv) return pick_tile<float, EPI_GELU, true>(a, s);
+  if (conv) return epi == EPI_GELU ? pick_tile<float, EPI_GELU, true>(a, s) : hipErrorInvalidValue;
   return by_epi<float, false>(a, epi, s);
 }
 

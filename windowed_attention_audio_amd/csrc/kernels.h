@@ -60,6 +60,14 @@ enum Epi : int {
   EPI_PE = 5,          // C (fp32) = acc + sinusoid(position of row, col)
   EPI_SWIGLU = 6,      // C (T) [row][f] = SiLU(gate) * up (gate/up interleaved by 16)
   EPI_OUT = 7,         // C (fp32) [mapped row][col] = acc (+ bias)
+  EPI_GELU_PE = 8,     // C (fp32) = GELU(acc + bias) + sinusoid(position of row, col)
+};
+
+// Convolution gathers (GemmArgs.conv_kind).
+enum {
+  CONV_2D_S2 = 0,  // 3x3, stride 2 in time and frequency: K index = (3 df + dt) C + channel
+  CONV_1D_S1 = 1,  // 3 taps over time, stride 1 (Fin = Fout = 1): K index = dt C + channel
+  CONV_1D_S2 = 2,  // 3 taps over time, stride 2
 };
 
 struct GemmArgs {
@@ -73,6 +81,7 @@ struct GemmArgs {
   int64_t ldc;
   // implicit-GEMM convolution (A gathered from a channels-last activation)
   int conv_C, conv_Fin, conv_Fout;
+  int conv_kind;          // CONV_*
   const int32_t* cu_in;   // [nseq+1] input time rows prefix
   const int32_t* cu_out;  // [nseq+1] output time rows prefix
   int nseq;
@@ -117,6 +126,10 @@ hipError_t launch_zero_pad_rows(float* out, const int32_t* cu_rows, int nseq, in
                                 int D, hipStream_t s);
 hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int32_t* cu_rows,
                             int nseq, int64_t stride, hipStream_t s);
+// Packed 16-bit rows from fp32 rows: dst[r] = src[row_off[sq] + r - cu[sq]]
+// (r in sequence sq), W values per row, dtype DT_BF16 or DT_F16.
+hipError_t launch_rows_to_half(const float* src, const int64_t* row_off, const int32_t* cu, int nseq,
+                               int64_t rows, int W, void* dst, int dtype, hipStream_t s);
 // Weight repacking (fp32 masters -> kernel layouts); dtype selects the
 // destination element type (DT_*).
 hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
@@ -126,6 +139,8 @@ hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t col
 hipError_t launch_splice(const int64_t* map, int64_t rows, const void* table, int dtype,
                          const float* audio, float* out, int d, hipStream_t s);
 hipError_t launch_pack_conv(const float* w, void* dst, int C, int dtype, hipStream_t s);
+// Conv1d [Co][Ci][3] -> [Co][3 Ci], column dt * Ci + ci.
+hipError_t launch_pack_conv1d(const float* w, void* dst, int Co, int Ci, int dtype, hipStream_t s);
 hipError_t launch_pack_conv_out(const float* w, void* dst, int D, int C, int F, int dtype,
                                 hipStream_t s);
 hipError_t launch_pack_swiglu(const float* gate, const float* up, void* dst, int A, int O, int dtype,

@@ -105,6 +105,30 @@ __global__ void pack_conv_kernel(const float* __restrict__ w, void* dst, int C, 
   }
 }
 
+// Conv1d [Co][Ci][3] -> [Co][3 Ci], column dt * Ci + ci (tap-major, the
+// order of the 1-D convolution gather).
+__global__ void pack_conv1d_kernel(const float* __restrict__ w, void* dst, int Co, int Ci, int dtype) {
+  const int64_t n = 3LL * Co * Ci;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t co = i / (3LL * Ci);
+    const int rem = (int)(i - co * 3LL * Ci);
+    const int dt = rem / Ci, ci = rem - dt * Ci;
+    put(dst, i, w[(co * Ci + ci) * 3 + dt], dtype);
+  }
+}
+
+// One workgroup per packed output row: the fp32 source row of sequence sq at
+// time r - cu[sq], converted to 16 bits (round to nearest even).
+__global__ void rows_to_half_kernel(const float* __restrict__ src, const int64_t* __restrict__ row_off,
+                                    const int32_t* __restrict__ cu, int nseq, int W, void* dst,
+                                    int dtype) {
+  const int64_t r = blockIdx.x;
+  const int sq = find_seq(cu, nseq, (int)r);
+  const float* s = src + (row_off[sq] + (r - cu[sq])) * W;
+  for (int c = threadIdx.x; c < W; c += blockDim.x) put(dst, r * W + c, s[c], dtype);
+}
+
 // conv_out [D][C*F] (column c*F + f) -> [D][F*C] (column f*C + c), matching the
 // channels-last [t][f][c] output of the last convolution.
 __global__ void pack_conv_out_kernel(const float* __restrict__ w, void* dst, int D, int C, int F,
@@ -236,6 +260,21 @@ hipError_t launch_splice(const int64_t* map, int64_t rows, const void* table, in
 
 hipError_t launch_pack_conv(const float* w, void* dst, int C, int dtype, hipStream_t s) {
   hipLaunchKernelGGL(pack_conv_kernel, grid_for(9LL * C * C), dim3(256), 0, s, w, dst, C, dtype);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_conv1d(const float* w, void* dst, int Co, int Ci, int dtype, hipStream_t s) {
+  hipLaunchKernelGGL(pack_conv1d_kernel, grid_for(3LL * Co * Ci), dim3(256), 0, s, w, dst, Co, Ci,
+                     dtype);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_to_half(const float* src, const int64_t* row_off, const int32_t* cu, int nseq,
+                               int64_t rows, int W, void* dst, int dtype, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dtype != DT_BF16 && dtype != DT_F16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_to_half_kernel, dim3((unsigned)rows), dim3(128), 0, s, src, row_off, cu, nseq,
+                     W, dst, dtype);
   return hipGetLastError();
 }
 
