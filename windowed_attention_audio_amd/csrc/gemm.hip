@@ -1202,6 +1202,15 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
         }
         return run_w8<T, 256, EPI>(a, s);
       }
+      // Narrow outputs (N < 2048) with many rows: 256 x 256 tiles once they
+      // fill 1.5 rounds of CUs (N = 1280, M = 24000, fp32 residual epilogue:
+      // K = 5120 360 us against 489 for the four-stage 256 x 128 kernel,
+      // K = 1280 106 against 129; in the encoder step, fc2 15.0 -> 10.6 ms
+      // and o 5.0 -> 4.1).  At M = 6000 the four-stage kernel stays (in
+      // the encoder step 256 x 128 tiles of 128 x 32 wavefronts measured
+      // fc2 3.25 ms against 2.97, although alone they ran 8 % faster).
+      if (w8 && a.M >= 2048 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 384)
+        return run_w8<T, 256, EPI>(a, s);
       if (w8 && a.M >= 2048) return run_w8q<T, 128, EPI, 4>(a, s);
       if (a.M >= 2048) return run_lds<T, 256, 128, 4, 2, 2, EPI, CONV>(a, s);
       return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
