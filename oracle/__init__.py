@@ -14,9 +14,10 @@ Modules
              2x time-downsampling front-end (page "CrisperWhisper -> ONNX
              (with cross-attentions)": whisper geometries)
   prompt   adapter frames spliced into the prompt's token embeddings
+  decoder  the language-model decoder (Qwen3-1.7B geometry) over a KV cache
 
 Every function below is pinned by tests under ``tests/`` that check it against
 closed forms, invariants, brute force, or an independent library routine.
 """
 
-from . import logmel, encoder, encoder2x, prompt  # noqa: F401
+from . import logmel, encoder, encoder2x, prompt, decoder  # noqa: F401

@@ -66,6 +66,12 @@ WHISPER_LARGE_GEOM = dict(
     head_dim=64, d_ffn=5120, d_out=1280, adapter_hidden=0,
 )
 
+# The language-model decoder of the model card (Architecture table, row LLM):
+# Qwen3-1.7B geometry, vocabulary 151 936.
+DEC_GEOM = dict(
+    vocab=151936, d_model=2048, n_layers=28, n_heads=16, n_kv_heads=8, head_dim=128, d_ffn=6144,
+)
+
 WEIGHT_SEED = 1234
 ADAPTER_SEED = 1235
 
@@ -247,3 +253,46 @@ def prompt_tokens(n_audio: int, vocab: int, audio_token: int, seed: int = 77) ->
         return [int(x) + (1 if x >= audio_token else 0) for x in t]
 
     return text(7) + [audio_token] * n_audio + text(9)
+
+
+# --------------------------------------------------------------------------
+# decoder weights
+
+
+def decoder_weight_names(geom: dict) -> list:
+    """Canonical tensor order of the decoder, with shapes (Linear weights
+    [out, in], no biases)."""
+    V, D, F = geom["vocab"], geom["d_model"], geom["d_ffn"]
+    Hq, Hkv, hd = geom["n_heads"], geom["n_kv_heads"], geom["head_dim"]
+    out = [("embed.weight", (V, D))]
+    for l in range(geom["n_layers"]):
+        p = f"layers.{l}."
+        out += [
+            (p + "input_norm.weight", (D,)),
+            (p + "q.weight", (Hq * hd, D)), (p + "k.weight", (Hkv * hd, D)), (p + "v.weight", (Hkv * hd, D)),
+            (p + "q_norm.weight", (hd,)), (p + "k_norm.weight", (hd,)),
+            (p + "o.weight", (D, Hq * hd)),
+            (p + "post_norm.weight", (D,)),
+            (p + "gate.weight", (F, D)), (p + "up.weight", (F, D)), (p + "down.weight", (D, F)),
+        ]
+    out.append(("norm.weight", (D,)))
+    return out
+
+
+def make_decoder_weights(geom: dict, bf16: bool = True, seed: int = 4321) -> dict:
+    """Seeded decoder weights, name -> float32 array: matrices N(0, 0.02^2)
+    (the embedding N(0, 1): its rows are the inputs), norm weights
+    1 + N(0, 0.1^2); bf16-valued when bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, shape in decoder_weight_names(geom):
+        if len(shape) == 1:
+            a = (1.0 + 0.1 * rng.standard_normal(shape)).astype(np.float32)
+        elif name == "embed.weight":
+            a = rng.standard_normal(shape, dtype=np.float32)
+        else:
+            a = rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+        if bf16:
+            a = round_to_bf16(a)
+        out[name] = np.ascontiguousarray(a, dtype=np.float32)
+    return out
