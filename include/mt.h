@@ -274,6 +274,80 @@ mt_status mt_trace_collect(double* total_ms, int32_t* launches);
 const char* mt_status_string(mt_status s);
 const char* mt_last_error(void);
 
+/* ---- language-model decoder (model card "MOSS-Transcribe-preview-2B-GGUF",
+ *      Architecture table, row LLM: Qwen3-1.7B) ---------------------------- */
+
+/* Decoder geometry.  The card's: {151936, 2048, 28, 16, 8, 128, 6144}.  The
+ * kernels require head_dim == 128, n_heads == 2 * n_kv_heads, d_model and
+ * d_ffn multiples of 256, vocab a multiple of 16, dtype MT_BF16 or MT_F16
+ * (weights, matrix operands and the KV cache; fp32 accumulation and residual
+ * stream). */
+typedef struct {
+  int32_t vocab;
+  int32_t d_model;
+  int32_t n_layers;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t d_ffn;
+  int32_t dtype;
+  float rms_eps;   /* RMSNorm epsilon: 1e-6 */
+  float rope_base; /* rotary base: 1e6 */
+} mt_decoder_config;
+
+typedef struct mt_decoder mt_decoder; /* opaque host handle */
+
+/* 1 + 11 * n_layers + 1, or -1 for an invalid configuration. */
+int32_t mt_decoder_n_weights(const mt_decoder_config* cfg);
+mt_status mt_decoder_packed_bytes(const mt_decoder_config* cfg, size_t* bytes);
+
+/* Build a decoder.  `weights`: HOST array of DEVICE pointers to contiguous
+ * fp32 tensors (Linear [out, in], no biases) in this order:
+ *   embed.weight [vocab, D] (also the output head: tied);
+ *   per layer: input_norm.weight [D], q.weight [Hq*128, D], k.weight
+ *     [Hkv*128, D], v.weight [Hkv*128, D], q_norm.weight [128],
+ *     k_norm.weight [128], o.weight [D, Hq*128], post_norm.weight [D],
+ *     gate.weight [F, D], up.weight [F, D], down.weight [D, F];
+ *   norm.weight [D].
+ * `packed` (device, >= mt_decoder_packed_bytes, 256-byte aligned) receives
+ * the kernel layouts and must outlive the handle. */
+mt_status mt_decoder_create(const mt_decoder_config* cfg, const float* const* weights, int32_t n_weights,
+                            void* packed, size_t packed_bytes, void* stream, mt_decoder** out);
+void mt_decoder_destroy(mt_decoder* dec);
+
+/* The packed embedding table (device, [vocab][d_model] of the decoder's
+ * dtype): the table mt_prompt_embed reads token rows from. */
+const void* mt_decoder_embedding(const mt_decoder* dec);
+
+/* Bytes of a KV cache for max_seqs sequences of up to max_pos positions:
+ * [n_layers][max_seqs][2 (K, V)][n_kv_heads][max_pos][128] of the dtype.
+ * The caller allocates it; K entries are stored after K-norm and rotation. */
+mt_status mt_decoder_cache_bytes(const mt_decoder* dec, int32_t max_seqs, int32_t max_pos, size_t* bytes);
+
+/* Workspace bytes for mt_decode with these rows (HOST seq / pos arrays). */
+mt_status mt_decode_workspace_size(const mt_decoder* dec, int32_t n_rows, const int32_t* seq, const int32_t* pos,
+                                   int32_t max_seqs, int32_t max_pos, size_t* bytes);
+
+/* One forward step of the decoder over n_rows new rows.
+ *   x       device fp32 [n_rows, d_model]: the rows' input embeddings (token
+ *           rows of the table, or adapter frames; see mt_prompt_embed).
+ *   seq     HOST int32 [n_rows]: cache slot (0 .. max_seqs-1) of each row.
+ *   pos     HOST int32 [n_rows]: each row's position (0 .. max_pos-1);
+ *           (seq, pos) pairs distinct.  A row attends to positions 0 .. pos
+ *           of its slot: positions below pos must hold K/V written by an
+ *           earlier call or by another row of this one (rows of one call
+ *           write their K/V before any row attends).  A prompt is one call
+ *           with positions 0 .. S-1; a decode step one row per sequence.
+ *   cache   device KV cache of mt_decoder_cache_bytes(max_seqs, max_pos).
+ *   logits  device fp32 [n_rows, vocab] (tied head on the final RMSNorm).
+ *   next    device int32 [n_rows] or NULL: the first index of each row's
+ *           largest logit.
+ * Up to 16 rows run the skinny matrix-vector kernels (the weights stream
+ * once); more rows run the tiled products. */
+mt_status mt_decode(const mt_decoder* dec, const float* x, int32_t n_rows, const int32_t* seq, const int32_t* pos,
+                    void* cache, int32_t max_seqs, int32_t max_pos, float* logits, int32_t* next, void* ws,
+                    size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,182 @@
+"""GPU parity of the language-model decoder step against the oracle
+(oracle.decoder), through the C ABI.
+
+  * a small geometry (d 256, 4/2 heads of 128, FFN 512, vocab 1024, 2 layers),
+    fp16 and bf16: a 37-row prompt in one call (tiled products), then single
+    rows (skinny matrix-vector kernels) continuing it; a 9-row prompt on the
+    skinny path; three sequences of different lengths in one call, then one
+    decode step with a row each; a 600-row prompt and decode steps past it
+    (attention over three 256-key chunks);
+  * the card's full width (d 2048, 16/8 heads, FFN 6144, vocab 151 936) with
+    two layers: prompt + decode steps against the oracle;
+  * the card's 28 layers: a 16-row decode step equals each row alone
+    (bitwise), and argmax equals the host's argmax of the returned logits.
+Logits are compared row by row: cosine >= 0.999 and max |diff| <= 0.02 RMS.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import decoder as OD
+from tests.helpers import assert_bf16_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL = dict(vocab=1024, d_model=256, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=128, d_ffn=512)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+class GpuDecoder:
+    def __init__(self, geom, weights, dt_name, max_seqs, max_pos):
+        import torch
+        import windowed_attention_audio_amd as W
+        self.W = W
+        self.geom = geom
+        dt = W.MT_F16 if dt_name == "f16" else W.MT_BF16
+        self.cfg = W.decoder_config(geom, dt)
+        dev = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in weights.values()]
+        self.dec = W.mt_decoder_create(self.cfg, dev)
+        torch.cuda.synchronize()
+        del dev
+        self.max_seqs, self.max_pos = max_seqs, max_pos
+        self.cache = torch.zeros(W.mt_decoder_cache_bytes(self.dec, max_seqs, max_pos), dtype=torch.uint8,
+                                 device="cuda")
+
+    def step(self, x, seq, pos):
+        import torch
+        xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+        logits, nxt = self.W.mt_decode(self.dec, xt, seq, pos, self.cache, self.max_seqs, self.max_pos)
+        torch.cuda.synchronize()
+        return logits.cpu().numpy(), nxt.cpu().numpy()
+
+
+def check_logits(gpu, ref, nxt, what):
+    r = assert_bf16_rows(gpu, ref, what=what)
+    assert np.array_equal(nxt, np.argmax(gpu, axis=1)), f"{what}: argmax differs from the returned logits"
+    return r
+
+
+@pytest.fixture(scope="module")
+def small_w():
+    return synth.make_decoder_weights(SMALL, bf16=True, seed=31)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_small_prompt_then_decode(small_w, dt):
+    P = {k: v.astype(np.float64) for k, v in small_w.items()}
+    toks = np.random.default_rng(1).integers(0, SMALL["vocab"], 42)
+    x = OD.embed(toks, P)
+    g = GpuDecoder(SMALL, small_w, dt, 2, 64)
+    cache = OD.empty_cache(SMALL)
+    say(f"decoder small {dt}: 37-row prompt (tiled path)")
+    gl, nx = g.step(x[:37], [1] * 37, list(range(37)))
+    check_logits(gl, OD.forward(x[:37], P, SMALL, cache), nx, "prompt")
+    for i in range(37, 42):
+        gl, nx = g.step(x[i:i + 1], [1], [i])
+        r = check_logits(gl, OD.forward(x[i:i + 1], P, SMALL, cache), nx, f"decode pos {i}")
+    say(f"  last step: cos {r['cos'].min():.6f} worst {r['maxabs_rms'].max():.4f}")
+
+
+def test_small_short_prompt_on_skinny_path(small_w):
+    P = {k: v.astype(np.float64) for k, v in small_w.items()}
+    toks = np.random.default_rng(2).integers(0, SMALL["vocab"], 9)
+    x = OD.embed(toks, P)
+    g = GpuDecoder(SMALL, small_w, "f16", 1, 32)
+    say("decoder small: 9-row prompt (skinny path)")
+    gl, nx = g.step(x, [0] * 9, list(range(9)))
+    check_logits(gl, OD.forward(x, P, SMALL, OD.empty_cache(SMALL)), nx, "9-row prompt")
+
+
+def test_small_three_sequences(small_w):
+    P = {k: v.astype(np.float64) for k, v in small_w.items()}
+    lens = [10, 20, 5]
+    rng = np.random.default_rng(3)
+    xs = [OD.embed(rng.integers(0, SMALL["vocab"], n + 1), P) for n in lens]
+    g = GpuDecoder(SMALL, small_w, "bf16", 4, 64)
+    slots = [3, 0, 2]
+    x = np.concatenate([xi[:n] for xi, n in zip(xs, lens)])
+    seq = sum(([s] * n for s, n in zip(slots, lens)), [])
+    pos = sum((list(range(n)) for n in lens), [])
+    say("decoder small: 3 prompts in one call, then one step each")
+    gl, nx = g.step(x, seq, pos)
+    caches = [OD.empty_cache(SMALL) for _ in lens]
+    ref = np.concatenate([OD.forward(xi[:n], P, SMALL, c) for xi, n, c in zip(xs, lens, caches)])
+    check_logits(gl, ref, nx, "3 prompts")
+    gl, nx = g.step(np.stack([xi[n] for xi, n in zip(xs, lens)]), slots, lens)
+    ref = np.concatenate([OD.forward(xi[n:n + 1], P, SMALL, c) for xi, n, c in zip(xs, lens, caches)])
+    check_logits(gl, ref, nx, "3 decode rows")
+
+
+def test_small_long_context(small_w):
+    P = {k: v.astype(np.float64) for k, v in small_w.items()}
+    toks = np.random.default_rng(4).integers(0, SMALL["vocab"], 603)
+    x = OD.embed(toks, P)
+    g = GpuDecoder(SMALL, small_w, "f16", 1, 1024)
+    cache = OD.empty_cache(SMALL)
+    say("decoder small: 600-row prompt, 3 decode steps (3 key chunks)")
+    gl, nx = g.step(x[:600], [0] * 600, list(range(600)))
+    ref = OD.forward(x[:600], P, SMALL, cache)
+    check_logits(gl[::37], ref[::37], nx[::37], "600-row prompt (sampled rows)")
+    for i in range(600, 603):
+        gl, nx = g.step(x[i:i + 1], [0], [i])
+        check_logits(gl, OD.forward(x[i:i + 1], P, SMALL, cache), nx, f"decode pos {i}")
+
+
+def test_full_width_two_layers():
+    geom = dict(synth.DEC_GEOM, n_layers=2)
+    say("decoder full width, 2 layers: weights")
+    w = synth.make_decoder_weights(geom, bf16=True, seed=5)
+    P = {k: v.astype(np.float64) for k, v in w.items()}
+    toks = np.random.default_rng(5).integers(0, geom["vocab"], 22)
+    x = OD.embed(toks, P)
+    g = GpuDecoder(geom, w, "f16", 1, 64)
+    cache = OD.empty_cache(geom)
+    say("  20-row prompt, 2 decode steps")
+    gl, nx = g.step(x[:20], [0] * 20, list(range(20)))
+    check_logits(gl, OD.forward(x[:20], P, geom, cache), nx, "full-width prompt")
+    for i in (20, 21):
+        gl, nx = g.step(x[i:i + 1], [0], [i])
+        r = check_logits(gl, OD.forward(x[i:i + 1], P, geom, cache), nx, f"full-width decode {i}")
+    say(f"  cos {r['cos'].min():.6f} worst {r['maxabs_rms'].max():.4f}")
+
+
+def test_full_geometry_batch_equals_single():
+    import torch
+    geom = synth.DEC_GEOM
+    say("decoder 28 layers: weights")
+    w = synth.make_decoder_weights(geom, bf16=True, seed=6)
+    g = GpuDecoder(geom, w, "bf16", 16, 128)
+    emb = w["embed.weight"]
+    rng = np.random.default_rng(6)
+    # 16 sequences with prompts of 3..18 rows in one call, then a 16-row step
+    lens = [3 + i for i in range(16)]
+    x = np.concatenate([emb[rng.integers(0, geom["vocab"], n)] for n in lens])
+    seq = sum(([s] * n for s, n in enumerate(lens)), [])
+    pos = sum((list(range(n)) for n in lens), [])
+    say("  16 prompts in one call")
+    g.step(x, seq, pos)
+    snap = g.cache.clone()
+    step_x = emb[rng.integers(0, geom["vocab"], 16)]
+    say("  16-row decode step vs each row alone")
+    gl, nx = g.step(step_x, list(range(16)), lens)
+    assert np.isfinite(gl).all()
+    for s in (0, 7, 15):
+        g.cache.copy_(snap)
+        l1, n1 = g.step(step_x[s:s + 1], [s], [lens[s]])
+        assert np.array_equal(l1[0], gl[s]), f"row {s}"
+        assert n1[0] == nx[s]
+    torch.cuda.synchronize()

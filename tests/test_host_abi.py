@@ -229,3 +229,32 @@ def test_packed_bytes_2x(L):
     b16 = W.mt_encoder_packed_bytes(W.encoder_config(geom, W.MT_BF16))
     expect = 2 * n_mat + 4 * n_vec
     assert expect <= b16 <= expect + 256 * (len(names) + 1)
+
+
+def test_decoder_config_validation(L):
+    cfg = W.decoder_config(synth.DEC_GEOM, W.MT_BF16)
+    assert W.mt_decoder_n_weights(cfg) == 1 + 11 * 28 + 1 == len(synth.decoder_weight_names(synth.DEC_GEOM))
+    names = synth.decoder_weight_names(synth.DEC_GEOM)
+    n_mat = sum(int(np.prod(s)) for _, s in names if len(s) > 1)
+    n_vec = sum(int(np.prod(s)) for _, s in names if len(s) == 1)
+    b = W.mt_decoder_packed_bytes(cfg)
+    assert 2 * n_mat + 4 * n_vec <= b <= 2 * n_mat + 4 * n_vec + 256 * (len(names) + 1)
+    for over, dt, status in ((dict(), W.MT_F32, W.MT_ERR_UNSUPPORTED),
+                             (dict(head_dim=64), W.MT_BF16, W.MT_ERR_UNSUPPORTED),
+                             (dict(n_kv_heads=4), W.MT_BF16, W.MT_ERR_UNSUPPORTED),
+                             (dict(d_model=1000), W.MT_BF16, W.MT_ERR_UNSUPPORTED),
+                             (dict(d_ffn=0), W.MT_BF16, W.MT_ERR_INVALID_ARG)):
+        c = W.decoder_config(dict(synth.DEC_GEOM, **over), dt)
+        with pytest.raises(W.MtError) as e:
+            W.mt_decoder_packed_bytes(c)
+        assert e.value.status == status, over
+    assert W.mt_decoder_n_weights(W.decoder_config(synth.DEC_GEOM, W.MT_F32)) == -1
+
+
+def test_decode_rejects_null_decoder(L):
+    n = ctypes.c_size_t()
+    seq = (ctypes.c_int32 * 1)(0)
+    pos = (ctypes.c_int32 * 1)(0)
+    assert L.mt_decode_workspace_size(None, 1, seq, pos, 1, 8, ctypes.byref(n)) == W.MT_ERR_INVALID_ARG
+    assert L.mt_decode(None, None, 1, seq, pos, None, 1, 8, None, None, None, 0, None) == W.MT_ERR_INVALID_ARG
+    assert L.mt_decoder_embedding(None) is None

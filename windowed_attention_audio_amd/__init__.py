@@ -36,6 +36,8 @@ EXPORTS = (
     "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
     "mt_encode_stream_workspace_size", "mt_encode_stream",
     "mt_prompt_embed_workspace_size", "mt_prompt_embed",
+    "mt_decoder_n_weights", "mt_decoder_packed_bytes", "mt_decoder_create", "mt_decoder_destroy",
+    "mt_decoder_embedding", "mt_decoder_cache_bytes", "mt_decode_workspace_size", "mt_decode",
     "mt_status_string", "mt_last_error", "mt_trace_arm", "mt_trace_collect",
 )
 
@@ -59,6 +61,13 @@ class EncoderConfig(ctypes.Structure):
                 ("adapter_hidden", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("with_head", ctypes.c_int32), ("ln_eps", ctypes.c_float),
                 ("frontend", ctypes.c_int32)]
+
+
+class DecoderConfig(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_ffn", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_base", ctypes.c_float)]
 
 
 _lib = None
@@ -100,6 +109,21 @@ def lib():
         L.mt_prompt_embed.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, ctypes.c_int32,
                                       vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp,
                                       ctypes.c_int64, vp, vp, c_sz, vp]
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        dcp = ctypes.POINTER(DecoderConfig)
+        L.mt_decoder_n_weights.argtypes = [dcp]
+        L.mt_decoder_packed_bytes.argtypes = [dcp, ctypes.POINTER(c_sz)]
+        L.mt_decoder_create.argtypes = [dcp, ctypes.POINTER(vp), ctypes.c_int32, vp, c_sz, vp,
+                                        ctypes.POINTER(vp)]
+        L.mt_decoder_destroy.argtypes = [vp]
+        L.mt_decoder_destroy.restype = None
+        L.mt_decoder_embedding.argtypes = [vp]
+        L.mt_decoder_embedding.restype = vp
+        L.mt_decoder_cache_bytes.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(c_sz)]
+        L.mt_decode_workspace_size.argtypes = [vp, ctypes.c_int32, i32p, i32p, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.POINTER(c_sz)]
+        L.mt_decode.argtypes = [vp, vp, ctypes.c_int32, i32p, i32p, vp, ctypes.c_int32, ctypes.c_int32,
+                                vp, vp, vp, c_sz, vp]
         L.mt_trace_arm.argtypes = [ctypes.c_char_p, ctypes.c_int32]
         L.mt_trace_arm.restype = ctypes.c_int
         L.mt_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -111,7 +135,9 @@ def lib():
         for name in ("mt_logmel_workspace_size", "mt_logmel", "mt_encoder_packed_bytes",
                      "mt_encoder_create", "mt_encode_workspace_size", "mt_encode",
                      "mt_encode_stream_workspace_size", "mt_encode_stream",
-                     "mt_prompt_embed_workspace_size", "mt_prompt_embed"):
+                     "mt_prompt_embed_workspace_size", "mt_prompt_embed",
+                     "mt_decoder_packed_bytes", "mt_decoder_create", "mt_decoder_cache_bytes",
+                     "mt_decode_workspace_size", "mt_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -326,6 +352,107 @@ def mt_prompt_embed(tokens, table, audio, audio_token, out=None, ws=None, stream
                                  ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                  ws.numel(), _stream_ptr(stream)))
     return out
+
+
+# ------------------------------------------------------------------ decoder
+
+
+def decoder_config(geom: dict, dtype: int, rms_eps: float = 1e-6, rope_base: float = 1e6):
+    return DecoderConfig(geom["vocab"], geom["d_model"], geom["n_layers"], geom["n_heads"],
+                         geom["n_kv_heads"], geom["head_dim"], geom["d_ffn"], dtype, rms_eps, rope_base)
+
+
+class Decoder:
+    """A decoder whose packed weights live in a torch-owned device buffer."""
+
+    def __init__(self, handle, cfg, packed):
+        self.handle = handle
+        self.cfg = cfg
+        self.packed = packed
+
+    def close(self):
+        if self.handle:
+            lib().mt_decoder_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mt_decoder_n_weights(cfg: DecoderConfig) -> int:
+    return lib().mt_decoder_n_weights(ctypes.byref(cfg))
+
+
+def mt_decoder_packed_bytes(cfg: DecoderConfig) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_decoder_packed_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def mt_decoder_create(cfg: DecoderConfig, weights, device="cuda", stream=None) -> Decoder:
+    """weights: fp32 CUDA tensors in the canonical order of include/mt.h."""
+    import torch
+    for w in weights:
+        assert w.is_cuda and w.dtype == torch.float32 and w.is_contiguous()
+    nbytes = mt_decoder_packed_bytes(cfg)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ptrs = (ctypes.c_void_p * len(weights))(*[w.data_ptr() for w in weights])
+    h = ctypes.c_void_p()
+    _check(lib().mt_decoder_create(ctypes.byref(cfg), ptrs, len(weights), ctypes.c_void_p(packed.data_ptr()),
+                                   nbytes, _stream_ptr(stream), ctypes.byref(h)))
+    return Decoder(h, cfg, packed)
+
+
+def mt_decoder_embedding(dec: Decoder):
+    """The packed [vocab, d_model] table as a torch view (bfloat16 / float16)."""
+    import torch
+    dt = torch.bfloat16 if dec.cfg.dtype == MT_BF16 else torch.float16
+    ptr = lib().mt_decoder_embedding(dec.handle)
+    off = ptr - dec.packed.data_ptr()
+    n = dec.cfg.vocab * dec.cfg.d_model * 2
+    return dec.packed[off:off + n].view(dt).view(dec.cfg.vocab, dec.cfg.d_model)
+
+
+def mt_decoder_cache_bytes(dec: Decoder, max_seqs: int, max_pos: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_decoder_cache_bytes(dec.handle, int(max_seqs), int(max_pos), ctypes.byref(n)))
+    return n.value
+
+
+def _i32(a):
+    return (ctypes.c_int32 * len(a))(*[int(v) for v in a])
+
+
+def mt_decode_workspace_size(dec: Decoder, seq, pos, max_seqs, max_pos) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_decode_workspace_size(dec.handle, len(seq), _i32(seq), _i32(pos), int(max_seqs),
+                                          int(max_pos), ctypes.byref(n)))
+    return n.value
+
+
+def mt_decode(dec: Decoder, x, seq, pos, cache, max_seqs, max_pos, logits=None, next_ids=None, ws=None,
+              stream=None):
+    """x: fp32 CUDA tensor [n, d_model]; seq, pos: host int sequences [n];
+    cache: CUDA byte tensor of mt_decoder_cache_bytes.  Returns (logits fp32
+    [n, vocab], next int32 [n])."""
+    import torch
+    n = len(seq)
+    assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.shape[0] == n
+    if logits is None:
+        logits = torch.empty((n, dec.cfg.vocab), dtype=torch.float32, device=x.device)
+    if next_ids is None:
+        next_ids = torch.empty(n, dtype=torch.int32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(mt_decode_workspace_size(dec, seq, pos, max_seqs, max_pos), 1), dtype=torch.uint8,
+                         device=x.device)
+    _check(lib().mt_decode(dec.handle, ctypes.c_void_p(x.data_ptr()), n, _i32(seq), _i32(pos),
+                           ctypes.c_void_p(cache.data_ptr()), int(max_seqs), int(max_pos),
+                           ctypes.c_void_p(logits.data_ptr()), ctypes.c_void_p(next_ids.data_ptr()),
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
+    return logits, next_ids
 
 
 def mt_trace_arm(stage, max_launches=4096):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmt.so")
 
-SOURCES = ["api.cpp", "mel.hip", "conv1.hip", "gemm.hip", "norm.hip", "attn.hip", "misc.hip"]
+SOURCES = ["api.cpp", "mel.hip", "conv1.hip", "gemm.hip", "norm.hip", "attn.hip", "misc.hip", "decoder.hip"]
 ARCH = "gfx950"
 
 

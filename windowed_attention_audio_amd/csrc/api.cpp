@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -654,7 +655,344 @@ mt_status stream_mel(const float* wav, int64_t n, int64_t m0, int64_t nf, float*
 
 }  // namespace
 
+// ================================================================== decoder
+namespace {
+
+struct DecLayer {
+  const float *in_norm, *q_norm, *k_norm, *post_norm;
+  const void *wqkv, *wo, *wgu, *wd;
+};
+
+struct DecLayout {
+  size_t embed, norm, zeros, bytes;
+  struct L {
+    size_t in_norm, wqkv, q_norm, k_norm, wo, post_norm, wgu, wd;
+  };
+  std::vector<L> layers;
+};
+
+mt_status check_decoder_config(const mt_decoder_config* c) {
+  if (!c) return fail(MT_ERR_INVALID_ARG, "decoder config is NULL");
+  if (c->dtype != MT_BF16 && c->dtype != MT_F16)
+    return fail(MT_ERR_UNSUPPORTED, "decoder dtype must be MT_BF16 or MT_F16 (got %d)", c->dtype);
+  if (c->vocab < 1 || c->d_model < 1 || c->n_layers < 0 || c->n_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 1 || c->d_ffn < 1)
+    return fail(MT_ERR_INVALID_ARG, "non-positive size in decoder config");
+  if (!(c->rms_eps > 0.f) || !(c->rope_base > 1.f))
+    return fail(MT_ERR_INVALID_ARG, "rms_eps must be > 0 and rope_base > 1");
+  if (c->head_dim != 128) return fail(MT_ERR_UNSUPPORTED, "decoder head_dim must be 128");
+  if (c->n_heads != 2 * c->n_kv_heads)
+    return fail(MT_ERR_UNSUPPORTED, "decoder needs two query heads per key/value head");
+  if (c->d_model % 256 || c->d_ffn % 256 || c->vocab % 16)
+    return fail(MT_ERR_UNSUPPORTED, "decoder d_model and d_ffn must be multiples of 256, vocab of 16");
+  return MT_OK;
+}
+
+DecLayout decoder_layout(const mt_decoder_config& c) {
+  const size_t V = c.vocab, D = c.d_model, F = c.d_ffn, hd = c.head_dim;
+  const size_t NQKV = (size_t)(c.n_heads + 2 * c.n_kv_heads) * hd, NQ = (size_t)c.n_heads * hd;
+  DecLayout p;
+  Carver k;
+  p.embed = k.take(V * D * 2);
+  p.layers.resize(c.n_layers);
+  for (auto& L : p.layers) {
+    L.in_norm = k.take(D * 4);
+    L.wqkv = k.take(NQKV * D * 2);
+    L.q_norm = k.take(hd * 4);
+    L.k_norm = k.take(hd * 4);
+    L.wo = k.take(D * NQ * 2);
+    L.post_norm = k.take(D * 4);
+    L.wgu = k.take(2 * F * D * 2);
+    L.wd = k.take(D * F * 2);
+  }
+  p.norm = k.take(D * 4);
+  p.zeros = k.take(256);
+  p.bytes = k.off;
+  return p;
+}
+
+// K splits of the skinny product: enough wavefronts in flight (~2048) for
+// the weight stream, whole 32-wide K steps per split
+int gemv_split(int N, int K) {
+  int s = 1;
+  while (s < 8 && (N / 16) * s < 2048 && K % (64 * s) == 0) s *= 2;
+  return s;
+}
+
+struct DecPlan {
+  int n = 0, n_items = 0, s_qkv = 1, s_o = 1, s_d = 1;
+  bool gemv = true;
+  std::vector<int32_t> words;  // seq | pos | items | first_item
+  size_t o_words, o_x, o_h, o_qkv, o_qf, o_po, o_pml, o_o16, o_opart, o_act, o_dpart, bytes;
+};
+
+}  // namespace
+
+struct mt_decoder {
+  mt_decoder_config cfg;
+  int dt;
+  const void* embed;
+  const float* norm;
+  std::vector<DecLayer> layers;
+  const void* zeros;
+};
+
+namespace {
+
+mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, const int32_t* pos, int32_t max_seqs,
+                      int32_t max_pos, DecPlan& p) {
+  if (!dec) return fail(MT_ERR_INVALID_ARG, "decoder is NULL");
+  if (n < 1 || n > (1 << 20)) return fail(MT_ERR_INVALID_ARG, "mt_decode: n_rows %d out of range [1, 2^20]", n);
+  if (!seq || !pos) return fail(MT_ERR_INVALID_ARG, "mt_decode: seq or pos is NULL");
+  if (max_seqs < 1 || max_pos < 1)
+    return fail(MT_ERR_INVALID_ARG, "mt_decode: max_seqs and max_pos must be >= 1");
+  const mt_decoder_config& c = dec->cfg;
+  std::vector<int64_t> keys(n);
+  p.n = n;
+  p.words.assign(2 * (size_t)n, 0);
+  std::vector<int32_t> items, first(n + 1, 0);
+  for (int i = 0; i < n; ++i) {
+    if (seq[i] < 0 || seq[i] >= max_seqs)
+      return fail(MT_ERR_INVALID_ARG, "mt_decode: seq[%d] = %d outside [0, %d)", i, seq[i], max_seqs);
+    if (pos[i] < 0 || pos[i] >= max_pos)
+      return fail(MT_ERR_INVALID_ARG, "mt_decode: pos[%d] = %d outside [0, %d)", i, pos[i], max_pos);
+    keys[i] = (int64_t)seq[i] * max_pos + pos[i];
+    p.words[i] = seq[i];
+    p.words[n + i] = pos[i];
+    first[i] = (int32_t)(items.size() / 2);
+    for (int ch = 0; ch * 256 <= pos[i]; ++ch) {
+      items.push_back(i);
+      items.push_back(ch);
+    }
+  }
+  first[n] = (int32_t)(items.size() / 2);
+  std::sort(keys.begin(), keys.end());
+  for (int i = 1; i < n; ++i)
+    if (keys[i] == keys[i - 1]) return fail(MT_ERR_INVALID_ARG, "mt_decode: two rows at the same (seq, pos)");
+  p.n_items = first[n];
+  p.words.insert(p.words.end(), items.begin(), items.end());
+  p.words.insert(p.words.end(), first.begin(), first.end());
+  const size_t D = c.d_model, F = c.d_ffn, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  const size_t NQKV = (Hq + 2 * Hkv) * hd, NQ = Hq * hd;
+  p.gemv = n <= 16;
+  if (p.gemv) {
+    p.s_qkv = gemv_split((int)NQKV, (int)D);
+    p.s_o = gemv_split((int)D, (int)NQ);
+    p.s_d = gemv_split((int)D, (int)F);
+  } else {
+    p.s_qkv = 1;
+    p.s_o = p.s_d = 0;  // the matrix kernels add into the residual stream
+  }
+  Carver k;
+  p.o_words = k.take(4 * p.words.size());
+  p.o_x = k.take((size_t)n * D * 4);
+  p.o_h = k.take((size_t)n * std::max(D, NQ) * 2);
+  p.o_qkv = k.take((size_t)p.s_qkv * n * NQKV * 4);
+  p.o_qf = k.take((size_t)n * NQ * 4);
+  p.o_po = k.take((size_t)p.n_items * Hkv * 2 * hd * 4);
+  p.o_pml = k.take((size_t)p.n_items * Hkv * 2 * 2 * 4);
+  p.o_o16 = k.take((size_t)n * NQ * 2);
+  p.o_opart = k.take((size_t)p.s_o * n * D * 4);
+  p.o_act = k.take((size_t)n * F * 2);
+  p.o_dpart = k.take((size_t)p.s_d * n * D * 4);
+  p.bytes = k.off;
+  return MT_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+int32_t mt_decoder_n_weights(const mt_decoder_config* cfg) {
+  if (check_decoder_config(cfg) != MT_OK) return -1;
+  return 1 + 11 * cfg->n_layers + 1;
+}
+
+mt_status mt_decoder_packed_bytes(const mt_decoder_config* cfg, size_t* bytes) {
+  mt_status st = check_decoder_config(cfg);
+  if (st != MT_OK) return st;
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = decoder_layout(*cfg).bytes;
+  return MT_OK;
+}
+
+mt_status mt_decoder_create(const mt_decoder_config* cfg, const float* const* wts, int32_t n_weights, void* packed,
+                            size_t packed_bytes, void* stream, mt_decoder** out) {
+  mt_status st = check_decoder_config(cfg);
+  if (st != MT_OK) return st;
+  if (!out) return fail(MT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const mt_decoder_config c = *cfg;
+  const int nw = 1 + 11 * c.n_layers + 1;
+  if (!wts) return fail(MT_ERR_INVALID_ARG, "weights is NULL");
+  if (n_weights != nw) return fail(MT_ERR_INVALID_ARG, "expected %d weight tensors, got %d", nw, n_weights);
+  for (int i = 0; i < n_weights; ++i)
+    if (!wts[i]) return fail(MT_ERR_INVALID_ARG, "weights[%d] is NULL", i);
+  const DecLayout L = decoder_layout(c);
+  if (!packed) return fail(MT_ERR_INVALID_ARG, "packed is NULL");
+  if ((uintptr_t)packed % ALIGN) return fail(MT_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+  if (packed_bytes < L.bytes)
+    return fail(MT_ERR_WORKSPACE, "packed buffer %zu bytes < required %zu", packed_bytes, L.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = c.dtype == MT_BF16 ? DT_BF16 : DT_F16;
+  char* P = (char*)packed;
+  const int64_t V = c.vocab, D = c.d_model, F = c.d_ffn, hd = c.head_dim;
+  const int64_t NQ = (int64_t)c.n_heads * hd, NKV = (int64_t)c.n_kv_heads * hd;
+  int wi = 0;
+  auto next = [&]() { return wts[wi++]; };
+  HIP_TRY(launch_convert(next(), P + L.embed, V, D, D, 0, dt, s), "pack embed");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& Ll = L.layers[l];
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.in_norm), D, s), "pack input_norm");
+    HIP_TRY(launch_convert(next(), P + Ll.wqkv, NQ, D, D, 0, dt, s), "pack q");  // rows 0 .. NQ-1
+    HIP_TRY(launch_convert(next(), P + Ll.wqkv + (size_t)NQ * D * 2, NKV, D, D, 0, dt, s), "pack k");
+    HIP_TRY(launch_convert(next(), P + Ll.wqkv + (size_t)(NQ + NKV) * D * 2, NKV, D, D, 0, dt, s), "pack v");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.q_norm), hd, s), "pack q_norm");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.k_norm), hd, s), "pack k_norm");
+    HIP_TRY(launch_convert(next(), P + Ll.wo, D, NQ, NQ, 0, dt, s), "pack o");
+    HIP_TRY(launch_copy_f32(next(), (float*)(P + Ll.post_norm), D, s), "pack post_norm");
+    const float* g = next();
+    const float* u = next();
+    HIP_TRY(launch_pack_swiglu(g, u, P + Ll.wgu, (int)F, (int)D, dt, s), "pack gate/up");
+    HIP_TRY(launch_convert(next(), P + Ll.wd, D, F, F, 0, dt, s), "pack down");
+  }
+  HIP_TRY(launch_copy_f32(next(), (float*)(P + L.norm), D, s), "pack norm");
+  HIP_TRY(launch_fill_i32((int*)(P + L.zeros), 0, 64, s), "zero block");
+  mt_decoder* d = new mt_decoder();
+  d->cfg = c;
+  d->dt = dt;
+  d->embed = P + L.embed;
+  d->norm = (const float*)(P + L.norm);
+  d->zeros = P + L.zeros;
+  d->layers.resize(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& Ll = L.layers[l];
+    DecLayer& y = d->layers[l];
+    y.in_norm = (const float*)(P + Ll.in_norm);
+    y.q_norm = (const float*)(P + Ll.q_norm);
+    y.k_norm = (const float*)(P + Ll.k_norm);
+    y.post_norm = (const float*)(P + Ll.post_norm);
+    y.wqkv = P + Ll.wqkv;
+    y.wo = P + Ll.wo;
+    y.wgu = P + Ll.wgu;
+    y.wd = P + Ll.wd;
+  }
+  *out = d;
+  return MT_OK;
+}
+
+void mt_decoder_destroy(mt_decoder* dec) { delete dec; }
+
+const void* mt_decoder_embedding(const mt_decoder* dec) { return dec ? dec->embed : nullptr; }
+
+mt_status mt_decoder_cache_bytes(const mt_decoder* dec, int32_t max_seqs, int32_t max_pos, size_t* bytes) {
+  if (!dec || !bytes) return fail(MT_ERR_INVALID_ARG, "decoder or bytes is NULL");
+  if (max_seqs < 1 || max_pos < 1) return fail(MT_ERR_INVALID_ARG, "max_seqs and max_pos must be >= 1");
+  const mt_decoder_config& c = dec->cfg;
+  *bytes = (size_t)c.n_layers * max_seqs * 2 * c.n_kv_heads * (size_t)max_pos * c.head_dim * 2;
+  return MT_OK;
+}
+
+mt_status mt_decode_workspace_size(const mt_decoder* dec, int32_t n_rows, const int32_t* seq, const int32_t* pos,
+                                   int32_t max_seqs, int32_t max_pos, size_t* bytes) {
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  DecPlan p;
+  mt_status st = plan_decode(dec, n_rows, seq, pos, max_seqs, max_pos, p);
+  if (st != MT_OK) return st;
+  *bytes = p.bytes;
+  return MT_OK;
+}
+
+mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, const int32_t* seq, const int32_t* pos,
+                    void* cache, int32_t max_seqs, int32_t max_pos, float* logits, int32_t* next, void* ws,
+                    size_t ws_bytes, void* stream) {
+  DecPlan p;
+  mt_status st = plan_decode(dec, n_rows, seq, pos, max_seqs, max_pos, p);
+  if (st != MT_OK) return st;
+  if (!x_in || !cache || !logits || !ws) return fail(MT_ERR_INVALID_ARG, "mt_decode: NULL device pointer");
+  if ((uintptr_t)ws % ALIGN || (uintptr_t)x_in % 16 || (uintptr_t)logits % 16 || (uintptr_t)cache % 16 ||
+      (uintptr_t)next % 4)
+    return fail(MT_ERR_INVALID_ARG, "mt_decode: misaligned pointer");
+  if (ws_bytes < p.bytes)
+    return fail(MT_ERR_WORKSPACE, "mt_decode: workspace %zu bytes < required %zu", ws_bytes, p.bytes);
+  const mt_decoder_config& c = dec->cfg;
+  const int dt = dec->dt, n = p.n;
+  const int D = c.d_model, F = c.d_ffn, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  const int NQKV = (Hq + 2 * Hkv) * hd, NQ = Hq * hd;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  HIP_TRY(upload_words((uint32_t*)(w + p.o_words), (const uint32_t*)p.words.data(), (int64_t)p.words.size(), s),
+          "upload tables");
+  const int32_t* wd = (const int32_t*)(w + p.o_words);
+  float* x = (float*)(w + p.o_x);
+  void* h = w + p.o_h;
+  float* qkv = (float*)(w + p.o_qkv);
+  float* opart = (float*)(w + p.o_opart);
+  float* dpart = (float*)(w + p.o_dpart);
+  void* act = w + p.o_act;
+  DecArgs a;
+  a.rows = n;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_seqs = max_seqs;
+  a.max_pos = max_pos;
+  a.eps = c.rms_eps;
+  a.log_base = std::log((double)c.rope_base);
+  a.seq = wd;
+  a.pos = wd + n;
+  a.items = wd + 2 * n;
+  a.first_item = wd + 2 * n + 2 * p.n_items;
+  a.qf = (float*)(w + p.o_qf);
+  a.cache = cache;
+  a.part_o = (float*)(w + p.o_po);
+  a.part_ml = (float*)(w + p.o_pml);
+  a.o16 = w + p.o_o16;
+  auto gemm_ = [&](const void* A_, int64_t lda, const void* B_, int M_, int N_, int K_, void* C_, int64_t ldc) {
+    GemmArgs g_ = ::gemm(A_, lda, B_, K_, M_, N_, K_, nullptr, C_, ldc);
+    g_.zeros = dec->zeros;
+    return g_;
+  };
+
+  HIP_TRY(launch_copy_f32(x_in, x, (int64_t)n * D, s), "copy input rows");
+  STAGE(launch_add_rmsnorm(x, nullptr, 0, c.n_layers ? dec->layers[0].in_norm : dec->norm, h, n, D, c.rms_eps, dt, s),
+        "rmsnorm");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const DecLayer& L = dec->layers[l];
+    a.layer = l;
+    a.q_norm = L.q_norm;
+    a.k_norm = L.k_norm;
+    if (p.gemv) {
+      STAGE(launch_gemv16(L.wqkv, h, qkv, n, NQKV, D, p.s_qkv, false, dt, s), "dec_qkv");
+    } else {
+      STAGE(launch_gemm(gemm_(h, D, L.wqkv, n, NQKV, D, qkv, NQKV), EPI_F32, dt, false, s), "dec_qkv");
+    }
+    STAGE(launch_qk_rope(a, qkv, p.s_qkv, dt, s), "dec_qk_rope");
+    STAGE(launch_attn_dec(a, p.n_items, dt, s), "dec_attn");
+    if (p.gemv) {
+      STAGE(launch_gemv16(L.wo, a.o16, opart, n, D, NQ, p.s_o, false, dt, s), "dec_o");
+    } else {
+      STAGE(launch_gemm(gemm_(a.o16, NQ, L.wo, n, D, NQ, x, D), EPI_RESID, dt, false, s), "dec_o");
+    }
+    STAGE(launch_add_rmsnorm(x, opart, p.s_o, L.post_norm, h, n, D, c.rms_eps, dt, s), "rmsnorm");
+    if (p.gemv) {
+      STAGE(launch_gemv16(L.wgu, h, act, n, 2 * F, D, 1, true, dt, s), "dec_gate_up");
+      STAGE(launch_gemv16(L.wd, act, dpart, n, D, F, p.s_d, false, dt, s), "dec_down");
+    } else {
+      STAGE(launch_gemm(gemm_(h, D, L.wgu, n, 2 * F, D, act, F), EPI_SWIGLU, dt, false, s), "dec_gate_up");
+      STAGE(launch_gemm(gemm_(act, F, L.wd, n, D, F, x, D), EPI_RESID, dt, false, s), "dec_down");
+    }
+    const float* nw = l + 1 < c.n_layers ? dec->layers[l + 1].in_norm : dec->norm;
+    STAGE(launch_add_rmsnorm(x, dpart, p.s_d, nw, h, n, D, c.rms_eps, dt, s), "rmsnorm");
+  }
+  if (p.gemv) {
+    STAGE(launch_gemv16(dec->embed, h, logits, n, c.vocab, D, 1, false, dt, s), "dec_head");
+  } else {
+    STAGE(launch_gemm(gemm_(h, D, dec->embed, n, c.vocab, D, logits, c.vocab), EPI_F32, dt, false, s), "dec_head");
+  }
+  if (next) STAGE(launch_argmax(logits, n, c.vocab, next, s), "argmax");
+  return MT_OK;
+}
+
 
 int64_t mt_mel_frames(int64_t n) { return n < 0 ? -1 : n / HOP; }
 

@@ -130,6 +130,37 @@ hipError_t launch_copy_rows(const float* x, float* out, int M, int D, const int3
 // (r in sequence sq), W values per row, dtype DT_BF16 or DT_F16.
 hipError_t launch_rows_to_half(const float* src, const int64_t* row_off, const int32_t* cu, int nseq,
                                int64_t rows, int W, void* dst, int dtype, hipStream_t s);
+// ------------------------------------------------------------------ decoder
+// Language-model decoder step (decoder.hip).  head_dim 128; the KV cache is
+// [layers][max_seqs][2 (K, V)][Hkv][max_pos][128] of the 16-bit type.
+struct DecArgs {
+  int rows, Hq, Hkv, layer, max_seqs, max_pos;
+  float eps;             // RMSNorm epsilon (Q/K-norm)
+  double log_base;       // ln(rotary base)
+  const int32_t* seq;    // [rows] cache slot of each row's sequence
+  const int32_t* pos;    // [rows] position of each row
+  const float* q_norm;   // [128] this layer's Q-norm weight
+  const float* k_norm;   // [128]
+  float* qf;             // [rows][Hq][128] rotated queries (fp32)
+  void* cache;
+  const int32_t* items;       // [n_items][2] (row, 256-key chunk), ordered by row
+  const int32_t* first_item;  // [rows + 1]
+  float* part_o;         // [n_items][Hkv][2][128]
+  float* part_ml;        // [n_items][Hkv][2][2] (chunk max, chunk sum)
+  void* o16;             // [rows][Hq][128] attention output (16-bit)
+};
+// out = x W^T for at most 16 rows of x (16-bit [rows][K]), W 16-bit [N][K]:
+// fp32 partial sums [ksplit][rows][N], or (swiglu, ksplit 1) SiLU(gate) * up
+// as 16 bits [rows][N / 2] from rows interleaved in blocks of 16.
+hipError_t launch_gemv16(const void* W, const void* x, void* out, int rows, int N, int K, int ksplit, bool swiglu,
+                         int dtype, hipStream_t s);
+// x += sum of S fp32 partials [S][rows][D]; h = RMSNorm(x) * w as dtype.
+hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w, void* h, int rows, int D, float eps,
+                              int dtype, hipStream_t s);
+hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, hipStream_t s);
+hipError_t launch_attn_dec(const DecArgs& a, int n_items, int dtype, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* next, hipStream_t s);
+
 // Weight repacking (fp32 masters -> kernel layouts); dtype selects the
 // destination element type (DT_*).
 hipError_t launch_convert(const float* src, void* dst, int64_t rows, int64_t cols, int64_t dst_ld,
