@@ -252,6 +252,89 @@ def measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel, steps=10, warmup
             "step_tflops": round(fl / (ms * 1e-3) / 1e12, 1), "breakdown_ms_per_step": stages}
 
 
+def measure_decoder(W, synth, torch, ctx=400, batches=(1, 16), reps=20):
+    """The language-model decoder step (Qwen3-1.7B geometry, bf16 weights,
+    seeded N(0, 0.02^2) weights drawn on the device) over B sequences whose
+    KV cache holds a ctx-position prompt: ms per step eager and as a replayed
+    HIP graph, tokens/s, and HBM bytes per step (every weight once, the KV
+    entries each row reads) against the 8 TB/s peak."""
+    import numpy as np
+    geom = synth.DEC_GEOM
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    dev = []
+    for name, shape in synth.decoder_weight_names(geom):
+        if len(shape) == 1:
+            dev.append(1.0 + 0.1 * torch.randn(shape, generator=gen, device="cuda"))
+        else:
+            dev.append(torch.randn(shape, generator=gen, device="cuda") * (1.0 if name == "embed.weight" else 0.02))
+    cfg = W.decoder_config(geom, W.MT_BF16)
+    dec = W.mt_decoder_create(cfg, dev)
+    torch.cuda.synchronize()
+    del dev
+    Bmax = max(batches)
+    cache = torch.zeros(W.mt_decoder_cache_bytes(dec, Bmax, ctx + 8), dtype=torch.uint8, device="cuda")
+    emb = W.mt_decoder_embedding(dec)
+    # prompts: ctx positions of every sequence, one call per sequence
+    for sq in range(Bmax):
+        x = emb[torch.randint(0, geom["vocab"], (ctx,), generator=gen, device="cuda")].float()
+        W.mt_decode(dec, x, [sq] * ctx, list(range(ctx)), cache, Bmax, ctx + 8)
+    torch.cuda.synchronize()
+    weight_bytes = 2 * sum(int(np.prod(s)) for n, s in synth.decoder_weight_names(geom) if len(s) > 1)
+    kv_row = geom["n_layers"] * 2 * geom["n_kv_heads"] * geom["head_dim"] * 2  # bytes per cached position
+    out = {"workload": "decode_step_qwen3_1.7b_bf16_ctx%d" % ctx, "weight_bytes": weight_bytes}
+    for B in batches:
+        x = emb[torch.randint(0, geom["vocab"], (B,), generator=gen, device="cuda")].float().contiguous()
+        seq, pos = list(range(B)), [ctx] * B
+        ws = torch.empty(W.mt_decode_workspace_size(dec, seq, pos, Bmax, ctx + 8), dtype=torch.uint8, device="cuda")
+        logits = torch.empty((B, geom["vocab"]), dtype=torch.float32, device="cuda")
+        nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def step():
+            W.mt_decode(dec, x, seq, pos, cache, Bmax, ctx + 8, logits, nxt, ws, stream=torch.cuda.current_stream())
+
+        for _ in range(3):
+            step()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) / reps
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        ref = logits.clone()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(logits, ref))
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / reps
+        nbytes = weight_bytes + B * (ctx + 1) * kv_row
+        out["B%d" % B] = {"ms_eager": round(eager, 4), "ms_graph": round(gms, 4),
+                          "tokens_per_s": round(B / (gms * 1e-3), 1), "hbm_bytes": nbytes,
+                          "GBps": round(nbytes / (gms * 1e-3) / 1e9, 1),
+                          "frac_of_8TBps": round(nbytes / (gms * 1e-3) / 8e12, 4),
+                          "graph_replay_equals_eager": same}
+        del graph
+    dec.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +343,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
+    ap.add_argument("--no-decoder", action="store_true",
+                    help="skip the language-model decoder step")
     ap.add_argument("--no-2x", action="store_true",
                     help="skip the 2x-front-end full-attention workload")
     ap.add_argument("--no-stream", action="store_true",
@@ -390,6 +475,8 @@ def main():
         res["prompt_splice"] = splice_measure(W, out, lens_T, synth, torch, np)
     if not args.no_2x:
         res["conv1d_2x_16x30s"] = measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel)
+    if not args.no_decoder:
+        res["decoder_step"] = measure_decoder(W, synth, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(clips[0], weights, geom, window)
     print(json.dumps(res), flush=True)

@@ -180,3 +180,37 @@ def test_full_geometry_batch_equals_single():
         assert np.array_equal(l1[0], gl[s]), f"row {s}"
         assert n1[0] == nx[s]
     torch.cuda.synchronize()
+
+
+def test_decode_step_graph_replays_match_eager(small_w):
+    """The decode step captured in a HIP graph (as the benchmark times it):
+    every replay, with eager work between replays, equals the eager step."""
+    import torch
+    import windowed_attention_audio_amd as W
+    g = GpuDecoder(SMALL, small_w, "bf16", 4, 64)
+    rng = np.random.default_rng(8)
+    emb = small_w["embed.weight"]
+    g.step(emb[rng.integers(0, SMALL["vocab"], 40)], sum(([s] * 10 for s in range(4)), []), list(range(10)) * 4)
+    x = torch.from_numpy(np.ascontiguousarray(emb[rng.integers(0, SMALL["vocab"], 4)])).cuda()
+    seq, pos = [0, 1, 2, 3], [10] * 4
+    ws = torch.empty(W.mt_decode_workspace_size(g.dec, seq, pos, 4, 64), dtype=torch.uint8, device="cuda")
+    logits = torch.empty((4, SMALL["vocab"]), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(4, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture
+        W.mt_decode(g.dec, x, seq, pos, g.cache, 4, 64, logits, nxt, ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = logits.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        W.mt_decode(g.dec, x, seq, pos, g.cache, 4, 64, logits, nxt, ws,
+                    stream=torch.cuda.current_stream())
+    for i in range(3):
+        logits.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, eager), f"replay {i}"
+        _ = (x * 2.0).sum().item()  # eager work between replays

@@ -720,10 +720,10 @@ int gemv_split(int N, int K) {
 }
 
 struct DecPlan {
-  int n = 0, n_items = 0, s_qkv = 1, s_o = 1, s_d = 1;
+  int n = 0, n_items = 0, s_qkv = 1, s_o = 1, s_gu = 1, s_d = 1;
   bool gemv = true;
   std::vector<int32_t> words;  // seq | pos | items | first_item
-  size_t o_words, o_x, o_h, o_qkv, o_qf, o_po, o_pml, o_o16, o_opart, o_act, o_dpart, bytes;
+  size_t o_words, o_x, o_h, o_qkv, o_qf, o_po, o_pml, o_o16, o_opart, o_gu, o_act, o_dpart, o_amv, o_ami, bytes;
 };
 
 }  // namespace
@@ -760,7 +760,7 @@ mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, cons
     p.words[i] = seq[i];
     p.words[n + i] = pos[i];
     first[i] = (int32_t)(items.size() / 2);
-    for (int ch = 0; ch * 256 <= pos[i]; ++ch) {
+    for (int ch = 0; ch * 64 <= pos[i]; ++ch) {  // 64-key attention chunks
       items.push_back(i);
       items.push_back(ch);
     }
@@ -778,9 +778,11 @@ mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, cons
   if (p.gemv) {
     p.s_qkv = gemv_split((int)NQKV, (int)D);
     p.s_o = gemv_split((int)D, (int)NQ);
+    p.s_gu = gemv_split(2 * (int)F, (int)D);
     p.s_d = gemv_split((int)D, (int)F);
   } else {
     p.s_qkv = 1;
+    p.s_gu = 0;
     p.s_o = p.s_d = 0;  // the matrix kernels add into the residual stream
   }
   Carver k;
@@ -793,8 +795,11 @@ mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, cons
   p.o_pml = k.take((size_t)p.n_items * Hkv * 2 * 2 * 4);
   p.o_o16 = k.take((size_t)n * NQ * 2);
   p.o_opart = k.take((size_t)p.s_o * n * D * 4);
+  p.o_gu = k.take((size_t)p.s_gu * n * 2 * F * 4);
   p.o_act = k.take((size_t)n * F * 2);
   p.o_dpart = k.take((size_t)p.s_d * n * D * 4);
+  p.o_amv = k.take((size_t)n * 64 * 4);
+  p.o_ami = k.take((size_t)n * 64 * 4);
   p.bytes = k.off;
   return MT_OK;
 }
@@ -962,21 +967,22 @@ mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, co
     a.q_norm = L.q_norm;
     a.k_norm = L.k_norm;
     if (p.gemv) {
-      STAGE(launch_gemv16(L.wqkv, h, qkv, n, NQKV, D, p.s_qkv, false, dt, s), "dec_qkv");
+      STAGE(launch_gemv16(L.wqkv, h, qkv, n, NQKV, D, p.s_qkv, dt, s), "dec_qkv");
     } else {
       STAGE(launch_gemm(gemm_(h, D, L.wqkv, n, NQKV, D, qkv, NQKV), EPI_F32, dt, false, s), "dec_qkv");
     }
     STAGE(launch_qk_rope(a, qkv, p.s_qkv, dt, s), "dec_qk_rope");
     STAGE(launch_attn_dec(a, p.n_items, dt, s), "dec_attn");
     if (p.gemv) {
-      STAGE(launch_gemv16(L.wo, a.o16, opart, n, D, NQ, p.s_o, false, dt, s), "dec_o");
+      STAGE(launch_gemv16(L.wo, a.o16, opart, n, D, NQ, p.s_o, dt, s), "dec_o");
     } else {
       STAGE(launch_gemm(gemm_(a.o16, NQ, L.wo, n, D, NQ, x, D), EPI_RESID, dt, false, s), "dec_o");
     }
     STAGE(launch_add_rmsnorm(x, opart, p.s_o, L.post_norm, h, n, D, c.rms_eps, dt, s), "rmsnorm");
     if (p.gemv) {
-      STAGE(launch_gemv16(L.wgu, h, act, n, 2 * F, D, 1, true, dt, s), "dec_gate_up");
-      STAGE(launch_gemv16(L.wd, act, dpart, n, D, F, p.s_d, false, dt, s), "dec_down");
+      STAGE(launch_gemv16(L.wgu, h, (float*)(w + p.o_gu), n, 2 * F, D, p.s_gu, dt, s), "dec_gate_up");
+      STAGE(launch_swiglu((const float*)(w + p.o_gu), p.s_gu, act, n, F, dt, s), "dec_swiglu");
+      STAGE(launch_gemv16(L.wd, act, dpart, n, D, F, p.s_d, dt, s), "dec_down");
     } else {
       STAGE(launch_gemm(gemm_(h, D, L.wgu, n, 2 * F, D, act, F), EPI_SWIGLU, dt, false, s), "dec_gate_up");
       STAGE(launch_gemm(gemm_(act, F, L.wd, n, D, F, x, D), EPI_RESID, dt, false, s), "dec_down");
@@ -985,11 +991,12 @@ mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, co
     STAGE(launch_add_rmsnorm(x, dpart, p.s_d, nw, h, n, D, c.rms_eps, dt, s), "rmsnorm");
   }
   if (p.gemv) {
-    STAGE(launch_gemv16(dec->embed, h, logits, n, c.vocab, D, 1, false, dt, s), "dec_head");
+    STAGE(launch_gemv16(dec->embed, h, logits, n, c.vocab, D, 1, dt, s), "dec_head");
   } else {
     STAGE(launch_gemm(gemm_(h, D, dec->embed, n, c.vocab, D, logits, c.vocab), EPI_F32, dt, false, s), "dec_head");
   }
-  if (next) STAGE(launch_argmax(logits, n, c.vocab, next, s), "argmax");
+  if (next)
+    STAGE(launch_argmax(logits, n, c.vocab, (float*)(w + p.o_amv), (int*)(w + p.o_ami), next, s), "argmax");
   return MT_OK;
 }
 

@@ -13,13 +13,17 @@
 // atomics: results do not depend on timing).
 //   * qkv partials -> qk_rope_kernel: sum, RMSNorm of each q / k head,
 //     rotation, q kept in fp32, k and v written into the cache;
-//   * attention: one workgroup per (row, key/value head, 256-key chunk), both
+//   * attention: one workgroup per (row, key/value head, 64-key chunk), both
 //     query heads of the group; chunk partials (max, sum, output) combined
 //     by attn_combine_kernel;
 //   * o and down partials -> add_rmsnorm_kernel: residual += sum, then the
 //     next RMSNorm;
-//   * gate/up (rows interleaved by 16) at full K with the SwiGLU epilogue;
-//   * the head: the tied embedding table, then argmax_kernel.
+//   * gate/up partials (rows interleaved by 16) -> swiglu_kernel;
+//   * the head: the tied embedding table, then a two-pass argmax.
+// Small kernels issue every load of their rows before the first use: at a
+// few rows per step, memory latency rather than bandwidth sets their time.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -46,95 +50,123 @@ __device__ __forceinline__ float wmax64(float v) {
 // row n0 + l16, columns k + 8g .. k + 8g + 7 (16 bytes) and the same columns
 // of x row l16.  The MFMA is issued as B = weights, A = x, so the lane holds
 // out[x row l16][n0 + 4g .. n0 + 4g + 3].
-// EPI 0: fp32 partials [S][rows][N]; EPI 1 (SwiGLU, S = 1): W rows
-// interleaved in blocks of 16 (16 gate rows, then the 16 up rows of the same
-// features), each wavefront takes 32 rows and writes SiLU(g) u as 16 bits
-// to out[r][feature].
-template <typename T, int EPI>
+// Output: fp32 partial sums [S][rows][N].  U K steps are loaded before the
+// first MFMA: U covers a wavefront's whole K range (one round trip to
+// memory) up to 32 steps.
+template <typename T, int U>
 __global__ __launch_bounds__(256) void gemv16_kernel(const T* __restrict__ W, const T* __restrict__ x,
-                                                     void* __restrict__ out, int rows, int N, int K,
-                                                     int ksplit) {
-  constexpr int TILES = EPI == 1 ? 2 : 1;  // 16-row weight tiles per wavefront
+                                                     float* __restrict__ out, int rows, int N, int K, int ksplit) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nblk = N / (16 * TILES);
+  const int nblk = N / 16;
   const int s = wid / nblk, blk = wid - s * nblk;
   if (s >= ksplit) return;
-  const int n0 = blk * 16 * TILES;
+  const int n0 = blk * 16;
   const int kl = K / ksplit, k0 = s * kl;
   const bool xr = l16 < rows;
-  const T* wp0 = W + (int64_t)(n0 + l16) * K + k0 + 8 * g;
-  const T* wp1 = W + (int64_t)(n0 + 16 + l16) * K + k0 + 8 * g;
+  const T* wp = W + (int64_t)(n0 + l16) * K + k0 + 8 * g;
   const T* xp = x + (int64_t)(xr ? l16 : 0) * K + k0 + 8 * g;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 8;  // K steps in flight
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < kl; k += 32 * U) {
-    uint4 wa[U], wb[U], xa[U];
+    uint4 wa[U], xa[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = k + 32 * u < kl;
-      wa[u] = in ? *(const uint4*)(wp0 + k + 32 * u) : make_uint4(0, 0, 0, 0);
-      if constexpr (TILES == 2) wb[u] = in ? *(const uint4*)(wp1 + k + 32 * u) : make_uint4(0, 0, 0, 0);
+      wa[u] = in ? *(const uint4*)(wp + k + 32 * u) : make_uint4(0, 0, 0, 0);
       xa[u] = (in && xr) ? *(const uint4*)(xp + k + 32 * u) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      mma16(acc0, wa[u], xa[u], T{});
-      if constexpr (TILES == 2) mma16(acc1, wb[u], xa[u], T{});
-    }
+    for (int u = 0; u < U; ++u) mma16(acc, wa[u], xa[u], T{});
   }
   if (!xr) return;
-  if constexpr (EPI == 0) {
-    float* o = (float*)out + ((int64_t)s * rows + l16) * N + n0 + 4 * g;
-    *(float4*)o = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-  } else {
-    // features blk * 16 + 4g .. + 3: gate in acc0, up in acc1
-    T* o = (T*)out + (int64_t)l16 * (N / 2) + blk * 16 + 4 * g;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = silu_f(acc0[e]) * acc1[e];
-    *(uint2*)o = make_uint2(pack2(Elem<T>::from_f(v[0]), Elem<T>::from_f(v[1])),
-                            pack2(Elem<T>::from_f(v[2]), Elem<T>::from_f(v[3])));
-  }
+  float* o = out + ((int64_t)s * rows + l16) * N + n0 + 4 * g;
+  *(float4*)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 // --------------------------------------------------- residual add + RMSNorm
-// One wavefront per row: x[r] += sum_s part[s][r] (S may be 0), then
-// h[r] = x[r] / sqrt(mean(x^2) + eps) * w as T (or fp32 when T = float).
+// One workgroup per row: x[r] += sum_s part[s][r] (S <= 8, may be 0), then
+// h[r] = x[r] / sqrt(mean(x^2) + eps) * w as T (fp32 when T = float).  Every
+// load of the row is issued before the first use (a row is 8 KB; latency,
+// not bandwidth, sets the time).
+constexpr int MAXS = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x, const float* __restrict__ part,
                                                           int S, const float* __restrict__ w, void* __restrict__ h,
                                                           int rows, int D, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  __shared__ float red[4];
+  constexpr int MC = 4;  // float4 chunks per thread: D <= 4096
+  const int r = blockIdx.x, t = threadIdx.x;
   float* xr = x + (int64_t)r * D;
+  const int nc = D / 4;
+  float4 v[MC];
   float ss = 0.f;
-  for (int c = lane * 4; c < D; c += 256) {
-    float4 v = *(float4*)(xr + c);
-    for (int s = 0; s < S; ++s) {
-      const float4 p = *(const float4*)(part + ((int64_t)s * rows + r) * D + c);
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
-    }
-    if (S) *(float4*)(xr + c) = v;
-    ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-  }
-  const float rs = 1.0f / sqrtf(wsum64(ss) / D + eps);
-  for (int c = lane * 4; c < D; c += 256) {
-    const float4 v = *(const float4*)(xr + c);
-    const float4 ww = *(const float4*)(w + c);
-    const float y0 = v.x * rs * ww.x, y1 = v.y * rs * ww.y, y2 = v.z * rs * ww.z, y3 = v.w * rs * ww.w;
-    if constexpr (sizeof(T) == 4) {
-      *(float4*)((float*)h + (int64_t)r * D + c) = make_float4(y0, y1, y2, y3);
-    } else {
-      typedef Elem<T> E;
-      *(uint2*)((T*)h + (int64_t)r * D + c) =
-          make_uint2(pack2(E::from_f(y0), E::from_f(y1)), pack2(E::from_f(y2), E::from_f(y3)));
+#pragma unroll
+  for (int i = 0; i < MC; ++i) {
+    const int c = t + 256 * i;
+    if (c < nc) {
+      v[i] = ((const float4*)xr)[c];
+      float4 p[MAXS];
+#pragma unroll
+      for (int s2 = 0; s2 < MAXS; ++s2)
+        if (s2 < S) p[s2] = ((const float4*)(part + ((int64_t)s2 * rows + r) * D))[c];
+#pragma unroll
+      for (int s2 = 0; s2 < MAXS; ++s2)
+        if (s2 < S) {
+          v[i].x += p[s2].x;
+          v[i].y += p[s2].y;
+          v[i].z += p[s2].z;
+          v[i].w += p[s2].w;
+        }
+      if (S) ((float4*)xr)[c] = v[i];
+      ss += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
     }
   }
+  ss = wsum64(ss);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / D + eps);
+#pragma unroll
+  for (int i = 0; i < MC; ++i) {
+    const int c = t + 256 * i;
+    if (c < nc) {
+      const float4 ww = ((const float4*)w)[c];
+      const float y0 = v[i].x * rs * ww.x, y1 = v[i].y * rs * ww.y, y2 = v[i].z * rs * ww.z, y3 = v[i].w * rs * ww.w;
+      if constexpr (sizeof(T) == 4) {
+        ((float4*)((float*)h + (int64_t)r * D))[c] = make_float4(y0, y1, y2, y3);
+      } else {
+        typedef Elem<T> E;
+        ((uint2*)((T*)h + (int64_t)r * D))[c] =
+            make_uint2(pack2(E::from_f(y0), E::from_f(y1)), pack2(E::from_f(y2), E::from_f(y3)));
+      }
+    }
+  }
+}
+
+// SwiGLU of the gate/up partial sums: act[r][f] = SiLU(sum g) * (sum u), gate
+// row 32 (f / 16) + f % 16 and up row 32 (f / 16) + 16 + f % 16 of the [S][rows]
+// [2F] partials.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, T* __restrict__ act,
+                                                     int rows, int F) {
+  const int r = blockIdx.y, f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= F) return;
+  const int gi = 32 * (f >> 4) + (f & 15);
+  float gp[MAXS], up[MAXS];
+#pragma unroll
+  for (int s2 = 0; s2 < MAXS; ++s2)
+    if (s2 < S) {
+      const float* p = part + ((int64_t)s2 * rows + r) * 2 * F;
+      gp[s2] = p[gi];
+      up[s2] = p[gi + 16];
+    }
+  float g = 0.f, u = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < MAXS; ++s2)
+    if (s2 < S) {
+      g += gp[s2];
+      u += up[s2];
+    }
+  act[(int64_t)r * F + f] = Elem<T>::from_f(silu_f(g) * u);
 }
 
 // ------------------------------------------- Q/K-norm, rotation, cache append
@@ -149,12 +181,21 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __
   if (item >= a.rows * nh) return;
   const int r = item / nh, hh = item - r * nh;
   const int ld = nh * HD;
+  float p0[MAXS], p1[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < S) {
+      const float* p = qkv + ((int64_t)s * a.rows + r) * ld + hh * HD;
+      p0[s] = p[lane];
+      p1[s] = p[lane + 64];
+    }
   float v0 = 0.f, v1 = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* p = qkv + ((int64_t)s * a.rows + r) * ld + hh * HD;
-    v0 += p[lane];
-    v1 += p[lane + 64];
-  }
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < S) {
+      v0 += p0[s];
+      v1 += p1[s];
+    }
   const int pos = a.pos[r], sq = a.seq[r];
   if (hh < a.Hq + a.Hkv) {
     const float* nw = hh < a.Hq ? a.q_norm : a.k_norm;
@@ -183,21 +224,24 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __
 }
 
 // ------------------------------------------------------------ attention
-// One workgroup per (chunk item, key/value head): item = (row, chunk of 256
-// keys) from the host's table; both query heads 2 kh, 2 kh + 1 (groups of
-// Hq / Hkv consecutive query heads; the kernel handles groups of 2).
-//   scores: thread t takes key c0 + t (keys past the row's position drop
-//   out), dot with both heads' q (fp32, LDS); chunk max / sum per head;
-//   output: thread (head, d) sums p V over the chunk's keys.
+// One workgroup per (chunk item, key/value head): item = (row, chunk of 64
+// keys) from the host's table; both query heads 2 kh, 2 kh + 1 of the group.
+//   scores: four threads per key, 32 values each (four 16-byte loads),
+//   reduced by shuffles; keys past the row's position drop out;
+//   output: thread (key group kg, 8 values dg) sums p V over keys kg, kg +
+//   16, kg + 32, kg + 48 with 16-byte loads, then the 16 key groups are
+//   added through LDS.
+constexpr int CHUNK = 64;
 template <typename T>
 __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
   __shared__ float qs[2][HD];
-  __shared__ float ps[2][256];
+  __shared__ float ps[2][CHUNK];
   __shared__ float red[2][8];
+  __shared__ float ro[16][2][HD];
   const int it = blockIdx.x, kh = blockIdx.y, t = threadIdx.x;
-  const int r = a.items[2 * it], c0 = a.items[2 * it + 1] * 256;
+  const int r = a.items[2 * it], c0 = a.items[2 * it + 1] * CHUNK;
   const int pos = a.pos[r], sq = a.seq[r];
-  const int nk = min(256, pos + 1 - c0);  // keys of this chunk (>= 1)
+  const int nk = min(CHUNK, pos + 1 - c0);  // keys of this chunk (>= 1)
   const T* Kc = (const T*)a.cache + ((((int64_t)a.layer * a.max_seqs + sq) * 2 + 0) * a.Hkv + kh) * a.max_pos * HD;
   const T* Vc = Kc + (int64_t)a.Hkv * a.max_pos * HD;
   {
@@ -205,26 +249,30 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
     qs[h][d] = a.qf[((int64_t)r * a.Hq + 2 * kh + h) * HD + d];
   }
   __syncthreads();
-  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
-  float s0 = -INFINITY, s1 = -INFINITY;
-  if (t < nk) {
-    const uint4* kr = (const uint4*)(Kc + (int64_t)(c0 + t) * HD);
-    float d0 = 0.f, d1 = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < HD / 8; ++c) {
-      const uint4 u = kr[c];
-      const T* e = (const T*)&u;
+  const int kk = t >> 2, part = t & 3;
+  float d0 = 0.f, d1 = 0.f;
+  if (kk < nk) {
+    const uint4* kr = (const uint4*)(Kc + (int64_t)(c0 + kk) * HD + part * 32);
+    uint4 u[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = kr[c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const T* e = (const T*)&u[c];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float kv = Elem<T>::to_f(e[j]);
-        d0 = fmaf(kv, qs[0][8 * c + j], d0);
-        d1 = fmaf(kv, qs[1][8 * c + j], d1);
+        d0 = fmaf(kv, qs[0][part * 32 + 8 * c + j], d0);
+        d1 = fmaf(kv, qs[1][part * 32 + 8 * c + j], d1);
       }
     }
-    s0 = d0 * scale;
-    s1 = d1 * scale;
   }
-  // chunk max per head
+  d0 += __shfl_xor(d0, 1, 64);
+  d1 += __shfl_xor(d1, 1, 64);
+  d0 += __shfl_xor(d0, 2, 64);
+  d1 += __shfl_xor(d1, 2, 64);
+  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  const float s0 = kk < nk ? d0 * scale : -INFINITY, s1 = kk < nk ? d1 * scale : -INFINITY;
   const int wv = t >> 6;
   float m0 = wmax64(s0), m1 = wmax64(s1);
   if ((t & 63) == 0) {
@@ -234,22 +282,50 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
   __syncthreads();
   m0 = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   m1 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-  const float p0 = t < nk ? __expf(s0 - m0) : 0.f, p1 = t < nk ? __expf(s1 - m1) : 0.f;
-  ps[0][t] = p0;
-  ps[1][t] = p1;
-  const float l0 = wsum64(p0), l1 = wsum64(p1);
-  __syncthreads();  // red (max) read by all before it is reused
+  const float p0 = kk < nk ? __expf(s0 - m0) : 0.f, p1 = kk < nk ? __expf(s1 - m1) : 0.f;
+  if (part == 0) {
+    ps[0][kk] = p0;
+    ps[1][kk] = p1;
+  }
+  // each key counted once (part 0 of its four threads)
+  const float l0 = wsum64(part == 0 ? p0 : 0.f), l1 = wsum64(part == 0 ? p1 : 0.f);
+  __syncthreads();
   if ((t & 63) == 0) {
     red[0][4 + wv] = l0;
     red[1][4 + wv] = l1;
   }
+  const int kg = t >> 4, dg = t & 15;
+  float o0[8], o1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o0[j] = o1[j] = 0.f;
+  uint4 vv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = kg + 16 * i;
+    vv[i] = k < nk ? *(const uint4*)(Vc + (int64_t)(c0 + k) * HD + dg * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = kg + 16 * i;
+    const float q0 = k < nk ? ps[0][k] : 0.f, q1 = k < nk ? ps[1][k] : 0.f;
+    const T* e = (const T*)&vv[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = Elem<T>::to_f(e[j]);
+      o0[j] = fmaf(q0, v, o0[j]);
+      o1[j] = fmaf(q1, v, o1[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ro[kg][0][dg * 8 + j] = o0[j];
+    ro[kg][1][dg * 8 + j] = o1[j];
+  }
   __syncthreads();
-  // output: thread (h, d)
   const int h = t >> 7, d = t & 127;
   float o = 0.f;
-  const T* vp = Vc + (int64_t)c0 * HD + d;
-  const float* pp = ps[h];
-  for (int k = 0; k < nk; ++k) o = fmaf(pp[k], Elem<T>::to_f(vp[(int64_t)k * HD]), o);
+#pragma unroll
+  for (int g2 = 0; g2 < 16; ++g2) o += ro[g2][h][d];
   // partial: [item][kh][h] -> (m, l) and o[HD]
   const int64_t slot = ((int64_t)it * a.Hkv + kh) * 2 + h;
   a.part_o[slot * HD + d] = o;
@@ -280,70 +356,80 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(DecArgs a) {
 }
 
 // ------------------------------------------------------------- argmax
-// One workgroup per row: the first index of the largest logit.
-__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int V, int32_t* next) {
+// Two passes: workgroup (b, r) reduces slice b of row r's logits to (value,
+// first index); then one wavefront per row reduces the AMB slices.  Ties go
+// to the lower index in both passes: the result is the row's first maximum.
+constexpr int AMB = 64;
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+__global__ __launch_bounds__(256) void argmax_part_kernel(const float* __restrict__ logits, int V, float* pv,
+                                                          int* pi) {
   __shared__ float bv[4];
   __shared__ int bi[4];
-  const int r = blockIdx.x, t = threadIdx.x;
+  const int b = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int len = (V + AMB - 1) / AMB, i0 = b * len, i1 = min(V, i0 + len);
   const float* l = logits + (int64_t)r * V;
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int i = t; i < V; i += 256) {
-    const float v = l[i];
-    if (v > best) {  // increasing i: the first maximum of this thread's subset
-      best = v;
-      idx = i;
-    }
-  }
+  for (int i = i0 + t; i < i1; i += 256) better(best, idx, l[i], i);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(best, off, 64);
-    const int oi = __shfl_xor(idx, off, 64);
-    if (ov > best || (ov == best && oi < idx)) {
-      best = ov;
-      idx = oi;
-    }
-  }
+  for (int off = 32; off >= 1; off >>= 1) better(best, idx, __shfl_xor(best, off, 64), __shfl_xor(idx, off, 64));
   if ((t & 63) == 0) {
     bv[t >> 6] = best;
     bi[t >> 6] = idx;
   }
   __syncthreads();
   if (t == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (bv[w] > best || (bv[w] == best && bi[w] < idx)) {
-        best = bv[w];
-        idx = bi[w];
-      }
-    next[r] = idx;
+    for (int w = 1; w < 4; ++w) better(best, idx, bv[w], bi[w]);
+    pv[r * AMB + b] = best;
+    pi[r * AMB + b] = idx;
   }
+}
+__global__ __launch_bounds__(64) void argmax_final_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                          int32_t* next) {
+  const int r = blockIdx.x, t = threadIdx.x;
+  float best = pv[r * AMB + t];
+  int idx = pi[r * AMB + t];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) better(best, idx, __shfl_xor(best, off, 64), __shfl_xor(idx, off, 64));
+  if (t == 0) next[r] = idx;
 }
 
 }  // namespace
 
-hipError_t launch_gemv16(const void* W, const void* x, void* out, int rows, int N, int K, int ksplit, bool swiglu,
-                         int dtype, hipStream_t s) {
-  if (rows < 1 || rows > 16 || K % (32 * ksplit) || N % (swiglu ? 32 : 16) || (swiglu && ksplit != 1))
-    return hipErrorInvalidValue;
-  const int waves = (N / (swiglu ? 32 : 16)) * ksplit;
+hipError_t launch_gemv16(const void* W, const void* x, float* out, int rows, int N, int K, int ksplit, int dtype,
+                         hipStream_t s) {
+  if (rows < 1 || rows > 16 || ksplit < 1 || K % (32 * ksplit) || N % 16) return hipErrorInvalidValue;
+  const int waves = (N / 16) * ksplit;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  if (dtype == DT_BF16) {
-    if (swiglu) hipLaunchKernelGGL((gemv16_kernel<bf16_t, 1>), grid, block, 0, s, (const bf16_t*)W, (const bf16_t*)x, out, rows, N, K, 1);
-    else hipLaunchKernelGGL((gemv16_kernel<bf16_t, 0>), grid, block, 0, s, (const bf16_t*)W, (const bf16_t*)x, out, rows, N, K, ksplit);
-  } else if (dtype == DT_F16) {
-    if (swiglu) hipLaunchKernelGGL((gemv16_kernel<f16_t, 1>), grid, block, 0, s, (const f16_t*)W, (const f16_t*)x, out, rows, N, K, 1);
-    else hipLaunchKernelGGL((gemv16_kernel<f16_t, 0>), grid, block, 0, s, (const f16_t*)W, (const f16_t*)x, out, rows, N, K, ksplit);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  const int steps = K / ksplit / 32;
+  auto go = [&](auto u) {
+    constexpr int U = decltype(u)::value;
+    if (dtype == DT_BF16)
+      hipLaunchKernelGGL((gemv16_kernel<bf16_t, U>), grid, block, 0, s, (const bf16_t*)W, (const bf16_t*)x, out, rows,
+                         N, K, ksplit);
+    else
+      hipLaunchKernelGGL((gemv16_kernel<f16_t, U>), grid, block, 0, s, (const f16_t*)W, (const f16_t*)x, out, rows, N,
+                         K, ksplit);
+  };
+  if (dtype != DT_BF16 && dtype != DT_F16) return hipErrorInvalidValue;
+  if (steps <= 8) go(std::integral_constant<int, 8>{});
+  else if (steps <= 16) go(std::integral_constant<int, 16>{});
+  else if (steps <= 24) go(std::integral_constant<int, 24>{});
+  else if (steps <= 32) go(std::integral_constant<int, 32>{});
+  else go(std::integral_constant<int, 8>{});
   return hipGetLastError();
 }
 
 hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w, void* h, int rows, int D, float eps,
                               int dtype, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (D % 256) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (D % 256 || D > 4096 || S < 0 || S > MAXS) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)rows), block(256);
   if (dtype == DT_BF16) hipLaunchKernelGGL(add_rmsnorm_kernel<bf16_t>, grid, block, 0, s, x, part, S, w, h, rows, D, eps);
   else if (dtype == DT_F16) hipLaunchKernelGGL(add_rmsnorm_kernel<f16_t>, grid, block, 0, s, x, part, S, w, h, rows, D, eps);
   else hipLaunchKernelGGL(add_rmsnorm_kernel<float>, grid, block, 0, s, x, part, S, w, h, rows, D, eps);
@@ -351,6 +437,7 @@ hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w
 }
 
 hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, hipStream_t s) {
+  if (S < 1 || S > MAXS) return hipErrorInvalidValue;
   const int items = a.rows * (a.Hq + 2 * a.Hkv);
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
   if (dtype == DT_BF16) hipLaunchKernelGGL(qk_rope_kernel<bf16_t>, grid, block, 0, s, a, qkv, S);
@@ -374,9 +461,20 @@ hipError_t launch_attn_dec(const DecArgs& a, int n_items, int dtype, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* next, hipStream_t s) {
+hipError_t launch_argmax(const float* logits, int rows, int V, float* pv, int* pi, int32_t* next, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(256), 0, s, logits, V, next);
+  hipLaunchKernelGGL(argmax_part_kernel, dim3(AMB, (unsigned)rows), dim3(256), 0, s, logits, V, pv, pi);
+  hipLaunchKernelGGL(argmax_final_kernel, dim3((unsigned)rows), dim3(64), 0, s, pv, pi, next);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float* part, int S, void* act, int rows, int F, int dtype, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (S < 1 || S > MAXS || F % 16) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((F + 255) / 256), (unsigned)rows), block(256);
+  if (dtype == DT_BF16) hipLaunchKernelGGL(swiglu_kernel<bf16_t>, grid, block, 0, s, part, S, (bf16_t*)act, rows, F);
+  else if (dtype == DT_F16) hipLaunchKernelGGL(swiglu_kernel<f16_t>, grid, block, 0, s, part, S, (f16_t*)act, rows, F);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

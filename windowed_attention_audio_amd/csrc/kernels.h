@@ -143,23 +143,26 @@ struct DecArgs {
   const float* k_norm;   // [128]
   float* qf;             // [rows][Hq][128] rotated queries (fp32)
   void* cache;
-  const int32_t* items;       // [n_items][2] (row, 256-key chunk), ordered by row
+  const int32_t* items;       // [n_items][2] (row, 64-key chunk), ordered by row
   const int32_t* first_item;  // [rows + 1]
   float* part_o;         // [n_items][Hkv][2][128]
   float* part_ml;        // [n_items][Hkv][2][2] (chunk max, chunk sum)
   void* o16;             // [rows][Hq][128] attention output (16-bit)
 };
 // out = x W^T for at most 16 rows of x (16-bit [rows][K]), W 16-bit [N][K]:
-// fp32 partial sums [ksplit][rows][N], or (swiglu, ksplit 1) SiLU(gate) * up
-// as 16 bits [rows][N / 2] from rows interleaved in blocks of 16.
-hipError_t launch_gemv16(const void* W, const void* x, void* out, int rows, int N, int K, int ksplit, bool swiglu,
-                         int dtype, hipStream_t s);
-// x += sum of S fp32 partials [S][rows][D]; h = RMSNorm(x) * w as dtype.
+// fp32 partial sums [ksplit][rows][N].
+hipError_t launch_gemv16(const void* W, const void* x, float* out, int rows, int N, int K, int ksplit, int dtype,
+                         hipStream_t s);
+// act [rows][F] (dtype) = SiLU(gate) * up from S <= 8 fp32 partials
+// [S][rows][2F] of rows interleaved in blocks of 16 (16 gate, 16 up).
+hipError_t launch_swiglu(const float* part, int S, void* act, int rows, int F, int dtype, hipStream_t s);
+// x += sum of S <= 8 fp32 partials [S][rows][D]; h = RMSNorm(x) * w as dtype.
 hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w, void* h, int rows, int D, float eps,
                               int dtype, hipStream_t s);
 hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, hipStream_t s);
 hipError_t launch_attn_dec(const DecArgs& a, int n_items, int dtype, hipStream_t s);
-hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* next, hipStream_t s);
+// next[r] = first index of the largest logit; pv / pi: [rows][64] scratch.
+hipError_t launch_argmax(const float* logits, int rows, int V, float* pv, int* pi, int32_t* next, hipStream_t s);
 
 // Weight repacking (fp32 masters -> kernel layouts); dtype selects the
 // destination element type (DT_*).
