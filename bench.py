@@ -343,6 +343,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
+    ap.add_argument("--only", choices=["2x", "decoder"],
+                    help="run only this secondary measurement and print its JSON (for profiling)")
     ap.add_argument("--no-decoder", action="store_true",
                     help="skip the language-model decoder step")
     ap.add_argument("--no-2x", action="store_true",
@@ -391,6 +393,13 @@ def main():
     def step():
         W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream)
         W.mt_encode(enc, mel, lens_T, window, out=out, ws=ws_enc, stream=stream)
+
+    if args.only == "2x":
+        print(json.dumps(measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel)), flush=True)
+        return
+    if args.only == "decoder":
+        print(json.dumps(measure_decoder(W, synth, torch)), flush=True)
+        return
 
     if args.copy_probe:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
