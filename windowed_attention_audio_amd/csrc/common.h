@@ -30,17 +30,17 @@ __device__ __forceinline__ uint32_t pack2(T a, T b) {
 // z >= 0, |error| <= 1.5e-7.  With z = |x| / sqrt 2 and the coefficients
 // halved, h = erfc(z) / 2 is the tail mass of the normal law beyond |x|:
 // Phi(x) = 1 - h for x >= 0 and h for x < 0, so GELU = x - x h or x h.
-// Written so for few instructions (it runs on every element of conv1-3 and
-// fc1): one reciprocal, one exp2, nine other ops; |error| below 3.5e-7
-// (float32, measured against the exact erf form on [-12, 12]).
+// Both signs in one expression: x Phi(x) = x / 2 + |x| (1/2 - h).  Written
+// so for few instructions (it runs on every element of conv1-3 and fc1):
+// one reciprocal, one exp2, ten other ops, no compare or select; |error|
+// below 3.5e-7 (float32, measured against the exact erf form on [-12, 12]).
 __device__ __forceinline__ float gelu_f(float x) {
   const float t = __builtin_amdgcn_rcpf(fmaf(0.23164190f, fabsf(x), 1.0f));  // p / sqrt 2
   const float P =
       t * fmaf(fmaf(fmaf(fmaf(0.5307027145f, t, -0.726576013f), t, 0.7107068705f), t, -0.142248368f),
                t, 0.127414796f);
-  const float h = P * __builtin_amdgcn_exp2f(x * x * -0.72134752044f);  // exp(-x^2 / 2)
-  const float xh = x * h;
-  return x < 0.f ? xh : x - xh;
+  const float r = fmaf(-P, __builtin_amdgcn_exp2f(x * x * -0.72134752044f), 0.5f);  // 1/2 - h
+  return fmaf(fabsf(x), r, 0.5f * x);
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
