@@ -104,7 +104,7 @@ def forward(x, P, geom: dict, cache: list, n_layers=None):
     """New rows x [n, D] (token embeddings) continuing one sequence whose cache
     holds its earlier positions -> logits [n, vocab]; the cache is extended."""
     L = geom["n_layers"] if n_layers is None else n_layers
-    pos0 = cache[0]["K"].shape[0]
+    pos0 = cache[0]["K"].shape[0] if cache else 0  # a decoder of 0 layers keeps no cache
     x = np.asarray(x, dtype=np.float64)
     for l in range(L):
         x = layer_step(x, P, l, geom, cache[l], pos0)
