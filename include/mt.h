@@ -338,7 +338,8 @@ mt_status mt_decode_workspace_size(const mt_decoder* dec, int32_t n_rows, const 
  *           earlier call or by another row of this one (rows of one call
  *           write their K/V before any row attends).  A prompt is one call
  *           with positions 0 .. S-1; a decode step one row per sequence.
- *   cache   device KV cache of mt_decoder_cache_bytes(max_seqs, max_pos).
+ *   cache   device KV cache of mt_decoder_cache_bytes(max_seqs, max_pos)
+ *           (may be NULL for a decoder of 0 layers).
  *   logits  device fp32 [n_rows, vocab] (tied head on the final RMSNorm).
  *   next    device int32 [n_rows] or NULL: the first index of each row's
  *           largest logit.

@@ -214,3 +214,30 @@ def test_decode_step_graph_replays_match_eager(small_w):
         torch.cuda.synchronize()
         assert torch.equal(logits, eager), f"replay {i}"
         _ = (x * 2.0).sum().item()  # eager work between replays
+
+
+def test_zero_layer_decoder_is_the_tied_head(small_w):
+    geom = dict(SMALL, n_layers=0)
+    w = {k: v for k, v in small_w.items() if not k.startswith("layers.")}
+    P = {k: v.astype(np.float64) for k, v in w.items()}
+    x = OD.embed(np.arange(5) * 100, P)
+    g = GpuDecoder(geom, w, "f16", 1, 8)
+    gl, nx = g.step(x, [0] * 5, list(range(5)))
+    check_logits(gl, OD.forward(x, P, geom, OD.empty_cache(geom)), nx, "0-layer")
+
+
+def test_decode_rejections(small_w):
+    import torch
+    import windowed_attention_audio_amd as W
+    g = GpuDecoder(SMALL, small_w, "bf16", 2, 16)
+    x = torch.zeros((2, SMALL["d_model"]), dtype=torch.float32, device="cuda")
+    for seq, pos, what in (([0, 0], [3, 3], "duplicate (seq, pos)"), ([0, 2], [0, 0], "seq >= max_seqs"),
+                           ([0, 1], [0, 16], "pos >= max_pos"), ([0, -1], [0, 0], "negative seq")):
+        with pytest.raises(W.MtError) as e:
+            W.mt_decode(g.dec, x, seq, pos, g.cache, 2, 16)
+        assert e.value.status == W.MT_ERR_INVALID_ARG, what
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(W.MtError) as e:
+        W.mt_decode(g.dec, x, [0, 1], [0, 0], g.cache, 2, 16, ws=ws)
+    assert e.value.status == W.MT_ERR_WORKSPACE
+    torch.cuda.synchronize()

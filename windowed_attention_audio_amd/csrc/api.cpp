@@ -914,7 +914,8 @@ mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, co
   DecPlan p;
   mt_status st = plan_decode(dec, n_rows, seq, pos, max_seqs, max_pos, p);
   if (st != MT_OK) return st;
-  if (!x_in || !cache || !logits || !ws) return fail(MT_ERR_INVALID_ARG, "mt_decode: NULL device pointer");
+  if (!x_in || (!cache && dec->cfg.n_layers > 0) || !logits || !ws)
+    return fail(MT_ERR_INVALID_ARG, "mt_decode: NULL device pointer");
   if ((uintptr_t)ws % ALIGN || (uintptr_t)x_in % 16 || (uintptr_t)logits % 16 || (uintptr_t)cache % 16 ||
       (uintptr_t)next % 4)
     return fail(MT_ERR_INVALID_ARG, "mt_decode: misaligned pointer");
