@@ -252,7 +252,7 @@ def measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel, steps=10, warmup
             "step_tflops": round(fl / (ms * 1e-3) / 1e12, 1), "breakdown_ms_per_step": stages}
 
 
-def measure_decoder(W, synth, torch, ctx=400, batches=(1, 16), reps=20):
+def measure_decoder(W, synth, torch, ctx=400, batches=(1, 16, 64), reps=20):
     """The language-model decoder step (Qwen3-1.7B geometry, bf16 weights,
     seeded N(0, 0.02^2) weights drawn on the device) over B sequences whose
     KV cache holds a ctx-position prompt: ms per step eager and as a replayed

@@ -343,8 +343,8 @@ mt_status mt_decode_workspace_size(const mt_decoder* dec, int32_t n_rows, const 
  *   logits  device fp32 [n_rows, vocab] (tied head on the final RMSNorm).
  *   next    device int32 [n_rows] or NULL: the first index of each row's
  *           largest logit.
- * Up to 16 rows run the skinny matrix-vector kernels (the weights stream
- * once); more rows run the tiled products. */
+ * Up to 64 rows run the skinny matrix-vector kernels (the weights stream
+ * once for all rows); more rows run the tiled products. */
 mt_status mt_decode(const mt_decoder* dec, const float* x, int32_t n_rows, const int32_t* seq, const int32_t* pos,
                     void* cache, int32_t max_seqs, int32_t max_pos, float* logits, int32_t* next, void* ws,
                     size_t ws_bytes, void* stream);

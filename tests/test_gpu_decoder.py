@@ -241,3 +241,26 @@ def test_decode_rejections(small_w):
         W.mt_decode(g.dec, x, [0, 1], [0, 0], g.cache, 2, 16, ws=ws)
     assert e.value.status == W.MT_ERR_WORKSPACE
     torch.cuda.synchronize()
+
+
+def test_small_wide_decode_batch(small_w):
+    """40 sequences: 3-row prompts in one call (tiled path), then a 40-row
+    decode step (skinny path, three 16-row tiles sharing weight fragments):
+    the oracle per sequence, and bitwise equality with a one-row step."""
+    P = {k: v.astype(np.float64) for k, v in small_w.items()}
+    B = 40
+    rng = np.random.default_rng(9)
+    xs = [OD.embed(rng.integers(0, SMALL["vocab"], 4), P) for _ in range(B)]
+    g = GpuDecoder(SMALL, small_w, "bf16", B, 8)
+    say("decoder small: 40 prompts of 3 rows, then a 40-row step")
+    g.step(np.concatenate([x[:3] for x in xs]), sum(([s] * 3 for s in range(B)), []), [0, 1, 2] * B)
+    snap = g.cache.clone()
+    gl, nx = g.step(np.stack([x[3] for x in xs]), list(range(B)), [3] * B)
+    caches = [OD.empty_cache(SMALL) for _ in range(B)]
+    for s in range(B):
+        OD.forward(xs[s][:3], P, SMALL, caches[s])
+    ref = np.concatenate([OD.forward(xs[s][3:4], P, SMALL, caches[s]) for s in range(B)])
+    check_logits(gl, ref, nx, "40-row step")
+    g.cache.copy_(snap)
+    l1, n1 = g.step(xs[17][3:4], [17], [3])
+    assert np.array_equal(l1[0], gl[17]) and n1[0] == nx[17]

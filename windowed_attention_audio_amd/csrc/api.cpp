@@ -774,7 +774,7 @@ mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, cons
   p.words.insert(p.words.end(), first.begin(), first.end());
   const size_t D = c.d_model, F = c.d_ffn, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
   const size_t NQKV = (Hq + 2 * Hkv) * hd, NQ = Hq * hd;
-  p.gemv = n <= 16;
+  p.gemv = n <= GEMV_MAX_ROWS;
   if (p.gemv) {
     p.s_qkv = gemv_split((int)NQKV, (int)D);
     p.s_o = gemv_split((int)D, (int)NQ);

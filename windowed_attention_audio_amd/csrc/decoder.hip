@@ -4,10 +4,11 @@
 // NEOX rotary positions base 1e6, tied embeddings).
 //
 // A decode step reads every weight once for a handful of rows: the products
-// are HBM-bound matrix-vector work.  The skinny product (at most 16 rows)
-// runs on the matrix cores anyway -- one 16 x 16 x 32 step per 16 weight rows
-// and 32 columns, the weight fragments loaded straight from memory -- so the
-// vector units stay free and 16 rows cost what one does.  K is split across
+// are HBM-bound matrix-vector work.  The skinny product (at most 64 rows)
+// runs on the matrix cores anyway -- one 16 x 16 x 32 step per 16 weight rows,
+// 32 columns and 16 rows, the weight fragments loaded straight from memory
+// once for up to four row tiles -- so the vector units stay free and 64 rows
+// cost little more than one.  K is split across
 // wavefronts so that each product keeps enough loads in flight; the partial
 // sums land in fixed slots and their consumers add them in order (no
 // atomics: results do not depend on timing).
@@ -45,15 +46,16 @@ __device__ __forceinline__ float wmax64(float v) {
 }
 
 // ---------------------------------------------------------------- skinny GEMV
-// out[s][r][n] = sum_{k in split s} x[r][k] W[n][k] for r < rows (<= 16).
+// out[s][r][n] = sum_{k in split s} x[r][k] W[n][k] for r < rows (<= 64).
 // One wavefront per (16 weight rows, K split); lane (g, l16) loads weight
 // row n0 + l16, columns k + 8g .. k + 8g + 7 (16 bytes) and the same columns
-// of x row l16.  The MFMA is issued as B = weights, A = x, so the lane holds
-// out[x row l16][n0 + 4g .. n0 + 4g + 3].
+// of x rows 16 q + l16.  The MFMA is issued as B = weights, A = x, so the
+// lane holds out[x row 16 q + l16][n0 + 4g .. n0 + 4g + 3].
 // Output: fp32 partial sums [S][rows][N].  U K steps are loaded before the
 // first MFMA: U covers a wavefront's whole K range (one round trip to
-// memory) up to 32 steps.
-template <typename T, int U>
+// memory) up to 32 steps.  RT tiles of 16 x rows (rows <= 16 RT) share each
+// weight fragment: up to 64 rows cost about what 16 do.
+template <typename T, int U, int RT>
 __global__ __launch_bounds__(256) void gemv16_kernel(const T* __restrict__ W, const T* __restrict__ x,
                                                      float* __restrict__ out, int rows, int N, int K, int ksplit) {
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
@@ -63,24 +65,38 @@ __global__ __launch_bounds__(256) void gemv16_kernel(const T* __restrict__ W, co
   if (s >= ksplit) return;
   const int n0 = blk * 16;
   const int kl = K / ksplit, k0 = s * kl;
-  const bool xr = l16 < rows;
   const T* wp = W + (int64_t)(n0 + l16) * K + k0 + 8 * g;
-  const T* xp = x + (int64_t)(xr ? l16 : 0) * K + k0 + 8 * g;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const T* xp[RT];
+  bool xr[RT];
+#pragma unroll
+  for (int q = 0; q < RT; ++q) {
+    xr[q] = 16 * q + l16 < rows;
+    xp[q] = x + (int64_t)(xr[q] ? 16 * q + l16 : 0) * K + k0 + 8 * g;
+  }
+  f32x4 acc[RT];
+#pragma unroll
+  for (int q = 0; q < RT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < kl; k += 32 * U) {
-    uint4 wa[U], xa[U];
+    uint4 wa[U], xa[RT][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = k + 32 * u < kl;
       wa[u] = in ? *(const uint4*)(wp + k + 32 * u) : make_uint4(0, 0, 0, 0);
-      xa[u] = (in && xr) ? *(const uint4*)(xp + k + 32 * u) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < RT; ++q)
+        xa[q][u] = (in && xr[q]) ? *(const uint4*)(xp[q] + k + 32 * u) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) mma16(acc, wa[u], xa[u], T{});
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < RT; ++q) mma16(acc[q], wa[u], xa[q][u], T{});
   }
-  if (!xr) return;
-  float* o = out + ((int64_t)s * rows + l16) * N + n0 + 4 * g;
-  *(float4*)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+  for (int q = 0; q < RT; ++q) {
+    if (!xr[q]) continue;
+    float* o = out + ((int64_t)s * rows + 16 * q + l16) * N + n0 + 4 * g;
+    *(float4*)o = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+  }
 }
 
 // --------------------------------------------------- residual add + RMSNorm
@@ -403,25 +419,40 @@ __global__ __launch_bounds__(64) void argmax_final_kernel(const float* __restric
 
 hipError_t launch_gemv16(const void* W, const void* x, float* out, int rows, int N, int K, int ksplit, int dtype,
                          hipStream_t s) {
-  if (rows < 1 || rows > 16 || ksplit < 1 || K % (32 * ksplit) || N % 16) return hipErrorInvalidValue;
+  if (rows < 1 || rows > GEMV_MAX_ROWS || ksplit < 1 || K % (32 * ksplit) || N % 16) return hipErrorInvalidValue;
+  if (dtype != DT_BF16 && dtype != DT_F16) return hipErrorInvalidValue;
   const int waves = (N / 16) * ksplit;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   const int steps = K / ksplit / 32;
-  auto go = [&](auto u) {
-    constexpr int U = decltype(u)::value;
+  const int rt = (rows + 15) / 16;
+  auto go = [&](auto u, auto r) {
+    constexpr int U = decltype(u)::value, RT = decltype(r)::value;
     if (dtype == DT_BF16)
-      hipLaunchKernelGGL((gemv16_kernel<bf16_t, U>), grid, block, 0, s, (const bf16_t*)W, (const bf16_t*)x, out, rows,
-                         N, K, ksplit);
+      hipLaunchKernelGGL((gemv16_kernel<bf16_t, U, RT>), grid, block, 0, s, (const bf16_t*)W, (const bf16_t*)x, out,
+                         rows, N, K, ksplit);
     else
-      hipLaunchKernelGGL((gemv16_kernel<f16_t, U>), grid, block, 0, s, (const f16_t*)W, (const f16_t*)x, out, rows, N,
-                         K, ksplit);
+      hipLaunchKernelGGL((gemv16_kernel<f16_t, U, RT>), grid, block, 0, s, (const f16_t*)W, (const f16_t*)x, out,
+                         rows, N, K, ksplit);
   };
-  if (dtype != DT_BF16 && dtype != DT_F16) return hipErrorInvalidValue;
-  if (steps <= 8) go(std::integral_constant<int, 8>{});
-  else if (steps <= 16) go(std::integral_constant<int, 16>{});
-  else if (steps <= 24) go(std::integral_constant<int, 24>{});
-  else if (steps <= 32) go(std::integral_constant<int, 32>{});
-  else go(std::integral_constant<int, 8>{});
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using U8 = std::integral_constant<int, 8>;
+  using U16 = std::integral_constant<int, 16>;
+  using U24 = std::integral_constant<int, 24>;
+  using U32 = std::integral_constant<int, 32>;
+  if (rt == 1) {  // one row tile: unroll to the wavefront's whole K range
+    if (steps <= 8) go(U8{}, I1{});
+    else if (steps <= 16) go(U16{}, I1{});
+    else if (steps <= 24) go(U24{}, I1{});
+    else if (steps <= 32) go(U32{}, I1{});
+    else go(U8{}, I1{});
+  } else if (rt == 2) {  // x fragments of two row tiles: at most 16 steps in registers
+    if (steps <= 8) go(U8{}, I2{});
+    else go(U16{}, I2{});
+  } else {
+    go(U8{}, I4{});
+  }
   return hipGetLastError();
 }
 

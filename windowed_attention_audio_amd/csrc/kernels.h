@@ -149,8 +149,9 @@ struct DecArgs {
   float* part_ml;        // [n_items][Hkv][2][2] (chunk max, chunk sum)
   void* o16;             // [rows][Hq][128] attention output (16-bit)
 };
-// out = x W^T for at most 16 rows of x (16-bit [rows][K]), W 16-bit [N][K]:
-// fp32 partial sums [ksplit][rows][N].
+// out = x W^T for at most GEMV_MAX_ROWS rows of x (16-bit [rows][K]), W 16-bit
+// [N][K]: fp32 partial sums [ksplit][rows][N].
+constexpr int GEMV_MAX_ROWS = 64;
 hipError_t launch_gemv16(const void* W, const void* x, float* out, int rows, int N, int K, int ksplit, int dtype,
                          hipStream_t s);
 // act [rows][F] (dtype) = SiLU(gate) * up from S <= 8 fp32 partials
