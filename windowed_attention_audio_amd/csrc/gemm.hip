@@ -1018,15 +1018,29 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
     }
   }
 
+  // This lane's K column k = kb * 32 + c * 8 as (tap, channel): slices are
+  // issued in order (kb = 0, 1, 2, ...), so the pair is carried forward by
+  // 32 columns per call (C >= 32: one wrap at most) instead of divided out.
+  [[maybe_unused]] int cv_k = c * 8, cv_tap = 0, cv_ch = c * 8;
+  if constexpr (CONV) {
+    cv_tap = cv_k / a.conv_C;
+    cv_ch = cv_k - cv_tap * a.conv_C;
+  }
   auto issue = [&](uint4* stage, int kb) {
+    (void)kb;
     int cdelta = 0;
     uint32_t need = 0;
     if constexpr (CONV) {
-      const int k = kb * 32 + c * 8;  // first column of this lane's chunk
-      const int tap = k / a.conv_C, ch = k - tap * a.conv_C;
-      const int df = one_d ? 1 : tap / 3, dt = one_d ? tap : tap - 3 * df;
+      const int tap = cv_tap, ch = cv_ch;
+      const int df = one_d ? 1 : (tap * 11) >> 5, dt = one_d ? tap : tap - 3 * df;  // tap / 3 for tap < 9
       cdelta = ((dt - 1) * a.conv_Fin + (df - 1)) * a.conv_C * (int)sizeof(T) + ch * (int)sizeof(T);
-      need = k < a.K ? (1u << dt) | (8u << df) : 0xffffffffu;  // past K: never satisfied
+      need = cv_k < a.K ? (1u << dt) | (8u << df) : 0xffffffffu;  // past K: never satisfied
+      cv_k += 32;
+      cv_ch += 32;
+      if (cv_ch >= a.conv_C) {
+        cv_ch -= a.conv_C;
+        ++cv_tap;
+      }
     }
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
@@ -1175,7 +1189,7 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
     // gather, 256 x 160 tiles of 64 x 80 wavefronts (480 output channels =
     // 3 tiles; the 256 x 256 variant spills with the gather's per-row state).
     if constexpr (CONV) {
-      if (a.conv_C % 8 == 0 && (int64_t)a.N * a.ldb * 2 < (1ll << 31))
+      if (a.conv_C % 8 == 0 && a.conv_C >= 32 && (int64_t)a.N * a.ldb * 2 < (1ll << 31))
         return run_w8q<T, 160, EPI, 4, true>(a, s);
     }
     if (CONV && a.conv_kind != CONV_2D_S2) return hipErrorInvalidValue;  // 1-D: that kernel only
