@@ -1227,7 +1227,13 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
         return run_w8<T, 256, EPI>(a, s);
       if (w8 && a.M >= 2048) return run_w8q<T, 128, EPI, 4>(a, s);
       if (a.M >= 2048) return run_lds<T, 256, 128, 4, 2, 2, EPI, CONV>(a, s);
-      return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
+      // Few rows (a single clip, a stream chunk, a decoder prompt): 128 x 128
+      // tiles only when there are enough of them for the CUs, else 64 x 64
+      // (measured: M = 375, N = 1280, K = 1280 17.7 -> 8.9 us; M = 832,
+      // N = 1280, K = 5120 67.3 -> 42.0 us; M = 832, N = 5120: 128 x 128
+      // stays ahead with 280 tiles).
+      if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 256) return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
+      return run_lds<T, 64, 64, 2, 2, 2, EPI, CONV>(a, s);
     }
   }
   if constexpr (CONV) {
