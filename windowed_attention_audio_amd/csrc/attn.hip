@@ -153,10 +153,10 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
             const uint4 vf = *(const uint4*)(vrow + 32 * u + 8 * g);
             typedef Elem<T> E;
             uint4 pf;
-            pf.x = pack2(E::from_f(st[2 * u][0]), E::from_f(st[2 * u][1]));
-            pf.y = pack2(E::from_f(st[2 * u][2]), E::from_f(st[2 * u][3]));
-            pf.z = pack2(E::from_f(st[2 * u + 1][0]), E::from_f(st[2 * u + 1][1]));
-            pf.w = pack2(E::from_f(st[2 * u + 1][2]), E::from_f(st[2 * u + 1][3]));
+            pf.x = pack2f<T>(st[2 * u][0], st[2 * u][1]);
+            pf.y = pack2f<T>(st[2 * u][2], st[2 * u][3]);
+            pf.z = pack2f<T>(st[2 * u + 1][0], st[2 * u + 1][1]);
+            pf.w = pack2f<T>(st[2 * u + 1][2], st[2 * u + 1][3]);
             mma16(o[nd], vf, pf, T{});
           }
         } else {
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
         if constexpr (sizeof(T) == 2) {
           typedef Elem<T> E;
           uint2 pk;
-          pk.x = pack2(E::from_f(o[nd][0] * inv), E::from_f(o[nd][1] * inv));
-          pk.y = pack2(E::from_f(o[nd][2] * inv), E::from_f(o[nd][3] * inv));
+          pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
+          pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);
           *(uint2*)(orow + d0) = pk;
         } else {
           *(float4*)(orow + d0) =
@@ -278,10 +278,10 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     uint4 pf;
-    pf.x = pack2((T)st[2 * u][0], (T)st[2 * u][1]);
-    pf.y = pack2((T)st[2 * u][2], (T)st[2 * u][3]);
-    pf.z = pack2((T)st[2 * u + 1][0], (T)st[2 * u + 1][1]);
-    pf.w = pack2((T)st[2 * u + 1][2], (T)st[2 * u + 1][3]);
+    pf.x = pack2_cast<T>(st[2 * u][0], st[2 * u][1]);
+    pf.y = pack2_cast<T>(st[2 * u][2], st[2 * u][3]);
+    pf.z = pack2_cast<T>(st[2 * u + 1][0], st[2 * u + 1][1]);
+    pf.w = pack2_cast<T>(st[2 * u + 1][2], st[2 * u + 1][3]);
     const int r1 = r0 + 32 * u + 4 * g + (l16 >> 2), r2 = r1 + 16;
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) {
@@ -374,8 +374,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void w
         const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
         typedef Elem<T> E;
         uint2 pk;
-        pk.x = pack2(E::from_f(o[nd][0] * inv), E::from_f(o[nd][1] * inv));
-        pk.y = pack2(E::from_f(o[nd][2] * inv), E::from_f(o[nd][3] * inv));
+        pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
+        pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);
         *(uint2*)(orow + d0) = pk;
       }
     }
@@ -486,8 +486,8 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
       const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
       typedef Elem<T> E;
       uint2 pk;
-      pk.x = pack2(E::from_f(o[nd][0] * inv), E::from_f(o[nd][1] * inv));
-      pk.y = pack2(E::from_f(o[nd][2] * inv), E::from_f(o[nd][3] * inv));
+      pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
+      pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);
       *(uint2*)(orow + d0) = pk;
     }
   }

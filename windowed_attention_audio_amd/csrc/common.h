@@ -24,6 +24,26 @@ __device__ __forceinline__ uint32_t pack2(T a, T b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// pack2((T)a, (T)b) as one v_cvt_pk_{f16,bf16}_f32 (round to nearest even)
+// instead of two conversions and a shift-or.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2_cast(float a, float b) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef T t2v __attribute__((ext_vector_type(2)));
+  const f2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, t2v));
+}
+
+// pack2(from_f(a), from_f(b)) in one packed conversion: fp16 saturates at
+// +-65504 first, bf16 converts as is.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2f(float a, float b) {
+  if constexpr (__is_same(T, _Float16))
+    return pack2_cast<T>(fminf(fmaxf(a, -65504.0f), 65504.0f), fminf(fmaxf(b, -65504.0f), 65504.0f));
+  else
+    return pack2_cast<T>(a, b);
+}
+
 // GELU with the erf form, x Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2.
 // erfc after Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
 // erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z),

@@ -61,10 +61,10 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
     }
     if constexpr (sizeof(T) == 2) {
       uint4 v;
-      v.x = pack2(Elem<T>::from_f(y[0]), Elem<T>::from_f(y[1]));
-      v.y = pack2(Elem<T>::from_f(y[2]), Elem<T>::from_f(y[3]));
-      v.z = pack2(Elem<T>::from_f(y[4]), Elem<T>::from_f(y[5]));
-      v.w = pack2(Elem<T>::from_f(y[6]), Elem<T>::from_f(y[7]));
+      v.x = pack2f<T>(y[0], y[1]);
+      v.y = pack2f<T>(y[2], y[3]);
+      v.z = pack2f<T>(y[4], y[5]);
+      v.w = pack2f<T>(y[6], y[7]);
       *(uint4*)(out + (int64_t)f1 * a.C) = v;
     } else {
       float4* o = (float4*)(out + (int64_t)f1 * a.C);

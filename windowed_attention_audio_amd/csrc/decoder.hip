@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
       } else {
         typedef Elem<T> E;
         ((uint2*)((T*)h + (int64_t)r * D))[c] =
-            make_uint2(pack2(E::from_f(y0), E::from_f(y1)), pack2(E::from_f(y2), E::from_f(y3)));
+            make_uint2(pack2f<T>(y0, y1), pack2f<T>(y2, y3));
       }
     }
   }

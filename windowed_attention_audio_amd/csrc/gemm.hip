@@ -59,7 +59,7 @@ __device__ __forceinline__ void store4(T* p, float v0, float v1, float v2, float
     *(float4*)p = make_float4(v0, v1, v2, v3);
   } else {
     typedef Elem<T> E;
-    *(uint2*)p = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
+    *(uint2*)p = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
   }
 }
 
@@ -576,7 +576,7 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
         v3 = gelu_f(v3);
       }
       typedef Elem<T> E;
-      const uint2 w = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
+      const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
       *(uint2*)(qb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }
   }
@@ -640,7 +640,7 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
         v3 = gelu_f(v3);
       }
       typedef Elem<T> E;
-      const uint2 w = make_uint2(pack2(E::from_f(v0), E::from_f(v1)), pack2(E::from_f(v2), E::from_f(v3)));
+      const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
       *(uint2*)(hb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }
   }
