@@ -256,10 +256,23 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
   }
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  // Lazy rescaling: the reference maximum m_run moves (and the running sum
+  // and the output accumulators are scaled down to it) only when some query
+  // of the wavefront has gained more than a factor 2^8 over it -- always in
+  // the first chunk (m_run = -inf), rarely after.  Otherwise the
+  // probabilities stay relative to the old reference, below 2^8, which the
+  // 16-bit operand types hold at the same relative precision as values
+  // below 1; the final division by the sum cancels the reference.  The
+  // decision is per wavefront, so the branch is uniform.
   const float m_new = fmaxf(m_run, cmax);
-  const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
-  const float mb = -m_new * sl2;
-  m_run = m_new;
+  if (__any((m_new - m_run) * sl2 > 8.0f)) {
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
+    m_run = m_new;
+    l_part *= alpha;
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
+  }
+  const float mb = -m_run * sl2;
   float psum = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -269,12 +282,10 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
       st[t][e] = p;
       psum += p;
     }
-  l_part = l_part * alpha + psum;
-#pragma unroll
-  for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
+  l_part += psum;
 
-  // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]; probabilities lie in [0, 1]:
-  // plain round-to-nearest-even conversions, no clamp
+  // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]; probabilities lie in
+  // [0, 2^8]: plain round-to-nearest-even conversions, no clamp
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     uint4 pf;
