@@ -722,6 +722,10 @@ int gemv_split(int N, int K) {
 struct DecPlan {
   int n = 0, n_items = 0, s_qkv = 1, s_o = 1, s_gu = 1, s_d = 1;
   bool gemv = true;
+  // at most GEMV_FUSE_ROWS rows: the down projection computes its SwiGLU
+  // input, the output projection combines the attention chunks itself
+  bool fuse_d = false, fuse_o = false;
+  int cmax = 0;  // most chunks of any row
   std::vector<int32_t> words;  // seq | pos | items | first_item
   size_t o_words, o_x, o_h, o_qkv, o_qf, o_po, o_pml, o_o16, o_opart, o_gu, o_act, o_dpart, o_amv, o_ami, bytes;
 };
@@ -784,6 +788,13 @@ mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, cons
     p.s_qkv = 1;
     p.s_gu = 0;
     p.s_o = p.s_d = 0;  // the matrix kernels add into the residual stream
+  }
+  if (p.gemv && n <= GEMV_FUSE_ROWS && D % 64 == 0) {
+    for (int i = 0; i < n; ++i) p.cmax = std::max(p.cmax, first[i + 1] - first[i]);
+    const size_t kld = F / p.s_d, klo = NQ / p.s_o;
+    p.fuse_d = kld % 32 == 0 && kld <= 1024 && n * kld * 2 <= 65536;
+    p.fuse_o = klo % hd == 0 && klo <= 1024 && p.cmax <= 64 &&
+               n * klo * 2 + n * (klo / hd) * (2 + 3 * p.cmax) * 4 <= 65536;
   }
   Carver k;
   p.o_words = k.take(4 * p.words.size());
@@ -973,8 +984,10 @@ mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, co
       STAGE(launch_gemm(gemm_(h, D, L.wqkv, n, NQKV, D, qkv, NQKV), EPI_F32, dt, false, s), "dec_qkv");
     }
     STAGE(launch_qk_rope(a, qkv, p.s_qkv, dt, s), "dec_qk_rope");
-    STAGE(launch_attn_dec(a, p.n_items, dt, s), "dec_attn");
-    if (p.gemv) {
+    STAGE(launch_attn_dec(a, p.n_items, !p.fuse_o, dt, s), "dec_attn");
+    if (p.fuse_o) {
+      STAGE(launch_gemv16x(L.wo, 2, nullptr, 0, a, p.cmax, opart, n, D, NQ, p.s_o, dt, s), "dec_o");
+    } else if (p.gemv) {
       STAGE(launch_gemv16(L.wo, a.o16, opart, n, D, NQ, p.s_o, dt, s), "dec_o");
     } else {
       STAGE(launch_gemm(gemm_(a.o16, NQ, L.wo, n, D, NQ, x, D), EPI_RESID, dt, false, s), "dec_o");
@@ -982,8 +995,13 @@ mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, co
     STAGE(launch_add_rmsnorm(x, opart, p.s_o, L.post_norm, h, n, D, c.rms_eps, dt, s), "rmsnorm");
     if (p.gemv) {
       STAGE(launch_gemv16(L.wgu, h, (float*)(w + p.o_gu), n, 2 * F, D, p.s_gu, dt, s), "dec_gate_up");
-      STAGE(launch_swiglu((const float*)(w + p.o_gu), p.s_gu, act, n, F, dt, s), "dec_swiglu");
-      STAGE(launch_gemv16(L.wd, act, dpart, n, D, F, p.s_d, dt, s), "dec_down");
+      if (p.fuse_d) {
+        STAGE(launch_gemv16x(L.wd, 1, (const float*)(w + p.o_gu), p.s_gu, a, 0, dpart, n, D, F, p.s_d, dt, s),
+              "dec_down");
+      } else {
+        STAGE(launch_swiglu((const float*)(w + p.o_gu), p.s_gu, act, n, F, dt, s), "dec_swiglu");
+        STAGE(launch_gemv16(L.wd, act, dpart, n, D, F, p.s_d, dt, s), "dec_down");
+      }
     } else {
       STAGE(launch_gemm(gemm_(h, D, L.wgu, n, 2 * F, D, act, F), EPI_SWIGLU, dt, false, s), "dec_gate_up");
       STAGE(launch_gemm(gemm_(act, F, L.wd, n, D, F, x, D), EPI_RESID, dt, false, s), "dec_down");

@@ -151,7 +151,6 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const uint4 vf = *(const uint4*)(vrow + 32 * u + 8 * g);
-            typedef Elem<T> E;
             uint4 pf;
             pf.x = pack2f<T>(st[2 * u][0], st[2 * u][1]);
             pf.y = pack2f<T>(st[2 * u][2], st[2 * u][3]);
@@ -180,7 +179,6 @@ __global__ __launch_bounds__(256) void wattn_kernel(AttnArgs a) {
       for (int nd = 0; nd < 4; ++nd) {
         const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
         if constexpr (sizeof(T) == 2) {
-          typedef Elem<T> E;
           uint2 pk;
           pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
           pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);
@@ -383,7 +381,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void w
 #pragma unroll
       for (int nd = 0; nd < 4; ++nd) {
         const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
-        typedef Elem<T> E;
         uint2 pk;
         pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
         pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);
@@ -495,7 +492,6 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) {
       const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
-      typedef Elem<T> E;
       uint2 pk;
       pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
       pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);

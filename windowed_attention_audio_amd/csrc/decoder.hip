@@ -150,7 +150,6 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
       if constexpr (sizeof(T) == 4) {
         ((float4*)((float*)h + (int64_t)r * D))[c] = make_float4(y0, y1, y2, y3);
       } else {
-        typedef Elem<T> E;
         ((uint2*)((T*)h + (int64_t)r * D))[c] =
             make_uint2(pack2f<T>(y0, y1), pack2f<T>(y2, y3));
       }
@@ -160,12 +159,10 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
 
 // SwiGLU of the gate/up partial sums: act[r][f] = SiLU(sum g) * (sum u), gate
 // row 32 (f / 16) + f % 16 and up row 32 (f / 16) + 16 + f % 16 of the [S][rows]
-// [2F] partials.
+// [2F] partials.  One function for the standalone pass and for the fused
+// load of the down projection, so that both give the same bits.
 template <typename T>
-__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, T* __restrict__ act,
-                                                     int rows, int F) {
-  const int r = blockIdx.y, f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
+__device__ __forceinline__ T swiglu_one(const float* __restrict__ part, int S, int rows, int F, int r, int f) {
   const int gi = 32 * (f >> 4) + (f & 15);
   float gp[MAXS], up[MAXS];
 #pragma unroll
@@ -182,7 +179,15 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
       g += gp[s2];
       u += up[s2];
     }
-  act[(int64_t)r * F + f] = Elem<T>::from_f(silu_f(g) * u);
+  return Elem<T>::from_f(silu_f(g) * u);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, T* __restrict__ act,
+                                                     int rows, int F) {
+  const int r = blockIdx.y, f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= F) return;
+  act[(int64_t)r * F + f] = swiglu_one<T>(part, S, rows, F, r, f);
 }
 
 // ------------------------------------------- Q/K-norm, rotation, cache append
@@ -352,23 +357,130 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
   }
 }
 
-// One workgroup of 128 threads per (row, query head): combine the row's chunk
-// partials (chunks first_item[r] .. first_item[r + 1] - 1) into o16.
+// Combining a row's chunk partials for query head hq (kv head hq / 2, head
+// h = hq % 2 of the group; chunks first_item[r] .. first_item[r + 1] - 1):
+// M = max m_i, f_i = exp(m_i - M), L = sum l_i f_i, o[d] = sum o_i[d] f_i,
+// out = o / L.  These helpers are shared by the standalone combine and the
+// fused load of the output projection, so that both give the same bits.
+__device__ __forceinline__ int64_t combine_slot(const DecArgs& a, int i, int hq) {
+  return ((int64_t)i * a.Hkv + (hq >> 1)) * 2 + (hq & 1);
+}
+__device__ __forceinline__ float combine_max(const DecArgs& a, int r, int hq) {
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int i = a.first_item[r]; i < a.first_item[r + 1]; ++i) M = fmaxf(M, a.part_ml[2 * combine_slot(a, i, hq)]);
+  return M;
+}
+__device__ __forceinline__ float combine_f(const DecArgs& a, int i, int hq, float M) {
+  return __expf(a.part_ml[2 * combine_slot(a, i, hq)] - M);
+}
+
+// One workgroup of 128 threads per (row, query head).
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(DecArgs a) {
   const int r = blockIdx.x, hq = blockIdx.y, d = threadIdx.x;
-  const int kh = hq >> 1, h = hq & 1;
-  const int i0 = a.first_item[r], i1 = a.first_item[r + 1];
-  float M = -INFINITY;
-  for (int i = i0; i < i1; ++i) M = fmaxf(M, a.part_ml[2 * (((int64_t)i * a.Hkv + kh) * 2 + h)]);
+  const float M = combine_max(a, r, hq);
   float L = 0.f, o = 0.f;
-  for (int i = i0; i < i1; ++i) {
-    const int64_t slot = ((int64_t)i * a.Hkv + kh) * 2 + h;
-    const float f = __expf(a.part_ml[2 * slot] - M);
+#pragma unroll 8
+  for (int i = a.first_item[r]; i < a.first_item[r + 1]; ++i) {
+    const int64_t slot = combine_slot(a, i, hq);
+    const float f = combine_f(a, i, hq, M);
     L += a.part_ml[2 * slot + 1] * f;
     o += a.part_o[slot * HD + d] * f;
   }
   ((T*)a.o16)[((int64_t)r * a.Hq + hq) * HD + d] = Elem<T>::from_f(o / L);
+}
+
+// ------------------------------------------ skinny GEMV with a computed x
+// The same product for at most GEMV_FUSE_ROWS rows whose x is computed from
+// its producer's partials instead of being stored first: XM = 1, SwiGLU of
+// the gate/up partials (src, S splits) for the down projection; XM = 2, the
+// attention chunk partials combined for the output projection.  The four
+// wavefronts of a workgroup share one K range (N is a multiple of 64): the
+// workgroup computes x[rows][k0, k0 + kl) once into LDS with the standalone
+// passes' helpers (so the bits are the same), then each wavefront reads its
+// fragments from there.  This saves the producer's launch; the price, every
+// workgroup of a split recomputing the same x, stays small at a few rows.
+// The weight fragments of the whole K range (kl <= 32 U) are requested
+// first, so their latency covers the x computation.
+//   dynamic LDS: x [rows][kl] (16-bit), then for XM = 2 per (row, head) of
+//   the range 2 + 3 cmax floats: L, unused, f_i and (m_i, l_i) of each chunk.
+template <typename T, int U, int XM>
+__global__ __launch_bounds__(256) void gemv16x_kernel(const T* __restrict__ W, const float* __restrict__ src, int S,
+                                                      DecArgs a, int cmax, float* __restrict__ out, int rows, int N,
+                                                      int K, int ksplit) {
+  extern __shared__ uint4 smem_x[];
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const int nblk = N / 16;
+  const int s = blockIdx.x * 4 / nblk, blk = blockIdx.x * 4 + (threadIdx.x >> 6) - s * nblk;
+  const int kl = K / ksplit, k0 = s * kl;
+  const int n0 = blk * 16;
+  const T* wp = W + (int64_t)(n0 + l16) * K + k0 + 8 * g;
+  uint4 wa[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) wa[u] = 32 * u < kl ? *(const uint4*)(wp + 32 * u) : make_uint4(0, 0, 0, 0);
+
+  T* xs = (T*)smem_x;
+  if constexpr (XM == 1) {
+    for (int i = threadIdx.x; i < rows * kl; i += 256) {
+      const int r = i / kl;
+      xs[i] = swiglu_one<T>(src, S, rows, K, r, k0 + i - r * kl);
+    }
+  } else {
+    // Every chunk's (max, sum) of the workgroup's (row, head) pairs is
+    // fetched at once (a loop per pair would wait for one load at a time),
+    // then one thread per pair forms M, the weights f_i and L from LDS, in
+    // the standalone combine's order.
+    const int nhl = kl / HD, h0 = k0 / HD;  // query heads of this K range
+    const int cs = 2 + 3 * cmax;            // floats per pair: L, -, f[cmax], (m, l)[cmax]
+    float* cw = (float*)(xs + rows * kl);   // [rows][nhl][cs]
+    for (int idx = threadIdx.x; idx < rows * nhl * cmax; idx += 256) {
+      const int pair = idx / cmax, i = idx - pair * cmax, r = pair / nhl;
+      const int i0 = a.first_item[r];
+      if (i0 + i < a.first_item[r + 1]) {
+        const int64_t slot = combine_slot(a, i0 + i, h0 + pair % nhl);
+        float* c = cw + pair * cs + 2 + cmax + 2 * i;
+        c[0] = a.part_ml[2 * slot];
+        c[1] = a.part_ml[2 * slot + 1];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < rows * nhl) {
+      const int r = threadIdx.x / nhl;
+      float* c = cw + threadIdx.x * cs;
+      const float* ml = c + 2 + cmax;
+      const int nch = a.first_item[r + 1] - a.first_item[r];
+      float M = -INFINITY;
+      for (int i = 0; i < nch; ++i) M = fmaxf(M, ml[2 * i]);
+      float L = 0.f;
+      for (int i = 0; i < nch; ++i) {
+        const float f = __expf(ml[2 * i] - M);
+        L += ml[2 * i + 1] * f;
+        c[2 + i] = f;
+      }
+      c[0] = L;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows * kl; i += 256) {
+      const int r = i / kl, k = k0 + i - r * kl, hq = k / HD, d = k % HD;
+      const float* c = cw + (r * nhl + hq - h0) * cs;
+      const int i0 = a.first_item[r], nch = a.first_item[r + 1] - i0;
+      float o = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < nch; ++j) o += a.part_o[combine_slot(a, i0 + j, hq) * HD + d] * c[2 + j];
+      xs[i] = Elem<T>::from_f(o / c[0]);
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool xr = l16 < rows;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint4 xa = (xr && 32 * u < kl) ? *(const uint4*)(xs + l16 * kl + 32 * u + 8 * g) : make_uint4(0, 0, 0, 0);
+    mma16(acc, wa[u], xa, T{});
+  }
+  if (xr) *(float4*)(out + ((int64_t)s * rows + l16) * N + n0 + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 // ------------------------------------------------------------- argmax
@@ -477,18 +589,56 @@ hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_dec(const DecArgs& a, int n_items, int dtype, hipStream_t s) {
+hipError_t launch_attn_dec(const DecArgs& a, int n_items, bool combine, int dtype, hipStream_t s) {
   if (a.Hq != 2 * a.Hkv) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_items, (unsigned)a.Hkv);
+  const dim3 cgrid((unsigned)a.rows, (unsigned)a.Hq);
   if (dtype == DT_BF16) {
     hipLaunchKernelGGL(attn_dec_kernel<bf16_t>, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3((unsigned)a.rows, (unsigned)a.Hq), dim3(128), 0, s, a);
+    if (combine) hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, cgrid, dim3(128), 0, s, a);
   } else if (dtype == DT_F16) {
     hipLaunchKernelGGL(attn_dec_kernel<f16_t>, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_combine_kernel<f16_t>, dim3((unsigned)a.rows, (unsigned)a.Hq), dim3(128), 0, s, a);
+    if (combine) hipLaunchKernelGGL(attn_combine_kernel<f16_t>, cgrid, dim3(128), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv16x(const void* W, int xm, const float* src, int S, const DecArgs& a, int cmax, float* out,
+                          int rows, int N, int K, int ksplit, int dtype, hipStream_t s) {
+  if (rows < 1 || rows > GEMV_FUSE_ROWS || ksplit < 1 || N % 64 || K % ksplit) return hipErrorInvalidValue;
+  const int kl = K / ksplit, steps = kl / 32;
+  if (kl % 32 || steps > 32) return hipErrorInvalidValue;
+  size_t lds = (size_t)rows * kl * 2;
+  if (xm == 1) {
+    if (S < 1 || S > MAXS) return hipErrorInvalidValue;
+  } else if (xm == 2) {
+    if (kl % HD || cmax < 1 || a.Hq != 2 * a.Hkv || K != a.Hq * HD) return hipErrorInvalidValue;
+    lds += (size_t)rows * (kl / HD) * (2 + 3 * cmax) * sizeof(float);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  if (lds > 65536) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(N / 16 * ksplit / 4)), block(256);
+  auto go = [&](auto u, auto m) {
+    constexpr int U = decltype(u)::value, XM = decltype(m)::value;
+    if (dtype == DT_BF16)
+      hipLaunchKernelGGL((gemv16x_kernel<bf16_t, U, XM>), grid, block, lds, s, (const bf16_t*)W, src, S, a, cmax,
+                         out, rows, N, K, ksplit);
+    else
+      hipLaunchKernelGGL((gemv16x_kernel<f16_t, U, XM>), grid, block, lds, s, (const f16_t*)W, src, S, a, cmax,
+                         out, rows, N, K, ksplit);
+  };
+  auto by_u = [&](auto m) {
+    if (steps <= 8) go(std::integral_constant<int, 8>{}, m);
+    else if (steps <= 16) go(std::integral_constant<int, 16>{}, m);
+    else if (steps <= 24) go(std::integral_constant<int, 24>{}, m);
+    else go(std::integral_constant<int, 32>{}, m);
+  };
+  if (dtype != DT_BF16 && dtype != DT_F16) return hipErrorInvalidValue;
+  if (xm == 1) by_u(std::integral_constant<int, 1>{});
+  else by_u(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 

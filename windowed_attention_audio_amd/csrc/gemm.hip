@@ -58,7 +58,6 @@ __device__ __forceinline__ void store4(T* p, float v0, float v1, float v2, float
   if constexpr (sizeof(T) == 4) {
     *(float4*)p = make_float4(v0, v1, v2, v3);
   } else {
-    typedef Elem<T> E;
     *(uint2*)p = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
   }
 }
@@ -575,7 +574,6 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
         v2 = gelu_f(v2);
         v3 = gelu_f(v3);
       }
-      typedef Elem<T> E;
       const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
       *(uint2*)(qb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }
@@ -639,7 +637,6 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
         v2 = gelu_f(v2);
         v3 = gelu_f(v3);
       }
-      typedef Elem<T> E;
       const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
       *(uint2*)(hb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }

@@ -161,7 +161,16 @@ hipError_t launch_swiglu(const float* part, int S, void* act, int rows, int F, i
 hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w, void* h, int rows, int D, float eps,
                               int dtype, hipStream_t s);
 hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, hipStream_t s);
-hipError_t launch_attn_dec(const DecArgs& a, int n_items, int dtype, hipStream_t s);
+// attention over the chunk items -> part_o / part_ml; with combine, then
+// o16 = the combined output (else the output projection combines them).
+hipError_t launch_attn_dec(const DecArgs& a, int n_items, bool combine, int dtype, hipStream_t s);
+// The skinny product for at most GEMV_FUSE_ROWS rows with x computed from
+// its producer's partials: xm = 1, x = SwiGLU of the gate/up partials src
+// (S splits, K = F); xm = 2, x = the attention chunk partials of a combined
+// (K = Hq * 128, cmax >= chunks of any row).  Same partial-sum output.
+constexpr int GEMV_FUSE_ROWS = 4;
+hipError_t launch_gemv16x(const void* W, int xm, const float* src, int S, const DecArgs& a, int cmax, float* out,
+                          int rows, int N, int K, int ksplit, int dtype, hipStream_t s);
 // next[r] = first index of the largest logit; pv / pi: [rows][64] scratch.
 hipError_t launch_argmax(const float* logits, int rows, int V, float* pv, int* pi, int32_t* next, hipStream_t s);
 
