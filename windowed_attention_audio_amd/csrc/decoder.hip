@@ -101,38 +101,43 @@ __global__ __launch_bounds__(256) void gemv16_kernel(const T* __restrict__ W, co
 
 // --------------------------------------------------- residual add + RMSNorm
 // One workgroup per row: x[r] += sum_s part[s][r] (S <= 8, may be 0), then
-// h[r] = x[r] / sqrt(mean(x^2) + eps) * w as T (fp32 when T = float).  Every
-// load of the row is issued before the first use (a row is 8 KB; latency,
-// not bandwidth, sets the time).
+// h[r] = x[r] / sqrt(mean(x^2) + eps) * w as T (fp32 when T = float).  A row
+// is 8 KB: latency, not bandwidth, sets the time, so every load of the row
+// (residual, partials, norm weight) is issued before the first use, from
+// clamped addresses (chunks past the row's end reload chunk 0 and are
+// ignored; S is a template parameter): guarded loads became branches that
+// waited for each load.
 constexpr int MAXS = 8;
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x, const float* __restrict__ part,
-                                                          int S, const float* __restrict__ w, void* __restrict__ h,
+                                                          const float* __restrict__ w, void* __restrict__ h,
                                                           int rows, int D, float eps) {
   __shared__ float red[4];
   constexpr int MC = 4;  // float4 chunks per thread: D <= 4096
   const int r = blockIdx.x, t = threadIdx.x;
   float* xr = x + (int64_t)r * D;
   const int nc = D / 4;
-  float4 v[MC];
+  float4 v[MC], ww[MC], p[MC][S > 0 ? S : 1];
+#pragma unroll
+  for (int i = 0; i < MC; ++i) {
+    const int c = t + 256 * i < nc ? t + 256 * i : 0;
+    v[i] = ((const float4*)xr)[c];
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) p[i][s2] = ((const float4*)(part + ((int64_t)s2 * rows + r) * D))[c];
+    ww[i] = ((const float4*)w)[c];
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < MC; ++i) {
     const int c = t + 256 * i;
     if (c < nc) {
-      v[i] = ((const float4*)xr)[c];
-      float4 p[MAXS];
 #pragma unroll
-      for (int s2 = 0; s2 < MAXS; ++s2)
-        if (s2 < S) p[s2] = ((const float4*)(part + ((int64_t)s2 * rows + r) * D))[c];
-#pragma unroll
-      for (int s2 = 0; s2 < MAXS; ++s2)
-        if (s2 < S) {
-          v[i].x += p[s2].x;
-          v[i].y += p[s2].y;
-          v[i].z += p[s2].z;
-          v[i].w += p[s2].w;
-        }
+      for (int s2 = 0; s2 < S; ++s2) {
+        v[i].x += p[i][s2].x;
+        v[i].y += p[i][s2].y;
+        v[i].z += p[i][s2].z;
+        v[i].w += p[i][s2].w;
+      }
       if (S) ((float4*)xr)[c] = v[i];
       ss += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
     }
@@ -145,13 +150,12 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(float* __restrict__ x,
   for (int i = 0; i < MC; ++i) {
     const int c = t + 256 * i;
     if (c < nc) {
-      const float4 ww = ((const float4*)w)[c];
-      const float y0 = v[i].x * rs * ww.x, y1 = v[i].y * rs * ww.y, y2 = v[i].z * rs * ww.z, y3 = v[i].w * rs * ww.w;
+      const float4 wv = ww[i];
+      const float y0 = v[i].x * rs * wv.x, y1 = v[i].y * rs * wv.y, y2 = v[i].z * rs * wv.z, y3 = v[i].w * rs * wv.w;
       if constexpr (sizeof(T) == 4) {
         ((float4*)((float*)h + (int64_t)r * D))[c] = make_float4(y0, y1, y2, y3);
       } else {
-        ((uint2*)((T*)h + (int64_t)r * D))[c] =
-            make_uint2(pack2f<T>(y0, y1), pack2f<T>(y2, y3));
+        ((uint2*)((T*)h + (int64_t)r * D))[c] = make_uint2(pack2f<T>(y0, y1), pack2f<T>(y2, y3));
       }
     }
   }
@@ -194,34 +198,34 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 // One wavefront per (row, head of q | k | v): lane l holds values l and l + 64
 // of the head (the rotation's pairs).  qkv: S partials [S][rows][(Hq + 2 Hkv)
 // HD] (fp32).  q -> qf [rows][Hq][HD] fp32; k, v -> cache.
-template <typename T>
-__global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __restrict__ qkv, int S) {
+template <typename T, int S>
+__global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __restrict__ qkv) {
   const int lane = threadIdx.x & 63;
   const int nh = a.Hq + 2 * a.Hkv;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.rows * nh) return;
   const int r = item / nh, hh = item - r * nh;
   const int ld = nh * HD;
-  float p0[MAXS], p1[MAXS];
+  // every load first (S is a template parameter: no guarded loads)
+  float p0[S], p1[S];
 #pragma unroll
-  for (int s = 0; s < MAXS; ++s)
-    if (s < S) {
-      const float* p = qkv + ((int64_t)s * a.rows + r) * ld + hh * HD;
-      p0[s] = p[lane];
-      p1[s] = p[lane + 64];
-    }
+  for (int s = 0; s < S; ++s) {
+    const float* p = qkv + ((int64_t)s * a.rows + r) * ld + hh * HD;
+    p0[s] = p[lane];
+    p1[s] = p[lane + 64];
+  }
+  const float* nw = hh < a.Hq ? a.q_norm : a.k_norm;
+  const float w0 = nw[lane], w1 = nw[lane + 64];
+  const int pos = a.pos[r], sq = a.seq[r];
   float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-  for (int s = 0; s < MAXS; ++s)
-    if (s < S) {
-      v0 += p0[s];
-      v1 += p1[s];
-    }
-  const int pos = a.pos[r], sq = a.seq[r];
+  for (int s = 0; s < S; ++s) {
+    v0 += p0[s];
+    v1 += p1[s];
+  }
   if (hh < a.Hq + a.Hkv) {
-    const float* nw = hh < a.Hq ? a.q_norm : a.k_norm;
     const float rs = 1.0f / sqrtf(wsum64(v0 * v0 + v1 * v1) / HD + a.eps);
-    const float a0 = v0 * rs * nw[lane], a1 = v1 * rs * nw[lane + 64];
+    const float a0 = v0 * rs * w0, a1 = v1 * rs * w1;
     // angle pos * base^(-lane / 64), in double then reduced to [-pi, pi]
     double ang = (double)pos * exp(-(double)lane * a.log_base / 64.0);
     ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
@@ -265,18 +269,32 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
   const int nk = min(CHUNK, pos + 1 - c0);  // keys of this chunk (>= 1)
   const T* Kc = (const T*)a.cache + ((((int64_t)a.layer * a.max_seqs + sq) * 2 + 0) * a.Hkv + kh) * a.max_pos * HD;
   const T* Vc = Kc + (int64_t)a.Hkv * a.max_pos * HD;
-  {
-    const int h = t >> 7, d = t & 127;
-    qs[h][d] = a.qf[((int64_t)r * a.Hq + 2 * kh + h) * HD + d];
-  }
-  __syncthreads();
+  // Every global load of the workgroup -- the queries, then its K and V
+  // fragments, in the order of use (loads complete in order) -- is issued
+  // before the first wait: three dependent round trips to memory would
+  // otherwise set the time of this small kernel.
   const int kk = t >> 2, part = t & 3;
+  const int kg = t >> 4, dg = t & 15;
+  const float qv = a.qf[((int64_t)r * a.Hq + 2 * kh + (t >> 7)) * HD + (t & 127)];
+  // Keys past the chunk's end load key c0 (always present) and are zeroed
+  // afterwards: guarded loads became branches that waited for each load.
+  uint4 u[4], vv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) u[c] = ((const uint4*)(Kc + (int64_t)(c0 + (kk < nk ? kk : 0)) * HD + part * 32))[c];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = kg + 16 * i;
+    vv[i] = *(const uint4*)(Vc + (int64_t)(c0 + (k < nk ? k : 0)) * HD + dg * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (kk >= nk) u[i] = make_uint4(0, 0, 0, 0);
+    if (kg + 16 * i >= nk) vv[i] = make_uint4(0, 0, 0, 0);
+  }
+  qs[t >> 7][t & 127] = qv;
+  __syncthreads();
   float d0 = 0.f, d1 = 0.f;
   if (kk < nk) {
-    const uint4* kr = (const uint4*)(Kc + (int64_t)(c0 + kk) * HD + part * 32);
-    uint4 u[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) u[c] = kr[c];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const T* e = (const T*)&u[c];
@@ -315,16 +333,9 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
     red[0][4 + wv] = l0;
     red[1][4 + wv] = l1;
   }
-  const int kg = t >> 4, dg = t & 15;
   float o0[8], o1[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o0[j] = o1[j] = 0.f;
-  uint4 vv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k = kg + 16 * i;
-    vv[i] = k < nk ? *(const uint4*)(Vc + (int64_t)(c0 + k) * HD + dg * 8) : make_uint4(0, 0, 0, 0);
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k = kg + 16 * i;
@@ -571,21 +582,50 @@ hipError_t launch_gemv16(const void* W, const void* x, float* out, int rows, int
 hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w, void* h, int rows, int D, float eps,
                               int dtype, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (D % 256 || D > 4096 || S < 0 || S > MAXS) return hipErrorInvalidValue;
+  if (D % 256 || D > 4096 || S < 0 || S > MAXS || (S > 0 && !part)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)rows), block(256);
-  if (dtype == DT_BF16) hipLaunchKernelGGL(add_rmsnorm_kernel<bf16_t>, grid, block, 0, s, x, part, S, w, h, rows, D, eps);
-  else if (dtype == DT_F16) hipLaunchKernelGGL(add_rmsnorm_kernel<f16_t>, grid, block, 0, s, x, part, S, w, h, rows, D, eps);
-  else hipLaunchKernelGGL(add_rmsnorm_kernel<float>, grid, block, 0, s, x, part, S, w, h, rows, D, eps);
+  auto go = [&](auto sc) {
+    constexpr int SC = decltype(sc)::value;
+    if (dtype == DT_BF16)
+      hipLaunchKernelGGL((add_rmsnorm_kernel<bf16_t, SC>), grid, block, 0, s, x, part, w, h, rows, D, eps);
+    else if (dtype == DT_F16)
+      hipLaunchKernelGGL((add_rmsnorm_kernel<f16_t, SC>), grid, block, 0, s, x, part, w, h, rows, D, eps);
+    else
+      hipLaunchKernelGGL((add_rmsnorm_kernel<float, SC>), grid, block, 0, s, x, part, w, h, rows, D, eps);
+  };
+  switch (S) {
+    case 0: go(std::integral_constant<int, 0>{}); break;
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, hipStream_t s) {
-  if (S < 1 || S > MAXS) return hipErrorInvalidValue;
+  if (S < 1 || S > MAXS || (dtype != DT_BF16 && dtype != DT_F16)) return hipErrorInvalidValue;
   const int items = a.rows * (a.Hq + 2 * a.Hkv);
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
-  if (dtype == DT_BF16) hipLaunchKernelGGL(qk_rope_kernel<bf16_t>, grid, block, 0, s, a, qkv, S);
-  else if (dtype == DT_F16) hipLaunchKernelGGL(qk_rope_kernel<f16_t>, grid, block, 0, s, a, qkv, S);
-  else return hipErrorInvalidValue;
+  auto go = [&](auto sc) {
+    constexpr int SC = decltype(sc)::value;
+    if (dtype == DT_BF16) hipLaunchKernelGGL((qk_rope_kernel<bf16_t, SC>), grid, block, 0, s, a, qkv);
+    else hipLaunchKernelGGL((qk_rope_kernel<f16_t, SC>), grid, block, 0, s, a, qkv);
+  };
+  switch (S) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
   return hipGetLastError();
 }
 
