@@ -1183,11 +1183,17 @@ template <typename T, int EPI, bool CONV>
 hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     // Convolutions: the four-stage eight-wavefront kernel with the tap
-    // gather, 256 x 160 tiles of 64 x 80 wavefronts (480 output channels =
-    // 3 tiles; the 256 x 256 variant spills with the gather's per-row state).
+    // gather.  Bias + GELU: 256 x 256 tiles of 128 x 64 wavefronts (480
+    // output channels = 2 tiles, 6 % of the MFMA work on padding, but 17 %
+    // fewer operand bytes per MFMA than 256 x 160 tiles of 64 x 80: in the
+    // 16 x 30 s step conv2 1.86 -> 1.57 ms, conv3 0.53 -> 0.40 ms); with the
+    // sinusoids added (more epilogue state) the 256 x 160 tiles stay.  The
+    // two-stage 256 x 256 kernel spills with the gather's per-row state.
     if constexpr (CONV) {
-      if (a.conv_C % 8 == 0 && a.conv_C >= 32 && (int64_t)a.N * a.ldb * 2 < (1ll << 31))
+      if (a.conv_C % 8 == 0 && a.conv_C >= 32 && (int64_t)a.N * a.ldb * 2 < (1ll << 31)) {
+        if constexpr (EPI == EPI_GELU) return run_w8q<T, 256, EPI, 2, true>(a, s);
         return run_w8q<T, 160, EPI, 4, true>(a, s);
+      }
     }
     if (CONV && a.conv_kind != CONV_2D_S2) return hipErrorInvalidValue;  // 1-D: that kernel only
     if constexpr (!CONV) {
