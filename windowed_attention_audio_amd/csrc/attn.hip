@@ -215,9 +215,13 @@ typedef __attribute__((address_space(3))) void* lds_vptr_t;
 // l16), scale, mask keys >= w, online-softmax update, O^T += V^T P^T.  K and
 // V rows r0 .. r0 + 63 of the LDS arrays hold keys kv0 .. kv0 + 63; 16-byte
 // chunk c of a row sits at slot c ^ (row & 7) (r0 is a multiple of 64).
+// The running sum of the probabilities is a matrix product too: lsum +=
+// 1 P^T with an all-ones first operand, so every lane gets its query's sum
+// of exactly the 16-bit probabilities that weight V, and the vector units
+// (which bound this kernel) skip an add per score.
 template <typename T>
 __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, int r0, int kv0, int w,
-                                             const uint4 (&qf)[2], float& m_run, float& l_part,
+                                             const uint4 (&qf)[2], float& m_run, f32x4& lsum,
                                              f32x4 (&o)[4], int g, int l16) {
   constexpr int CPR = 8;
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
@@ -266,21 +270,15 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
   if (__any((m_new - m_run) * sl2 > 8.0f)) {
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
     m_run = m_new;
-    l_part *= alpha;
+    lsum *= alpha;
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
   }
   const float mb = -m_run * sl2;
-  float psum = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(st[t][e], sl2, mb));
-      st[t][e] = p;
-      psum += p;
-    }
-  l_part += psum;
+    for (int e = 0; e < 4; ++e) st[t][e] = __builtin_amdgcn_exp2f(fmaf(st[t][e], sl2, mb));
 
   // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]; probabilities lie in
   // [0, 2^8]: plain round-to-nearest-even conversions, no clamp
@@ -291,6 +289,8 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
     pf.y = pack2_cast<T>(st[2 * u][2], st[2 * u][3]);
     pf.z = pack2_cast<T>(st[2 * u + 1][0], st[2 * u + 1][1]);
     pf.w = pack2_cast<T>(st[2 * u + 1][2], st[2 * u + 1][3]);
+    const uint32_t one2 = pack2_cast<T>(1.0f, 1.0f);
+    mma16(lsum, make_uint4(one2, one2, one2, one2), pf, T{});
     const int r1 = r0 + 32 * u + 4 * g + (l16 >> 2), r2 = r1 + 16;
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) {
@@ -367,15 +367,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void w
     const int q = qg * 16 + l16;  // this lane's query row (window-local)
     uint4 qf[2] = {qn[0], qn[1]};
     load_q(qg + 4, qn);  // next group, in flight during this one
-    float m_run = -INFINITY, l_part = 0.f;
-    f32x4 o[4];
+    float m_run = -INFINITY;
+    f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f}, o[4];
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = 0; kc < nkc; ++kc) attn_chunk16<T>(Ks, Vs, kc * 64, kc * 64, w, qf, m_run, l_part, o, g, l16);
-    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    const float inv = 1.0f / l_tot;
+    for (int kc = 0; kc < nkc; ++kc) attn_chunk16<T>(Ks, Vs, kc * 64, kc * 64, w, qf, m_run, lsum, o, g, l16);
+    const float inv = 1.0f / lsum[0];
     if (q < w) {
       T* orow = (T*)a.out + (int64_t)(s0 + q) * a.D + head * HD;
 #pragma unroll
@@ -459,8 +457,8 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
     }
   };
 
-  float m_run = -INFINITY, l_part = 0.f;
-  f32x4 o[4];
+  float m_run = -INFINITY;
+  f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f}, o[4];
 #pragma unroll
   for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -474,7 +472,7 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
     __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8) | ((8 >> 4) << 14));  // vmcnt(8)
     __syncthreads();
     issue(kt + 3, FK, FV);
-    if (active) attn_chunk16<T>(K, V, 0, kt * 64, w, qf, m_run, l_part, o, g, l16);
+    if (active) attn_chunk16<T>(K, V, 0, kt * 64, w, qf, m_run, lsum, o, g, l16);
   };
   for (int kt = 0; kt < nkt; kt += 4) {
     step(kt, k0, v0, k3, v3);
@@ -485,9 +483,7 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
   __builtin_amdgcn_s_waitcnt(0);  // drain the loads of tiles past the window
 
   if (active && q < w) {
-    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / lsum[0];
     T* orow = (T*)a.out + (int64_t)(s0 + q) * a.D + head * HD;
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) {
