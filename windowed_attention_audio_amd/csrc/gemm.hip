@@ -155,6 +155,36 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
   }
 }
 
+// EPI_RESID with the residual tile already in registers (R[i][j] = C at the
+// accumulator's place, read before the main loop): C = R + (acc + bias), the
+// same arithmetic as epilogue4.
+template <int MI, int NI>
+__device__ __forceinline__ void epilogue_resid_pre(const GemmArgs& a, f32x4 (&acc)[MI][NI],
+                                                   const float4 (&R)[MI][NI], const int rbase, const int cbase) {
+  float4 bias[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int col = cbase + 16 * j;
+    bias[j] = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = rbase + 16 * i;
+    if (row >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int col = cbase + 16 * j;
+      if (col >= a.N) continue;
+      float4 r = R[i][j];
+      r.x += acc[i][j][0] + bias[j].x;
+      r.y += acc[i][j][1] + bias[j].y;
+      r.z += acc[i][j][2] + bias[j].z;
+      r.w += acc[i][j][3] + bias[j].w;
+      *(float4*)((float*)a.C + (int64_t)row * a.ldc + col) = r;
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int EPI, bool CONV>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int NT = 256;
@@ -1125,6 +1155,23 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
     if (refill) issue(FREE, s + 3);
   };
 
+  // Residual epilogue: this wavefront's part of the fp32 residual tile is
+  // requested before the first DMA, so its read overlaps the main loop
+  // instead of following it (with one round of tiles every CU would read
+  // and write the residual stream at the same moment).  Rows past M read
+  // row M - 1 and are not stored.
+  constexpr bool PRE = EPI == EPI_RESID && !CONV;
+  float4 rpre[PRE ? MI : 1][PRE ? NI : 1];
+  if constexpr (PRE) {
+    const int rb = m0 + wm * WTM + (lane & 15), cb = n0 + wn * WTN + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int row = min(rb + 16 * i, a.M - 1), col = min(cb + 16 * j, a.N - 4);
+        rpre[i][j] = *(const float4*)((const float*)a.C + (int64_t)row * a.ldc + col);
+      }
+  }
   const int nkb = CONV ? (a.K + 127) / 128 * 4 : a.K / 32;  // a multiple of 4; conv: zero slices
   issue(st0, 0);
   issue(st1, 1);
@@ -1158,6 +1205,8 @@ __global__ __launch_bounds__(512, 1) void gemm_w8q_kernel(GemmArgs a) {
 
   if constexpr (EPI == EPI_ACT || EPI == EPI_GELU) {
     epilogue_staged4<T, EPI, BN, MI, NI>(a, acc, st0, st1, st2, st3, m0, n0, wm, wn);
+  } else if constexpr (PRE) {
+    epilogue_resid_pre<MI, NI>(a, acc, rpre, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
   } else {
     epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
   }
