@@ -5,11 +5,11 @@
 // encoder frames [kW, min((k+1)W, N)) of each sequence form window k; a row
 // attends only to the rows of its own window: o = softmax(q k^T / 8) v.
 //
-// One workgroup per (window, head).  The window's K (row-major) and V
-// (transposed, d-major) are staged in LDS once; each wavefront then takes
-// groups of 16 query rows and walks the keys in chunks of 64 with an online
-// softmax (running max and sum in fp32 registers; probabilities enter the
-// second product in the operand type).  Scores are computed
+// One workgroup per (window, head), or for windows longer than 256 keys per
+// (window, 64 queries, head) with the keys streamed through LDS.  Each
+// wavefront takes groups of 16 query rows and walks the keys in chunks of
+// 64 with an online softmax (running maximum and output in fp32 registers;
+// probabilities enter the second product in the operand type).  Scores are computed
 // transposed, S^T = K Q^T, so that every lane owns one query row (its lane
 // index mod 16): the row statistics need only two cross-lane steps, and the
 // probabilities already sit where the next product, O^T = V^T P^T, wants its

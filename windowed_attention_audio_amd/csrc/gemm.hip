@@ -7,11 +7,19 @@
 // activation (implicit GEMM: K index = tap * C + input channel, tap =
 // 3 * freq offset + time offset, zero outside each sequence).
 //
-// Block: 256 threads = 4 wavefronts in a 2 x 2 grid; each wavefront owns a
-// (BM/2) x (BN/2) tile made of 16 x 16 MFMA tiles.  K advances in slices of
-// 128 bytes per row (64 bf16 or 32 fp32).  Slices are double-buffered in
-// LDS; the next slice is fetched into registers while the current one feeds
-// the matrix cores.  Within LDS each row's eight 16-byte chunks are XOR-
+// Kernels (pick_tile at the end chooses by shape, epilogue and dtype):
+//   gemm_w8_kernel   256 x BN tiles, eight wavefronts, two LDS stages of
+//                    64-wide K slices loaded by DMA straight into LDS (wide
+//                    outputs: qkv, fc1; narrow ones at M >= 2048 when the
+//                    tiles fill the CUs);
+//   gemm_w8q_kernel  the same with four stages of 32-wide slices (narrow
+//                    outputs at M = 6000, the convolutions with the tap
+//                    gather);
+//   gemm_lds_kernel  128 x 128 / 64 x 64 tiles, four wavefronts (few rows);
+//   gemm_kernel      register-staged tiles for fp32 operands.
+// Every 16-bit kernel accumulates each output over K in 32-wide steps in
+// the same order, so a row's result does not depend on the kernel, the tile
+// or the batch it was computed in.  Within LDS each row's 16-byte chunks are XOR-
 // swizzled by the row index so that 16 lanes reading 16 rows at one chunk
 // hit distinct banks.
 //
