@@ -70,16 +70,32 @@ __device__ __forceinline__ void store4(T* p, float v0, float v1, float v2, float
   }
 }
 
+// The bias vectors of a lane's NI column fragments (cbase + 16 j .. + 3),
+// all requested before the first is used: a guarded load per fragment
+// compiled to a branch and a wait each, one L2 round trip after another at
+// the end of every tile.  Columns past N read the last four (never stored;
+// N is a multiple of 4); without a bias, zeros (a uniform branch).
+template <int NI>
+__device__ __forceinline__ void load_bias(const GemmArgs& a, const int cbase, float4 (&b)[NI]) {
+  if (!a.bias) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) b[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j) b[j] = *(const float4*)(a.bias + min(cbase + 16 * j, a.N - 4));
+}
+
 template <typename T, int EPI, int MI, int NI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI], const int rbase,
                                           const int cbase) {
   float4 bias[NI];
+  load_bias<NI>(a, cbase, bias);
   constexpr bool PE = EPI == EPI_PE || EPI == EPI_GELU_PE;
   double tau[PE ? NI * 4 : 1];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int col = cbase + 16 * j;
-    bias[j] = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (PE) {
       const int half = a.N / 2;
 #pragma unroll
@@ -170,11 +186,7 @@ template <int MI, int NI>
 __device__ __forceinline__ void epilogue_resid_pre(const GemmArgs& a, f32x4 (&acc)[MI][NI],
                                                    const float4 (&R)[MI][NI], const int rbase, const int cbase) {
   float4 bias[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int col = cbase + 16 * j;
-    bias[j] = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  load_bias<NI>(a, cbase, bias);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int row = rbase + 16 * i;
@@ -593,6 +605,8 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
   constexpr int SWM = CPR % 8 == 0 ? 7 : 3;  // chunks are swizzled within aligned groups
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, l16 = lane & 15;
+  float4 bias[NI];
+  load_bias<NI>(a, n0 + wn * WTN + 4 * g, bias);
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -601,8 +615,7 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
     const int r = (R & 63) + l16;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int col = n0 + wn * WTN + 16 * j + 4 * g;
-      const float4 b = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = bias[j];
       const int q = (wn * WTN + 16 * j + 4 * g) >> 3;  // chunk of the 4 values
       float v0 = acc[i][j][0] + b.x, v1 = acc[i][j][1] + b.y, v2 = acc[i][j][2] + b.z,
             v3 = acc[i][j][3] + b.w;
@@ -658,11 +671,12 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
   uint4* half = wm / WPS ? st1 : st0;
   char* hb = (char*)half;
   const int rw = (wm % WPS) * WTM;  // first row of this wavefront inside its stage
+  float4 bias[NI];
+  load_bias<NI>(a, n0 + wn * WTN + 4 * g, bias);
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
-    const int col = n0 + wn * WTN + 16 * j + 4 * g;
-    const float4 b = (a.bias && col < a.N) ? *(const float4*)(a.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = bias[j];
     const int q = (wn * WTN + 16 * j + 4 * g) >> 3;  // chunk of the 4 values
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -1326,6 +1340,7 @@ hipError_t by_epi(const GemmArgs& a, int epi, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStream_t s) {
+  if (a.N < 4 || a.N % 4) return hipErrorInvalidValue;  // epilogues write 4 columns at a time
   // the convolutions always end in bias + GELU (then the sinusoids for the
   // last 1-D one); no other product takes EPI_GELU_PE
   if (conv && epi != EPI_GELU && epi != EPI_GELU_PE) return hipErrorInvalidValue;
