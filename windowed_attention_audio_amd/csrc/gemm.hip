@@ -107,6 +107,43 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
       }
     }
   }
+  if constexpr (EPI == EPI_RESID) {
+    // C += acc + bias on the fp32 residual stream.  A guarded read per
+    // fragment compiled to a branch and a wait each (MI x NI round trips in a
+    // row); instead the NI vectors of fragment row i + 1 are requested,
+    // from clamped addresses, before row i is added and stored.
+    auto read_row = [&](int i, float4 (&R)[NI]) {
+      const int row = min(rbase + 16 * i, a.M - 1);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        R[j] = *(const float4*)((const float*)a.C + (int64_t)row * a.ldc + min(cbase + 16 * j, a.N - 4));
+    };
+    float4 Rn[NI];
+    read_row(0, Rn);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      float4 R[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) R[j] = Rn[j];
+      if (i + 1 < MI) read_row(i + 1, Rn);
+      const int row = rbase + 16 * i;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int col = cbase + 16 * j;
+        if (col >= a.N) continue;
+        const float v0 = acc[i][j][0] + bias[j].x, v1 = acc[i][j][1] + bias[j].y;
+        const float v2 = acc[i][j][2] + bias[j].z, v3 = acc[i][j][3] + bias[j].w;
+        float4 r = R[j];
+        r.x += v0;
+        r.y += v1;
+        r.z += v2;
+        r.w += v3;
+        *(float4*)((float*)a.C + (int64_t)row * a.ldc + col) = r;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int row = rbase + 16 * i;
