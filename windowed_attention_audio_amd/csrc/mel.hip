@@ -41,32 +41,52 @@ __global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
   __shared__ float xs[FPB][400];       // raw frame samples, later |X|^2 [FPB][201]
   __shared__ double2 ys[FPB][25][9];   // step-A output, k1 = 0..8
   __shared__ float fmax_s[FPB];
-  __shared__ int fseq_s[FPB];
+  __shared__ int fseq_s[FPB], ft_s[FPB], fn_s[FPB];
+  __shared__ int64_t foff_s[FPB];
 
   const int tid = threadIdx.x;
   const int64_t f0 = (int64_t)blockIdx.x * FPB;
 
-  // frame -> sequence (one lookup per frame)
+  // frame -> sequence, its frame index in the stream and the sequence's
+  // samples (one lookup per frame, kept in LDS for the load below)
   if (tid < FPB) {
     const int64_t gf = f0 + tid;
-    fseq_s[tid] = gf < a.total_frames ? find_seq(a.cu_frames, a.nseq, (int)gf) : -1;
+    const int sq = gf < a.total_frames ? find_seq(a.cu_frames, a.nseq, (int)gf) : -1;
+    fseq_s[tid] = sq;
+    ft_s[tid] = sq >= 0 ? (int)gf - a.cu_frames[sq] + (int)a.frame_off : 0;
+    fn_s[tid] = sq >= 0 ? a.seq_len[sq] : 1;
+    foff_s[tid] = sq >= 0 ? a.seq_sample_off[sq] : 0;
   }
   __syncthreads();
 
-  // ---- load (the window is applied in double in step A)
-  for (int idx = tid; idx < FPB * 400; idx += NTH) {
-    const int f = idx / 400, j = idx - f * 400;
-    const int sq = fseq_s[f];
-    float v = 0.f;
-    if (sq >= 0) {
-      const int t = (int)(f0 + f) - a.cu_frames[sq] + (int)a.frame_off;
-      const int n = a.seq_len[sq];
-      int q = 160 * t + j - 200;
-      q = q < 0 ? -q : q;
-      q = q >= n ? 2 * (n - 1) - q : q;
-      v = a.wav[a.seq_sample_off[sq] + q];
+  // ---- load (the window is applied in double in step A).  All 25 samples
+  // of a thread are requested before the first is stored: a guarded load
+  // per iteration waited for each one in turn.  Frames past the end read
+  // sample 0 and store zeros.
+  {
+    constexpr int PER = FPB * 400 / NTH;
+    static_assert(FPB * 400 % NTH == 0, "load plan");
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + NTH * u;
+      const int f = idx / 400, j = idx - f * 400;
+      int64_t src = 0;
+      if (fseq_s[f] >= 0) {
+        const int n = fn_s[f];
+        int q = 160 * ft_s[f] + j - 200;
+        q = q < 0 ? -q : q;
+        q = q >= n ? 2 * (n - 1) - q : q;
+        src = foff_s[f] + q;
+      }
+      v[u] = a.wav[src];
     }
-    xs[f][j] = v;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + NTH * u;
+      const int f = idx / 400;
+      xs[f][idx - f * 400] = fseq_s[f] >= 0 ? v[u] : 0.f;
+    }
   }
   __syncthreads();
 
