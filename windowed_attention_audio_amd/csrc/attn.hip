@@ -211,6 +211,20 @@ typedef short tr4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) tr4_t* tr_ptr_t;
 typedef __attribute__((address_space(3))) void* lds_vptr_t;
 
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes holding
+// one query's scores).  v_permlane16_swap of a register with itself gives
+// each lane the value of lane l ^ 16, v_permlane32_swap that of lane l ^ 32:
+// two VALU swaps instead of two LDS permutes, which waited on the LDS.
+// Scores are finite or -inf, so a plain comparison serves as the maximum.
+__device__ __forceinline__ float max4_lanes(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a0 = __uint_as_float(a[0]), a1 = __uint_as_float(a[1]);
+  v = a0 > a1 ? a0 : a1;
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float b0 = __uint_as_float(b[0]), b1 = __uint_as_float(b[1]);
+  return b0 > b1 ? b0 : b1;
+}
+
 // One chunk of 64 keys for one 16-query group: S^T = K Q^T (lane = query
 // l16), scale, mask keys >= w, online-softmax update, O^T += V^T P^T.  K and
 // V rows r0 .. r0 + 63 of the LDS arrays hold keys kv0 .. kv0 + 63; 16-byte
@@ -256,8 +270,7 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
         cmax = fmaxf(cmax, v);
       }
   }
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  cmax = max4_lanes(cmax);
   // Lazy rescaling: the reference maximum m_run moves (and the running sum
   // and the output accumulators are scaled down to it) only when some query
   // of the wavefront has gained more than a factor 2^8 over it -- always in
