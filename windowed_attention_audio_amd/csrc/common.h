@@ -65,6 +65,35 @@ __device__ __forceinline__ float gelu_f(float x) {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
+// Reductions over the 64 lanes of a wavefront in the butterfly order (the
+// partner of lane l is l ^ 32, then l ^ 16, 8, 4, 2, 1), every lane ending
+// with the same bits, without the LDS: v_permlane32_swap / v_permlane16_swap
+// of a register with itself hand each lane its xor-32 / xor-16 partner (as
+// the pair (own, partner) or (partner, own); addition is commutative), and
+// once the bits above m are reduced the values repeat with period 2m, so a
+// DPP rotation by m within each 16-lane row reads the same value as the xor
+// partner.  Same results as __shfl_xor butterflies, without the ds_bpermute
+// round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce64(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  v = op(v, dpp_f<0x128>(v));  // row_ror:8
+  v = op(v, dpp_f<0x124>(v));  // row_ror:4
+  v = op(v, dpp_f<0x122>(v));  // row_ror:2
+  v = op(v, dpp_f<0x121>(v));  // row_ror:1
+  return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) { return wave_reduce64<false>(v); }
+__device__ __forceinline__ float wave_max64(float v) { return wave_reduce64<true>(v); }
+
 // Order-preserving map float -> int for atomicMax on floats of any sign.
 __device__ __forceinline__ int float_key(float f) {
   int i = __float_as_int(f);

@@ -34,16 +34,8 @@ namespace {
 
 constexpr int HD = 128;  // head_dim
 
-__device__ __forceinline__ float wsum64(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-__device__ __forceinline__ float wmax64(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
+__device__ __forceinline__ float wsum64(float v) { return wave_sum64(v); }
+__device__ __forceinline__ float wmax64(float v) { return wave_max64(v); }
 
 // ---------------------------------------------------------------- skinny GEMV
 // out[s][r][n] = sum_{k in split s} x[r][k] W[n][k] for r < rows (<= 64).
@@ -306,10 +298,12 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
       }
     }
   }
-  d0 += __shfl_xor(d0, 1, 64);
-  d1 += __shfl_xor(d1, 1, 64);
-  d0 += __shfl_xor(d0, 2, 64);
-  d1 += __shfl_xor(d1, 2, 64);
+  // sum over the key's four threads (a quad): DPP quad permutations
+  // [1, 0, 3, 2] and [2, 3, 0, 1] give the xor-1 and xor-2 partners
+  d0 += dpp_f<0xB1>(d0);
+  d1 += dpp_f<0xB1>(d1);
+  d0 += dpp_f<0x4E>(d0);
+  d1 += dpp_f<0x4E>(d1);
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
   const float s0 = kk < nk ? d0 * scale : -INFINITY, s1 = kk < nk ? d1 * scale : -INFINITY;
   const int wv = t >> 6;

@@ -162,8 +162,12 @@ __global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) out[part + 16 * r] = L[r];
     }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 16));
+    // maximum over the 16 lanes of the frame: DPP row rotations (the maximum
+    // does not depend on the order)
+    lmax = fmaxf(lmax, dpp_f<0x128>(lmax));
+    lmax = fmaxf(lmax, dpp_f<0x124>(lmax));
+    lmax = fmaxf(lmax, dpp_f<0x122>(lmax));
+    lmax = fmaxf(lmax, dpp_f<0x121>(lmax));
     if (part == 0) fmax_s[f] = lmax;
   }
   __syncthreads();
