@@ -233,77 +233,87 @@ __device__ __forceinline__ float max4_lanes(float v) {
 // 1 P^T with an all-ones first operand, so every lane gets its query's sum
 // of exactly the 16-bit probabilities that weight V, and the vector units
 // (which bound this kernel) skip an add per score.
-template <typename T>
-__device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, int r0, int kv0, int w,
-                                             const uint4 (&qf)[2], float& m_run, f32x4& lsum,
-                                             f32x4 (&o)[4], int g, int l16) {
+template <typename T, int NG>
+__device__ __forceinline__ void attn_chunkN(const uint4* Ks, const uint4* Vs, int r0, int kv0, int w,
+                                            const uint4 (&qf)[NG][2], float (&m_run)[NG], f32x4 (&lsum)[NG],
+                                            f32x4 (&o)[NG][4], int g, int l16) {
   constexpr int CPR = 8;
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
-  f32x4 st[4];
+  f32x4 st[NG][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int G = 0; G < NG; ++G) st[G][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kvr = r0 + t * 16 + l16;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint4 kf = Ks[kvr * CPR + ((4 * s + g) ^ (kvr & 7))];
-      mma16(st[t], kf, qf[s], T{});
+#pragma unroll
+      for (int G = 0; G < NG; ++G) mma16(st[G][t], kf, qf[G][s], T{});
     }
   }
-  // lane holds S^T[kv = kv0 + 16t + 4g + e][q] (unscaled); mask, row max.
-  // m_run is kept in raw-score units: p = 2^((s - m) sl2) is one fma and
-  // one v_exp_f32 (its argument is never positive: no range handling).
-  float cmax = -INFINITY;
-  if (kv0 + 64 <= w) {
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    // lane holds S^T[kv = kv0 + 16t + 4g + e][q] (unscaled); mask, row max.
+    // m_run is kept in raw-score units: p = 2^((s - m) sl2) is one fma and
+    // one v_exp_f32 (its argument is never positive: no range handling).
+    float cmax = -INFINITY;
+    if (kv0 + 64 <= w) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cmax = fmaxf(cmax, st[G][t][e]);
+    } else {  // last, partial chunk: keys >= w drop out
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kv = kv0 + t * 16 + 4 * g + e;
+          const float v = kv < w ? st[G][t][e] : -INFINITY;
+          st[G][t][e] = v;
+          cmax = fmaxf(cmax, v);
+        }
+    }
+    cmax = max4_lanes(cmax);
+    // Lazy rescaling: the reference maximum m_run moves (and the running
+    // sum and the output accumulators are scaled down to it) only when some
+    // query of the group has gained more than a factor 2^8 over it --
+    // always in the first chunk (m_run = -inf), rarely after.  Otherwise
+    // the probabilities stay relative to the old reference, below 2^8,
+    // which the 16-bit operand types hold at the same relative precision as
+    // values below 1; the final division by the sum cancels the reference.
+    // The decision is per group of 16 queries (all lanes of the wavefront),
+    // so the branch is uniform.
+    const float m_new = fmaxf(m_run[G], cmax);
+    if (__any((m_new - m_run[G]) * sl2 > 8.0f)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_run[G] - m_new) * sl2);
+      m_run[G] = m_new;
+      lsum[G] *= alpha;
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) o[G][nd] *= alpha;
+    }
+    const float mb = -m_run[G] * sl2;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cmax = fmaxf(cmax, st[t][e]);
-  } else {  // last, partial chunk: keys >= w drop out
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kv = kv0 + t * 16 + 4 * g + e;
-        const float v = kv < w ? st[t][e] : -INFINITY;
-        st[t][e] = v;
-        cmax = fmaxf(cmax, v);
-      }
+      for (int e = 0; e < 4; ++e) st[G][t][e] = __builtin_amdgcn_exp2f(fmaf(st[G][t][e], sl2, mb));
   }
-  cmax = max4_lanes(cmax);
-  // Lazy rescaling: the reference maximum m_run moves (and the running sum
-  // and the output accumulators are scaled down to it) only when some query
-  // of the wavefront has gained more than a factor 2^8 over it -- always in
-  // the first chunk (m_run = -inf), rarely after.  Otherwise the
-  // probabilities stay relative to the old reference, below 2^8, which the
-  // 16-bit operand types hold at the same relative precision as values
-  // below 1; the final division by the sum cancels the reference.  The
-  // decision is per wavefront, so the branch is uniform.
-  const float m_new = fmaxf(m_run, cmax);
-  if (__any((m_new - m_run) * sl2 > 8.0f)) {
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
-    m_run = m_new;
-    lsum *= alpha;
-#pragma unroll
-    for (int nd = 0; nd < 4; ++nd) o[nd] *= alpha;
-  }
-  const float mb = -m_run * sl2;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st[t][e] = __builtin_amdgcn_exp2f(fmaf(st[t][e], sl2, mb));
 
   // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]; probabilities lie in
-  // [0, 2^8]: plain round-to-nearest-even conversions, no clamp
+  // [0, 2^8]: plain round-to-nearest-even conversions, no clamp.  Each V
+  // fragment read feeds the NG groups' products.
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    uint4 pf;
-    pf.x = pack2_cast<T>(st[2 * u][0], st[2 * u][1]);
-    pf.y = pack2_cast<T>(st[2 * u][2], st[2 * u][3]);
-    pf.z = pack2_cast<T>(st[2 * u + 1][0], st[2 * u + 1][1]);
-    pf.w = pack2_cast<T>(st[2 * u + 1][2], st[2 * u + 1][3]);
+    uint4 pf[NG];
     const uint32_t one2 = pack2_cast<T>(1.0f, 1.0f);
-    mma16(lsum, make_uint4(one2, one2, one2, one2), pf, T{});
+#pragma unroll
+    for (int G = 0; G < NG; ++G) {
+      pf[G].x = pack2_cast<T>(st[G][2 * u][0], st[G][2 * u][1]);
+      pf[G].y = pack2_cast<T>(st[G][2 * u][2], st[G][2 * u][3]);
+      pf[G].z = pack2_cast<T>(st[G][2 * u + 1][0], st[G][2 * u + 1][1]);
+      pf[G].w = pack2_cast<T>(st[G][2 * u + 1][2], st[G][2 * u + 1][3]);
+      mma16(lsum[G], make_uint4(one2, one2, one2, one2), pf[G], T{});
+    }
     const int r1 = r0 + 32 * u + 4 * g + (l16 >> 2), r2 = r1 + 16;
 #pragma unroll
     for (int nd = 0; nd < 4; ++nd) {
@@ -313,9 +323,26 @@ __device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, i
       const tr4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (tr_ptr_t)((char*)(Vs + r2 * CPR + (c ^ (r2 & 7))) + half));
       const uint2 w1 = __builtin_bit_cast(uint2, v1), w2 = __builtin_bit_cast(uint2, v2);
-      mma16(o[nd], make_uint4(w1.x, w1.y, w2.x, w2.y), pf, T{});
+#pragma unroll
+      for (int G = 0; G < NG; ++G) mma16(o[G][nd], make_uint4(w1.x, w1.y, w2.x, w2.y), pf[G], T{});
     }
   }
+}
+
+// One query group (the on-chip kernel).
+template <typename T>
+__device__ __forceinline__ void attn_chunk16(const uint4* Ks, const uint4* Vs, int r0, int kv0, int w,
+                                             const uint4 (&qf)[2], float& m_run, f32x4& lsum,
+                                             f32x4 (&o)[4], int g, int l16) {
+  uint4 q1[1][2] = {{qf[0], qf[1]}};
+  float m1[1] = {m_run};
+  f32x4 l1[1] = {lsum};
+  f32x4 o1[1][4] = {{o[0], o[1], o[2], o[3]}};
+  attn_chunkN<T, 1>(Ks, Vs, r0, kv0, w, q1, m1, l1, o1, g, l16);
+  m_run = m1[0];
+  lsum = l1[0];
+#pragma unroll
+  for (int nd = 0; nd < 4; ++nd) o[nd] = o1[0][nd];
 }
 
 template <typename T>
@@ -413,15 +440,19 @@ hipError_t run_attn16(const AttnArgs& a, hipStream_t s) {
 }
 
 // Windows longer than the on-chip maximum (any W; W >= N is full attention
-// over each sequence): one workgroup per (window, block of 64 queries,
-// head), 16 queries per wavefront, and the window's keys stream through LDS
-// in tiles of 64 (K and V, 16 KB per stage, four stages: each tile's DMA is
-// issued three tiles ahead; tiles past the window read zeros, so every
-// wavefront issues the same loads).  Same per-chunk math as above.
+// over each sequence): one workgroup per (window, block of 128 queries,
+// head), two groups of 16 queries per wavefront, and the window's keys
+// stream through LDS in tiles of 64 (K and V, 16 KB per stage, four stages:
+// each tile's DMA is issued three tiles ahead; tiles past the window read
+// zeros, so every wavefront issues the same loads).  Same per-chunk math as
+// above; each K and V fragment read from LDS feeds both groups, and the two
+// groups' softmax chains interleave (one group per wavefront left the
+// matrix cores waiting on each chunk's max -> exp -> product chain).
 template <typename T>
 __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) {
   static_assert(sizeof(T) == 2, "16-bit operands");
   constexpr int HD = 64, CPR = 8;
+  constexpr int NG = 2, QB = 64 * NG;  // query groups per wavefront, queries per workgroup
   __shared__ uint4 k0[64 * CPR], k1[64 * CPR], k2[64 * CPR], k3[64 * CPR];
   __shared__ uint4 v0[64 * CPR], v1[64 * CPR], v2[64 * CPR], v3[64 * CPR];
 
@@ -432,7 +463,7 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
   const int N = a.cu_rows[sq + 1] - a.cu_rows[sq];
   const int s0 = a.cu_rows[sq] + kwin * a.window;
   const int w = min(a.window, N - kwin * a.window);
-  if (qb * 64 >= w) return;  // the whole workgroup: before any barrier
+  if (qb * QB >= w) return;  // the whole workgroup: before any barrier
 
   const int ldb = 3 * a.D * (int)sizeof(T);  // bytes per qkv row
   const char* base = (const char*)a.qkv + (int64_t)s0 * ldb;
@@ -443,18 +474,23 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
   const int g = lane >> 4, l16 = lane & 15;
   const int nkt = (w + 63) >> 6;
 
-  // query group of this wavefront (may lie past w in the last block)
-  const int q = qb * 64 + wave * 16 + l16;
-  const bool active = qb * 64 + wave * 16 < w;
-  uint4 qf[2];
+  // query groups of this wavefront: rows qb QB + 64 G + 16 wave + l16 (the
+  // second may lie past w, then it is computed and not stored)
+  int q[NG];
+  uint4 qf[NG][2];
   {
     const T* Qg = (const T*)base + head * HD;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      qf[s] = make_uint4(0, 0, 0, 0);
-      if (q < w) qf[s] = *(const uint4*)(Qg + (int64_t)q * (3 * a.D) + (4 * s + g) * 8);
+    for (int G = 0; G < NG; ++G) {
+      q[G] = qb * QB + 64 * G + wave * 16 + l16;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        qf[G][s] = make_uint4(0, 0, 0, 0);
+        if (q[G] < w) qf[G][s] = *(const uint4*)(Qg + (int64_t)q[G] * (3 * a.D) + (4 * s + g) * 8);
+      }
     }
   }
+  const bool active = qb * QB + wave * 16 < w;
 
   // tile kt into (K, V): 16 blocks of 8 rows, four per wavefront
   auto issue = [&](int kt, uint4* K, uint4* V) {
@@ -470,10 +506,15 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
     }
   };
 
-  float m_run = -INFINITY;
-  f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f}, o[4];
+  float m_run[NG];
+  f32x4 lsum[NG], o[NG][4];
 #pragma unroll
-  for (int nd = 0; nd < 4; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int G = 0; G < NG; ++G) {
+    m_run[G] = -INFINITY;
+    lsum[G] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd) o[G][nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   issue(0, k0, v0);
   issue(1, k1, v1);
@@ -485,7 +526,7 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
     __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8) | ((8 >> 4) << 14));  // vmcnt(8)
     __syncthreads();
     issue(kt + 3, FK, FV);
-    if (active) attn_chunk16<T>(K, V, 0, kt * 64, w, qf, m_run, lsum, o, g, l16);
+    if (active) attn_chunkN<T, NG>(K, V, 0, kt * 64, w, qf, m_run, lsum, o, g, l16);
   };
   for (int kt = 0; kt < nkt; kt += 4) {
     step(kt, k0, v0, k3, v3);
@@ -495,16 +536,19 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the loads of tiles past the window
 
-  if (active && q < w) {
-    const float inv = 1.0f / lsum[0];
-    T* orow = (T*)a.out + (int64_t)(s0 + q) * a.D + head * HD;
 #pragma unroll
-    for (int nd = 0; nd < 4; ++nd) {
-      const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
-      uint2 pk;
-      pk.x = pack2f<T>(o[nd][0] * inv, o[nd][1] * inv);
-      pk.y = pack2f<T>(o[nd][2] * inv, o[nd][3] * inv);
-      *(uint2*)(orow + d0) = pk;
+  for (int G = 0; G < NG; ++G) {
+    if (active && q[G] < w) {
+      const float inv = 1.0f / lsum[G][0];
+      T* orow = (T*)a.out + (int64_t)(s0 + q[G]) * a.D + head * HD;
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) {
+        const int d0 = nd * 16 + 4 * g;  // lane holds O^T[d0 + e][q]
+        uint2 pk;
+        pk.x = pack2f<T>(o[G][nd][0] * inv, o[G][nd][1] * inv);
+        pk.y = pack2f<T>(o[G][nd][2] * inv, o[G][nd][3] * inv);
+        *(uint2*)(orow + d0) = pk;
+      }
     }
   }
 }
@@ -512,7 +556,7 @@ __global__ __launch_bounds__(256) void wattn16s_kernel(AttnArgs a, int qblocks) 
 template <typename T>
 hipError_t run_attn16s(const AttnArgs& a, hipStream_t s) {
   if (a.n_windows == 0) return hipSuccess;
-  const int qblocks = (a.wpad + 63) / 64;
+  const int qblocks = (a.wpad + 127) / 128;  // 128 queries per workgroup
   hipLaunchKernelGGL(wattn16s_kernel<T>, dim3(a.n_windows * qblocks, a.n_heads), dim3(256), 0, s, a,
                      qblocks);
   return hipGetLastError();
