@@ -102,8 +102,8 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
       for (int e = 0; e < 4; ++e) {
         const int c = col + e;
         const int jj = c < half ? c : c - half;
-        // timescale 10000^(-jj / (half - 1))
-        tau[4 * j + e] = exp(-(double)jj * 9.2103403719761836 / (double)(half - 1));
+        // timescale 10000^(-jj / (half - 1)), in revolutions per position
+        tau[4 * j + e] = exp(-(double)jj * 9.2103403719761836 / (double)(half - 1)) * 0.15915494309189535;
       }
     }
   }
@@ -144,17 +144,34 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
     }
     return;
   }
+  // Sequence of the lane's rows (PE, padded EPI_OUT): one search for its
+  // first row, then a step forward whenever a row passes the sequence's end
+  // (rows rbase + 16 i increase; a search per row waited on its chain of
+  // dependent loads for every row).  Same result as find_seq for each row.
+  [[maybe_unused]] int sq_c = 0, sq_lo = 0, sq_hi = 0;
+  constexpr bool SEQ = PE || EPI == EPI_OUT;
+  if constexpr (SEQ) {
+    if (PE || a.out_seq_stride > 0) {
+      sq_c = find_seq(a.cu_rows, a.nseq, min(rbase, a.M - 1));
+      sq_lo = a.cu_rows[sq_c];
+      sq_hi = a.cu_rows[sq_c + 1];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int row = rbase + 16 * i;
     if (row >= a.M) continue;
     int64_t orow = row;
     int pos = 0;
-    if constexpr (PE || EPI == EPI_OUT) {
+    if constexpr (SEQ) {
       if (PE || a.out_seq_stride > 0) {
-        const int sq = find_seq(a.cu_rows, a.nseq, row);
-        pos = row - a.cu_rows[sq] + (PE ? a.pos_offset : 0);
-        if (EPI == EPI_OUT) orow = (int64_t)sq * a.out_seq_stride + pos;
+        while (row >= sq_hi && sq_c + 1 < a.nseq) {
+          ++sq_c;
+          sq_lo = sq_hi;
+          sq_hi = a.cu_rows[sq_c + 1];
+        }
+        pos = row - sq_lo + (PE ? a.pos_offset : 0);
+        if (EPI == EPI_OUT) orow = (int64_t)sq_c * a.out_seq_stride + pos;
       }
     }
 #pragma unroll
@@ -202,10 +219,14 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            double ang = (double)pos * tau[4 * j + e];
-            ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-            const float fa = (float)ang;
-            o[e] = (EPI == EPI_GELU_PE ? gelu_f(v[e]) : acc[i][j][e]) + (col + e < half ? sinf(fa) : cosf(fa));
+            // angle in revolutions, reduced to [-1/2, 1/2] in double; the
+            // hardware sine / cosine take revolutions (max error 1.2e-7 on
+            // this range, as for sinf of the angle rounded to float)
+            double rev = (double)pos * tau[4 * j + e];
+            rev -= rint(rev);
+            const float fr = (float)rev;
+            o[e] = (EPI == EPI_GELU_PE ? gelu_f(v[e]) : acc[i][j][e]) +
+                   (col + e < half ? __builtin_amdgcn_sinf(fr) : __builtin_amdgcn_cosf(fr));
           }
           store4((float*)a.C + (int64_t)row * a.ldc + col, o[0], o[1], o[2], o[3]);
         } else if constexpr (EPI == EPI_OUT) {
