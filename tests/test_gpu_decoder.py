@@ -8,7 +8,9 @@
     decode step with a row each; a 600-row prompt and decode steps past it
     (attention over three 256-key chunks);
   * the card's full width (d 2048, 16/8 heads, FFN 6144, vocab 151 936) with
-    two layers: prompt + decode steps against the oracle;
+    two layers: prompt + decode steps against the oracle, and a 3-row step of
+    three sequences (up to four rows the output and down projections compute
+    their input -- the attention combine, SwiGLU -- themselves);
   * the card's 28 layers: a 16-row decode step equals each row alone
     (bitwise), and argmax equals the host's argmax of the returned logits.
 Logits are compared row by row: cosine >= 0.999 and max |diff| <= 0.02 RMS.
@@ -151,6 +153,29 @@ def test_full_width_two_layers():
     for i in (20, 21):
         gl, nx = g.step(x[i:i + 1], [0], [i])
         r = check_logits(gl, OD.forward(x[i:i + 1], P, geom, cache), nx, f"full-width decode {i}")
+    say(f"  cos {r['cos'].min():.6f} worst {r['maxabs_rms'].max():.4f}")
+
+
+def test_full_width_three_rows_fused_products():
+    """At most four rows the output and down projections compute their input
+    (the attention combine, SwiGLU) inside the product; at full width both
+    apply.  Three sequences, then one 3-row step, against the oracle."""
+    geom = dict(synth.DEC_GEOM, n_layers=2)
+    say("decoder full width, 2 layers: 3 prompts, then a 3-row step")
+    w = synth.make_decoder_weights(geom, bf16=True, seed=9)
+    P = {k: v.astype(np.float64) for k, v in w.items()}
+    lens = [7, 70, 2]  # 1, 2 and 1 chunks of 64 keys at the step
+    rng = np.random.default_rng(9)
+    xs = [OD.embed(rng.integers(0, geom["vocab"], n + 1), P) for n in lens]
+    g = GpuDecoder(geom, w, "f16", 3, 128)
+    slots = [1, 2, 0]
+    caches = [OD.empty_cache(geom) for _ in lens]
+    for xi, n, c, sl in zip(xs, lens, caches, slots):
+        g.step(xi[:n], [sl] * n, list(range(n)))
+        OD.forward(xi[:n], P, geom, c)
+    gl, nx = g.step(np.stack([xi[n] for xi, n in zip(xs, lens)]), slots, lens)
+    ref = np.concatenate([OD.forward(xi[n:n + 1], P, geom, c) for xi, n, c in zip(xs, lens, caches)])
+    r = check_logits(gl, ref, nx, "3-row step")
     say(f"  cos {r['cos'].min():.6f} worst {r['maxabs_rms'].max():.4f}")
 
 
