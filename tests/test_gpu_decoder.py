@@ -12,7 +12,10 @@
     three sequences (up to four rows the output and down projections compute
     their input -- the attention combine, SwiGLU -- themselves);
   * the card's 28 layers: a 16-row decode step equals each row alone
-    (bitwise), and argmax equals the host's argmax of the returned logits.
+    (bitwise), and argmax equals the host's argmax of the returned logits;
+  * steps with one row per sequence (queries and the new key / value computed
+    inside the attention kernel) equal two rows of one sequence in one call
+    (separate Q/K-norm pass), bitwise.
 Logits are compared row by row: cosine >= 0.999 and max |diff| <= 0.02 RMS.
 """
 
@@ -121,6 +124,25 @@ def test_small_three_sequences(small_w):
     gl, nx = g.step(np.stack([xi[n] for xi, n in zip(xs, lens)]), slots, lens)
     ref = np.concatenate([OD.forward(xi[n:n + 1], P, SMALL, c) for xi, n, c in zip(xs, lens, caches)])
     check_logits(gl, ref, nx, "3 decode rows")
+
+
+def test_fused_qk_equals_separate_pass(small_w):
+    """With one row per sequence the attention kernel computes the queries and
+    the new key / value itself; two rows of one sequence in one call take the
+    separate Q/K-norm pass (the second row attends to the first one's new
+    entry).  The same two rows in two calls must give the same bits."""
+    P = {k: v.astype(np.float64) for k, v in small_w.items()}
+    x = OD.embed(np.random.default_rng(6).integers(0, SMALL["vocab"], 12), P)
+    say("decoder small: 2 rows of one sequence in one call vs two calls")
+    ga = GpuDecoder(SMALL, small_w, "bf16", 1, 64)
+    gb = GpuDecoder(SMALL, small_w, "bf16", 1, 64)
+    ga.step(x[:10], [0] * 10, list(range(10)))
+    gb.step(x[:10], [0] * 10, list(range(10)))
+    la, na = ga.step(x[10:12], [0, 0], [10, 11])
+    lb0, nb0 = gb.step(x[10:11], [0], [10])
+    lb1, nb1 = gb.step(x[11:12], [0], [11])
+    assert np.array_equal(la[0], lb0[0]) and np.array_equal(la[1], lb1[0])
+    assert na[0] == nb0[0] and na[1] == nb1[0]
 
 
 def test_small_long_context(small_w):

@@ -726,6 +726,9 @@ struct DecPlan {
   // input, the output projection combines the attention chunks itself
   bool fuse_d = false, fuse_o = false;
   int cmax = 0;  // most chunks of any row
+  // one row per sequence: the attention kernel computes its queries and the
+  // new keys / values itself (no row of the call reads another's new entry)
+  bool fuse_qk = false;
   std::vector<int32_t> words;  // seq | pos | items | first_item
   size_t o_words, o_x, o_h, o_qkv, o_qf, o_po, o_pml, o_o16, o_opart, o_gu, o_act, o_dpart, o_amv, o_ami, bytes;
 };
@@ -788,6 +791,13 @@ mt_status plan_decode(const mt_decoder* dec, int32_t n, const int32_t* seq, cons
     p.s_qkv = 1;
     p.s_gu = 0;
     p.s_o = p.s_d = 0;  // the matrix kernels add into the residual stream
+  }
+  {
+    std::vector<int32_t> sq(seq, seq + n);
+    std::sort(sq.begin(), sq.end());
+    const bool distinct = std::adjacent_find(sq.begin(), sq.end()) == sq.end();
+    const int S = p.s_qkv;
+    p.fuse_qk = distinct && (S == 1 || S == 2 || S == 4 || S == 8);
   }
   if (p.gemv && n <= GEMV_FUSE_ROWS && D % 64 == 0) {
     for (int i = 0; i < n; ++i) p.cmax = std::max(p.cmax, first[i + 1] - first[i]);
@@ -983,8 +993,9 @@ mt_status mt_decode(const mt_decoder* dec, const float* x_in, int32_t n_rows, co
     } else {
       STAGE(launch_gemm(gemm_(h, D, L.wqkv, n, NQKV, D, qkv, NQKV), EPI_F32, dt, false, s), "dec_qkv");
     }
-    STAGE(launch_qk_rope(a, qkv, p.s_qkv, dt, s), "dec_qk_rope");
-    STAGE(launch_attn_dec(a, p.n_items, !p.fuse_o, dt, s), "dec_attn");
+    if (!p.fuse_qk) STAGE(launch_qk_rope(a, qkv, p.s_qkv, dt, s), "dec_qk_rope");
+    STAGE(launch_attn_dec(a, p.n_items, !p.fuse_o, p.fuse_qk ? qkv : nullptr, p.fuse_qk ? p.s_qkv : 0, dt, s),
+          "dec_attn");
     if (p.fuse_o) {
       STAGE(launch_gemv16x(L.wo, 2, nullptr, 0, a, p.cmax, opart, n, D, NQ, p.s_o, dt, s), "dec_o");
     } else if (p.gemv) {

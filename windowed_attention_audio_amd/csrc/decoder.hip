@@ -190,6 +190,34 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 // One wavefront per (row, head of q | k | v): lane l holds values l and l + 64
 // of the head (the rotation's pairs).  qkv: S partials [S][rows][(Hq + 2 Hkv)
 // HD] (fp32).  q -> qf [rows][Hq][HD] fp32; k, v -> cache.
+// One head of one row from its S fp32 partials: lane l gets values l and
+// l + 64.  q and k heads (rot): RMSNorm over the head with weights (w0, w1),
+// then the rotation at position pos (value j paired with j + 64, angle
+// pos * base^(-j / 64)).  Shared by the standalone pass and the attention
+// kernel that computes its own queries, so both give the same bits.
+template <int S>
+__device__ __forceinline__ void qk_head(const DecArgs& a, const float (&p0)[S], const float (&p1)[S], float w0,
+                                        float w1, bool rot, int pos, int lane, float& v0, float& v1) {
+  v0 = 0.f;
+  v1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    v0 += p0[s];
+    v1 += p1[s];
+  }
+  if (rot) {
+    const float rs = 1.0f / sqrtf(wsum64(v0 * v0 + v1 * v1) / HD + a.eps);
+    const float a0 = v0 * rs * w0, a1 = v1 * rs * w1;
+    // angle pos * base^(-lane / 64), in double then reduced to [-pi, pi]
+    double ang = (double)pos * exp(-(double)lane * a.log_base / 64.0);
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    v0 = a0 * cs - a1 * sn;
+    v1 = a1 * cs + a0 * sn;
+  }
+}
+
 template <typename T, int S>
 __global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __restrict__ qkv) {
   const int lane = threadIdx.x & 63;
@@ -209,23 +237,8 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __
   const float* nw = hh < a.Hq ? a.q_norm : a.k_norm;
   const float w0 = nw[lane], w1 = nw[lane + 64];
   const int pos = a.pos[r], sq = a.seq[r];
-  float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    v0 += p0[s];
-    v1 += p1[s];
-  }
-  if (hh < a.Hq + a.Hkv) {
-    const float rs = 1.0f / sqrtf(wsum64(v0 * v0 + v1 * v1) / HD + a.eps);
-    const float a0 = v0 * rs * w0, a1 = v1 * rs * w1;
-    // angle pos * base^(-lane / 64), in double then reduced to [-pi, pi]
-    double ang = (double)pos * exp(-(double)lane * a.log_base / 64.0);
-    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
-    v0 = a0 * cs - a1 * sn;
-    v1 = a1 * cs + a0 * sn;
-  }
+  float v0, v1;
+  qk_head<S>(a, p0, p1, w0, w1, hh < a.Hq + a.Hkv, pos, lane, v0, v1);
   if (hh < a.Hq) {
     float* q = a.qf + ((int64_t)r * a.Hq + hh) * HD;
     q[lane] = v0;
@@ -249,25 +262,55 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(DecArgs a, const float* __
 //   16, kg + 32, kg + 48 with 16-byte loads, then the 16 key groups are
 //   added through LDS.
 constexpr int CHUNK = 64;
-template <typename T>
-__global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
+//
+// S > 0: the calls with one row per sequence.  The workgroup computes its two
+// query heads itself from the S qkv partials (qkv, the standalone pass's
+// helper), and the workgroup whose chunk holds the row's own position also
+// the new key and value: it writes them into the cache for later steps and
+// uses a copy in LDS (the same 16-bit values) for that key, since the
+// chunk's cache loads were issued before they were written.  No other row
+// of the call reads this sequence's cache, so the standalone pass can go.
+template <typename T, int S>
+__global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a, const float* __restrict__ qkv) {
   __shared__ float qs[2][HD];
   __shared__ float ps[2][CHUNK];
   __shared__ float red[2][8];
   __shared__ float ro[16][2][HD];
+  __shared__ __align__(16) T kvn[2][HD];  // S > 0: the new key and value (read as 16-byte vectors)
   const int it = blockIdx.x, kh = blockIdx.y, t = threadIdx.x;
   const int r = a.items[2 * it], c0 = a.items[2 * it + 1] * CHUNK;
   const int pos = a.pos[r], sq = a.seq[r];
   const int nk = min(CHUNK, pos + 1 - c0);  // keys of this chunk (>= 1)
+  const bool own = pos - c0 < CHUNK;        // the chunk holds position pos
   const T* Kc = (const T*)a.cache + ((((int64_t)a.layer * a.max_seqs + sq) * 2 + 0) * a.Hkv + kh) * a.max_pos * HD;
   const T* Vc = Kc + (int64_t)a.Hkv * a.max_pos * HD;
-  // Every global load of the workgroup -- the queries, then its K and V
-  // fragments, in the order of use (loads complete in order) -- is issued
-  // before the first wait: three dependent round trips to memory would
-  // otherwise set the time of this small kernel.
+  // Every global load of the workgroup -- the queries (or their partials),
+  // then its K and V fragments, in the order of use (loads complete in
+  // order) -- is issued before the first wait: three dependent round trips
+  // to memory would otherwise set the time of this small kernel.
   const int kk = t >> 2, part = t & 3;
   const int kg = t >> 4, dg = t & 15;
-  const float qv = a.qf[((int64_t)r * a.Hq + 2 * kh + (t >> 7)) * HD + (t & 127)];
+  const int wv = t >> 6, lane = t & 63;
+  [[maybe_unused]] float qv = 0.f;
+  [[maybe_unused]] float pq0[S > 0 ? S : 1], pq1[S > 0 ? S : 1];
+  [[maybe_unused]] float w0 = 0.f, w1 = 0.f;
+  if constexpr (S == 0) {
+    qv = a.qf[((int64_t)r * a.Hq + 2 * kh + (t >> 7)) * HD + (t & 127)];
+  } else {
+    // wavefronts 0, 1: query heads 2 kh, 2 kh + 1; 2: key head kh; 3: value
+    // head kh (the last two only in the chunk that holds pos)
+    const int nh = a.Hq + 2 * a.Hkv, ld = nh * HD;
+    const int hh = wv < 2 ? 2 * kh + wv : a.Hq + (wv - 2) * a.Hkv + kh;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float* pp = qkv + ((int64_t)s * a.rows + r) * ld + hh * HD;
+      pq0[s] = pp[lane];
+      pq1[s] = pp[lane + 64];
+    }
+    const float* nw = wv < 2 ? a.q_norm : a.k_norm;
+    w0 = nw[lane];
+    w1 = nw[lane + 64];
+  }
   // Keys past the chunk's end load key c0 (always present) and are zeroed
   // afterwards: guarded loads became branches that waited for each load.
   uint4 u[4], vv[4];
@@ -283,8 +326,36 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
     if (kk >= nk) u[i] = make_uint4(0, 0, 0, 0);
     if (kg + 16 * i >= nk) vv[i] = make_uint4(0, 0, 0, 0);
   }
-  qs[t >> 7][t & 127] = qv;
+  if constexpr (S == 0) {
+    qs[t >> 7][t & 127] = qv;
+  } else {
+    if (wv < 2 || own) {
+      float v0, v1;
+      qk_head<S>(a, pq0, pq1, w0, w1, wv < 3, pos, lane, v0, v1);
+      if (wv < 2) {
+        qs[wv][lane] = v0;
+        qs[wv][lane + 64] = v1;
+      } else {
+        const T e0 = Elem<T>::from_f(v0), e1 = Elem<T>::from_f(v1);
+        kvn[wv - 2][lane] = e0;
+        kvn[wv - 2][lane + 64] = e1;
+        T* c = (T*)(wv == 2 ? Kc : Vc) + (int64_t)pos * HD;
+        c[lane] = e0;
+        c[lane + 64] = e1;
+      }
+    }
+  }
   __syncthreads();
+  if constexpr (S > 0) {
+    // the new key and value replace what the chunk's loads found at pos
+    if (own && c0 + kk == pos) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) u[c] = *(const uint4*)&kvn[0][part * 32 + 8 * c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (own && c0 + kg + 16 * i == pos) vv[i] = *(const uint4*)&kvn[1][dg * 8];
+  }
   float d0 = 0.f, d1 = 0.f;
   if (kk < nk) {
 #pragma unroll
@@ -306,7 +377,6 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(DecArgs a) {
   d1 += dpp_f<0x4E>(d1);
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
   const float s0 = kk < nk ? d0 * scale : -INFINITY, s1 = kk < nk ? d1 * scale : -INFINITY;
-  const int wv = t >> 6;
   float m0 = wmax64(s0), m1 = wmax64(s1);
   if ((t & 63) == 0) {
     red[0][wv] = m0;
@@ -623,19 +693,31 @@ hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_dec(const DecArgs& a, int n_items, bool combine, int dtype, hipStream_t s) {
+hipError_t launch_attn_dec(const DecArgs& a, int n_items, bool combine, const float* qkv, int S, int dtype,
+                           hipStream_t s) {
   if (a.Hq != 2 * a.Hkv) return hipErrorInvalidValue;
+  if (dtype != DT_BF16 && dtype != DT_F16) return hipErrorInvalidValue;
+  if (S != 0 && S != 1 && S != 2 && S != 4 && S != 8) return hipErrorInvalidValue;
+  if (S && !qkv) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_items, (unsigned)a.Hkv);
   const dim3 cgrid((unsigned)a.rows, (unsigned)a.Hq);
-  if (dtype == DT_BF16) {
-    hipLaunchKernelGGL(attn_dec_kernel<bf16_t>, grid, dim3(256), 0, s, a);
-    if (combine) hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, cgrid, dim3(128), 0, s, a);
-  } else if (dtype == DT_F16) {
-    hipLaunchKernelGGL(attn_dec_kernel<f16_t>, grid, dim3(256), 0, s, a);
-    if (combine) hipLaunchKernelGGL(attn_combine_kernel<f16_t>, cgrid, dim3(128), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  auto go = [&](auto tt, auto sc) {
+    using T = decltype(tt);
+    constexpr int SC = decltype(sc)::value;
+    hipLaunchKernelGGL((attn_dec_kernel<T, SC>), grid, dim3(256), 0, s, a, qkv);
+    if (combine) hipLaunchKernelGGL(attn_combine_kernel<T>, cgrid, dim3(128), 0, s, a);
+  };
+  auto by_s = [&](auto tt) {
+    switch (S) {
+      case 0: go(tt, std::integral_constant<int, 0>{}); break;
+      case 1: go(tt, std::integral_constant<int, 1>{}); break;
+      case 2: go(tt, std::integral_constant<int, 2>{}); break;
+      case 4: go(tt, std::integral_constant<int, 4>{}); break;
+      default: go(tt, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  if (dtype == DT_BF16) by_s(bf16_t{});
+  else by_s(f16_t{});
   return hipGetLastError();
 }
 

@@ -163,7 +163,11 @@ hipError_t launch_add_rmsnorm(float* x, const float* part, int S, const float* w
 hipError_t launch_qk_rope(const DecArgs& a, const float* qkv, int S, int dtype, hipStream_t s);
 // attention over the chunk items -> part_o / part_ml; with combine, then
 // o16 = the combined output (else the output projection combines them).
-hipError_t launch_attn_dec(const DecArgs& a, int n_items, bool combine, int dtype, hipStream_t s);
+// S = 0: queries from qf (after launch_qk_rope).  S = 1, 2, 4 or 8, for calls
+// with one row per sequence: the kernel computes the queries and the new
+// key / value (cache append) itself from the S qkv partials.
+hipError_t launch_attn_dec(const DecArgs& a, int n_items, bool combine, const float* qkv, int S, int dtype,
+                           hipStream_t s);
 // The skinny product for at most GEMV_FUSE_ROWS rows with x computed from
 // its producer's partials: xm = 1, x = SwiGLU of the gate/up partials src
 // (S splits, K = F); xm = 2, x = the attention chunk partials of a combined
