@@ -76,6 +76,25 @@ def test_logmel_edge_lengths():
     assert np.all(split_rows(mel, T)[2] == -1.5)
 
 
+def test_logmel_many_sequences():
+    # more sequences than the kernel stages in LDS (128): the frame lookup
+    # then searches the tables in memory; short ragged clips, packed and padded
+    rng = np.random.default_rng(7)
+    lens = [int(n) for n in rng.integers(201, 2400, size=131)]
+    wavs = [rng.standard_normal(n).astype(np.float32) * 0.2 for n in lens]
+    say("logmel many sequences", len(wavs))
+    packed = gpu_logmel(wavs, layout=0)
+    padded = gpu_logmel(wavs, layout=1)
+    T = [n // 160 for n in lens]
+    assert packed.shape == (sum(T), 128)
+    err = 0.0
+    for i, (x, m) in enumerate(zip(wavs, split_rows(packed, T))):
+        err = max(err, float(np.abs(m - OL.log_mel(x)).max()))
+        assert np.array_equal(padded[i, :T[i]], m)
+    say("  max abs", err)
+    assert err <= MEL_TOL
+
+
 def test_logmel_long_stream_c3():
     w = synth.workload(3)
     wav = synth.make_clips(w)
