@@ -6,8 +6,10 @@
 // attends only to the rows of its own window: o = softmax(q k^T / 8) v.
 //
 // One workgroup per (window, head), or for windows longer than 256 keys per
-// (window, 64 queries, head) with the keys streamed through LDS.  Each
-// wavefront takes groups of 16 query rows and walks the keys in chunks of
+// (window, 128 queries, head) with the keys streamed through LDS (each
+// wavefront two interleaved groups of 16 queries that share every K and V
+// fragment read).  Each wavefront takes groups of 16 query rows and walks the
+// keys in chunks of
 // 64 with an online softmax (running maximum and output in fp32 registers;
 // probabilities enter the second product in the operand type).  Scores are computed
 // transposed, S^T = K Q^T, so that every lane owns one query row (its lane

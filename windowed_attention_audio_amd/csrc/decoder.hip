@@ -13,13 +13,16 @@
 // sums land in fixed slots and their consumers add them in order (no
 // atomics: results do not depend on timing).
 //   * qkv partials -> qk_rope_kernel: sum, RMSNorm of each q / k head,
-//     rotation, q kept in fp32, k and v written into the cache;
+//     rotation, q kept in fp32, k and v written into the cache (calls with
+//     one row per sequence do this inside the attention kernel instead);
 //   * attention: one workgroup per (row, key/value head, 64-key chunk), both
 //     query heads of the group; chunk partials (max, sum, output) combined
-//     by attn_combine_kernel;
+//     by attn_combine_kernel (at most GEMV_FUSE_ROWS rows: inside the output
+//     projection, gemv16x_kernel);
 //   * o and down partials -> add_rmsnorm_kernel: residual += sum, then the
 //     next RMSNorm;
-//   * gate/up partials (rows interleaved by 16) -> swiglu_kernel;
+//   * gate/up partials (rows interleaved by 16) -> swiglu_kernel (at most
+//     GEMV_FUSE_ROWS rows: inside the down projection);
 //   * the head: the tied embedding table, then a two-pass argmax.
 // Small kernels issue every load of their rows before the first use: at a
 // few rows per step, memory latency rather than bandwidth sets their time.
