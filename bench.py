@@ -252,6 +252,66 @@ def measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel, steps=10, warmup
             "step_tflops": round(fl / (ms * 1e-3) / 1e12, 1), "breakdown_ms_per_step": stages}
 
 
+def measure_varlen_adapter(W, synth, torch, np, weights, steps=5, warmup=2):
+    """The 32-clip variable-length packed batch (durations uniform in 2-60 s,
+    window 52) through the whole path with the SwiGLU adapter: audio-s/s of
+    log-mel + encoder + head + adapter, and the adapter's two products
+    (gate/up with the SwiGLU epilogue, down) against the MFMA peak."""
+    wl = synth.workload(4)
+    geom = synth.geom_for(wl)
+    wts = synth.with_adapter(weights, geom, bf16=True)
+    lens = wl.n_samples
+    lens_T = [n // 160 for n in lens]
+    dev_w = [torch.from_numpy(v).cuda() for v in wts.values()]
+    enc = W.mt_encoder_create(W.encoder_config(geom, W.MT_F16), dev_w)
+    torch.cuda.synchronize()
+    del dev_w
+    wav = torch.from_numpy(np.concatenate(synth.make_clips(wl))).cuda()
+    mel = torch.empty((sum(lens_T), 128), dtype=torch.float32, device="cuda")
+    M = sum(W.mt_encoder_frames(t) for t in lens_T)
+    out = torch.empty((M, geom["d_out"]), dtype=torch.float32, device="cuda")
+    ws_mel = torch.empty(W.mt_logmel_workspace_size(lens), dtype=torch.uint8, device="cuda")
+    ws_enc = torch.empty(W.mt_encode_workspace_size(enc, lens_T, wl.window), dtype=torch.uint8,
+                         device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream)
+        W.mt_encode(enc, mel, lens_T, wl.window, out=out, ws=ws_enc, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    stage = {}
+    for st in ("adapter_gu", "adapter_down"):
+        W.mt_trace_arm(st, max_launches=8)
+        W.mt_trace_collect()
+        step()
+        torch.cuda.synchronize()
+        stage[st] = round(W.mt_trace_collect()[0], 4)
+    W.mt_trace_arm(None)
+    flops = algorithmic_flops(geom, lens_T, wl.window)
+    ad_ms = stage["adapter_gu"] + stage["adapter_down"]
+    res = {"workload": wl.name, "clips": len(lens), "audio_s": round(sum(lens) / 16000.0, 2),
+           "window": wl.window, "encoder_frames": M, "ms_per_step": round(ms, 4),
+           "audio_s_per_s": round(sum(lens) / 16000.0 / (ms * 1e-3), 1),
+           "step_tflops": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
+           "adapter_ms": stage,
+           "adapter_tflops": round(flops["adapter"] / (ad_ms * 1e-3) / 1e12, 1),
+           "adapter_frac": round(flops["adapter"] / (ad_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del enc, wav, mel, out, ws_mel, ws_enc
+    torch.cuda.synchronize()
+    return res
+
+
 def measure_decoder(W, synth, torch, ctx=400, batches=(1, 16, 64), reps=20):
     """The language-model decoder step (Qwen3-1.7B geometry, bf16 weights,
     seeded N(0, 0.02^2) weights drawn on the device) over B sequences whose
@@ -343,7 +403,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
-    ap.add_argument("--only", choices=["2x", "decoder"],
+    ap.add_argument("--only", choices=["2x", "decoder", "varlen"],
                     help="run only this secondary measurement and print its JSON (for profiling)")
     ap.add_argument("--no-decoder", action="store_true",
                     help="skip the language-model decoder step")
@@ -351,6 +411,8 @@ def main():
                     help="skip the 2x-front-end full-attention workload")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the bounded-memory stream measurement (10-minute stream)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the 32-clip variable-length workload with the adapter")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before the steps, copy 256 MiB device-to-device once (a kernel of known "
                          "traffic, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -399,6 +461,9 @@ def main():
         return
     if args.only == "decoder":
         print(json.dumps(measure_decoder(W, synth, torch)), flush=True)
+        return
+    if args.only == "varlen":
+        print(json.dumps(measure_varlen_adapter(W, synth, torch, np, weights)), flush=True)
         return
 
     if args.copy_probe:
@@ -482,6 +547,8 @@ def main():
     if not args.no_stream:
         res["stream_10min"] = stream_measure(W, enc, synth, torch, np)
         res["prompt_splice"] = splice_measure(W, out, lens_T, synth, torch, np)
+    if not args.no_varlen:
+        res["varlen_adapter"] = measure_varlen_adapter(W, synth, torch, np, weights)
     if not args.no_2x:
         res["conv1d_2x_16x30s"] = measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel)
     if not args.no_decoder:

@@ -234,6 +234,24 @@ def make_weights(geom: dict, bf16: bool, seed: int = WEIGHT_SEED,
     return out
 
 
+def with_adapter(weights: dict, geom: dict, bf16: bool, adapter_seed: int = ADAPTER_SEED) -> dict:
+    """The weights of geom given those of the same geometry without the
+    adapter: the encoder tensors reused, the adapter tensors drawn as
+    make_weights draws them (their own generator), so the result equals
+    make_weights(geom, bf16) without drawing the encoder again."""
+    arng = np.random.Generator(np.random.PCG64(adapter_seed))
+    out = {}
+    for name, shape in weight_names(geom):
+        if name.startswith("adapter."):
+            a = arng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+            if bf16:
+                a = round_to_bf16(a)
+            out[name] = np.ascontiguousarray(a, dtype=np.float32)
+        else:
+            out[name] = weights[name]
+    return out
+
+
 def geom_for(w: Workload, **over) -> dict:
     g = dict(FULL_GEOM)
     g["adapter_hidden"] = w.adapter_hidden

@@ -258,3 +258,17 @@ def test_decode_rejects_null_decoder(L):
     assert L.mt_decode_workspace_size(None, 1, seq, pos, 1, 8, ctypes.byref(n)) == W.MT_ERR_INVALID_ARG
     assert L.mt_decode(None, None, 1, seq, pos, None, 1, 8, None, None, None, 0, None) == W.MT_ERR_INVALID_ARG
     assert L.mt_decoder_embedding(None) is None
+
+
+def test_with_adapter_equals_full_draw():
+    # the bench's variable-length workload adds the adapter to the main
+    # workload's weights; the result must be the full seeded draw
+    g0 = dict(synth.FULL_GEOM, n_layers=1, conv_ch=32, d_model=64, n_heads=1, d_ffn=128, d_out=64,
+              adapter_hidden=0)
+    g1 = dict(g0, adapter_hidden=128)
+    full = synth.make_weights(g1, bf16=True)
+    built = synth.with_adapter(synth.make_weights(g0, bf16=True), g1, bf16=True)
+    assert list(full) == list(built)
+    assert any(k.startswith("adapter.") for k in full)
+    for k in full:
+        assert np.array_equal(full[k], built[k]), k
