@@ -76,11 +76,13 @@ def test_logmel_edge_lengths():
     assert np.all(split_rows(mel, T)[2] == -1.5)
 
 
-def test_logmel_many_sequences():
-    # more sequences than the kernel stages in LDS (128): the frame lookup
-    # then searches the tables in memory; short ragged clips, packed and padded
+@pytest.mark.parametrize("nseq", [128, 131])
+def test_logmel_many_sequences(nseq):
+    # the most sequences whose tables the kernel stages in LDS (128), and more
+    # (the frame lookup then searches the tables in memory); short ragged
+    # clips, packed and padded
     rng = np.random.default_rng(7)
-    lens = [int(n) for n in rng.integers(201, 2400, size=131)]
+    lens = [int(n) for n in rng.integers(201, 2400, size=nseq)]
     wavs = [rng.standard_normal(n).astype(np.float32) * 0.2 for n in lens]
     say("logmel many sequences", len(wavs))
     packed = gpu_logmel(wavs, layout=0)
