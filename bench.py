@@ -4,18 +4,21 @@ A step is one pass of the whole forward path over one batch: waveform ->
 log-mel (mt_logmel) -> conv front-end, 32 windowed-attention layers and the
 encoder head (mt_encode).  The workload is 16 clips of 30 s of synthetic
 16 kHz audio (sum of three tones plus noise, 20 % silent gaps), bf16-valued
-weights, fp16 matrix operands with fp32 accumulation (the 16-bit operand type
-that meets the parity bar; bf16 operands are selectable with --operands bf16),
-window 104 encoder frames.
+weights, window 104 encoder frames.  The headline runs fp16 matrix operands
+with fp32 accumulation: the 16-bit operand type that meets the parity bar on
+every workload (bf16 activations miss it on the 32-clip adapter workload; the
+bf16-operand throughput is reported beside it as `bf16_operands`).
 Inputs are resident in device memory before the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-Prints one JSON line.  `value` is encoder audio-seconds per second.
+Prints one JSON line.  `value` is encoder audio-seconds per second over the
+median step of the K timed steps (each step bracketed by its own pair of HIP
+events on the launch stream; no stage timer is armed meanwhile).
 `roofline` describes the dominant kernel (the FFN up-projection GEMM with
-fused bias + GELU), timed live with HIP events on the launch stream during
-the timed steps; `cpu_baseline` times the CPU oracle on one clip of the same
-workload.
+fused bias + GELU), its launches timed with HIP events on the launch stream
+in a separate pass of the same steps; `cpu_baseline` times the CPU oracle on
+one clip of the same workload.
 """
 
 import argparse
@@ -86,11 +89,26 @@ def cpu_baseline(clip, weights, geom, window, min_seconds=10.0, max_clips=4):
     import numpy as np  # noqa: F401
     from oracle import encoder as OE
     from oracle import logmel as OL
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        info = threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in info] + [1])
+        libs = [p for p in info if p.get("user_api") == "blas"]
+        if libs:
+            blas = "%s %s (%s)" % (libs[0].get("internal_api"), libs[0].get("version"),
+                                   os.path.basename(libs[0].get("filepath", "")))
     except Exception:
         cores = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     P = OE.as_f64(weights)
     done, t0 = 0, time.perf_counter()
     while True:
@@ -103,7 +121,8 @@ def cpu_baseline(clip, weights, geom, window, min_seconds=10.0, max_clips=4):
     audio = done * len(clip) / 16000.0
     return {"value": audio / el, "unit": "audio-s/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} x 30 s clip (clip 0 of the 16 x 30 s workload): log-mel + "
-                      f"full encoder in NumPy float64, {el:.1f} s wall"}
+                      f"full encoder in NumPy float64, {el:.1f} s wall",
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(), "blas": blas}
 
 
 def stream_measure(W, enc, synth, torch, np, chunks=(8, 32), reps=4):
@@ -132,15 +151,26 @@ def stream_measure(W, enc, synth, torch, np, chunks=(8, 32), reps=4):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    res = {"workload": wl.name, "audio_s": n / 16000.0}
+    res = {"workload": wl.name, "audio_s": n / 16000.0,
+           "peak_note": "peak_bytes: the most device memory torch held during the measurement "
+                        "(waveform, output, workspaces; the library allocates none), packed "
+                        "weights excluded (weights_bytes)",
+           "weights_bytes": enc.packed.numel()}
+    base = torch.cuda.memory_allocated()
     for cw in chunks:
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
         nb = W.mt_encode_stream_workspace_size(enc, n, wl.window, cw)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
         ms = timed(lambda: W.mt_encode_stream(enc, dwav, wl.window, cw, out=out, ws=ws,
                                               stream=stream))
         res[f"chunk{cw}"] = {"ms": round(ms, 3), "audio_s_per_s": round(n / 16000.0 / (ms * 1e-3), 1),
-                             "workspace_bytes": nb}
+                             "workspace_bytes": nb,
+                             "peak_bytes": torch.cuda.max_memory_allocated() - base + dwav.numel() * 4
+                             + out.numel() * 4}
         del ws
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     mel = torch.empty((T, 128), dtype=torch.float32, device="cuda")
     ws_m = torch.empty(W.mt_logmel_workspace_size([n]), dtype=torch.uint8, device="cuda")
     ws_e = torch.empty(W.mt_encode_workspace_size(enc, [T], wl.window), dtype=torch.uint8,
@@ -152,7 +182,25 @@ def stream_measure(W, enc, synth, torch, np, chunks=(8, 32), reps=4):
 
     ms = timed(whole)
     res["whole"] = {"ms": round(ms, 3), "audio_s_per_s": round(n / 16000.0 / (ms * 1e-3), 1),
-                    "workspace_bytes": ws_m.numel() + ws_e.numel() + mel.numel() * 4}
+                    "workspace_bytes": ws_m.numel() + ws_e.numel() + mel.numel() * 4,
+                    "peak_bytes": torch.cuda.max_memory_allocated() - base + dwav.numel() * 4
+                    + out.numel() * 4}
+    # log-mel alone on the stream (the HBM-bound stage): per call, median of reps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(41)]
+    for _ in range(5):
+        W.mt_logmel(dwav, [n], mel=mel, ws=ws_m, stream=stream)
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(40):
+        W.mt_logmel(dwav, [n], mel=mel, ws=ws_m, stream=stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(40))
+    mel_ms = per[len(per) // 2]
+    alg = 4 * n + 4 * 128 * T
+    res["logmel"] = {"ms_median": round(mel_ms, 4), "algorithmic_bytes": alg,
+                     "GBps": round(alg / (mel_ms * 1e-3) / 1e9, 1),
+                     "frac_of_8TBps": round(alg / (mel_ms * 1e-3) / 8e12, 4)}
     return res
 
 
@@ -266,6 +314,9 @@ def measure_varlen_adapter(W, synth, torch, np, weights, steps=5, warmup=2):
     enc = W.mt_encoder_create(W.encoder_config(geom, W.MT_F16), dev_w)
     torch.cuda.synchronize()
     del dev_w
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     wav = torch.from_numpy(np.concatenate(synth.make_clips(wl))).cuda()
     mel = torch.empty((sum(lens_T), 128), dtype=torch.float32, device="cuda")
     M = sum(W.mt_encoder_frames(t) for t in lens_T)
@@ -306,7 +357,11 @@ def measure_varlen_adapter(W, synth, torch, np, weights, steps=5, warmup=2):
            "step_tflops": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
            "adapter_ms": stage,
            "adapter_tflops": round(flops["adapter"] / (ad_ms * 1e-3) / 1e12, 1),
-           "adapter_frac": round(flops["adapter"] / (ad_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+           "adapter_frac": round(flops["adapter"] / (ad_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "peak_bytes": torch.cuda.max_memory_allocated() - base,
+           "weights_bytes": enc.packed.numel(),
+           "peak_note": "peak_bytes: the most device memory torch held for the workload "
+                        "(waveform, log-mel, output, workspaces), packed weights excluded"}
     del enc, wav, mel, out, ws_mel, ws_enc
     torch.cuda.synchronize()
     return res
@@ -395,16 +450,104 @@ def measure_decoder(W, synth, torch, ctx=400, batches=(1, 16, 64), reps=20):
     return out
 
 
+def timed_steps(torch, fn, stream, steps):
+    """Runs fn() `steps` times, each bracketed by HIP events recorded on
+    `stream`; returns (median ms, mean ms, per-step ms)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    srt = sorted(per)
+    med = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
+    return med, evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def graph_replay(torch, fn, reps=50, warmup=10):
+    """Captures fn() (launches on the current stream) into a HIP graph and
+    times `reps` replays after `warmup`: (median ms, replay output equals the
+    eager output bitwise) -- fn returns the output tensor."""
+    stream = torch.cuda.current_stream()
+    ref = fn().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, ref))
+    med, _, _ = timed_steps(torch, g.replay, stream, reps)
+    torch.cuda.synchronize()
+    same = same and bool(torch.equal(out, ref))
+    del g
+    return med, same
+
+
+def latency_single_clip(W, synth, torch, np, weights_bf16):
+    """Time to a usable result for one clip: the 1 s clip with fp32 operands
+    (its own fp32 weights) and the 30 s clip with fp16 operands; mt_logmel +
+    mt_encode per call, eager and replayed as a HIP graph."""
+    res = {}
+    for cid, dt_name in ((0, "f32"), (1, "f16")):
+        wl = synth.workload(cid)
+        geom = synth.geom_for(wl)
+        if dt_name == "f32":
+            wts = synth.make_weights(geom, bf16=False)
+            dt = W.MT_F32
+        else:
+            wts = weights_bf16
+            dt = W.MT_F16
+        dev_w = [torch.from_numpy(v).cuda() for v in wts.values()]
+        enc = W.mt_encoder_create(W.encoder_config(geom, dt), dev_w)
+        torch.cuda.synchronize()
+        del dev_w
+        wav = torch.from_numpy(synth.make_clips(wl)[0]).cuda()
+        n = wav.numel()
+        T = n // 160
+        mel = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+        out = torch.empty((W.mt_encoder_frames(T), geom["d_out"]), dtype=torch.float32, device="cuda")
+        ws_m = torch.empty(W.mt_logmel_workspace_size([n]), dtype=torch.uint8, device="cuda")
+        ws_e = torch.empty(W.mt_encode_workspace_size(enc, [T], wl.window), dtype=torch.uint8, device="cuda")
+
+        def call():
+            s = torch.cuda.current_stream()
+            W.mt_logmel(wav, [n], mel=mel, ws=ws_m, stream=s)
+            W.mt_encode(enc, mel, [T], wl.window, out=out, ws=ws_e, stream=s)
+            return out
+
+        for _ in range(5):
+            call()
+        eager, _, _ = timed_steps(torch, call, torch.cuda.current_stream(), 30)
+        gms, same = graph_replay(torch, call, reps=30)
+        res[wl.name] = {"operands": dt_name, "ms_eager_median": round(eager, 4),
+                        "ms_graph_median": round(gms, 4), "graph_equals_eager": same,
+                        "audio_s_per_s_graph": round(n / 16000.0 / (gms * 1e-3), 1)}
+        enc.close()
+        del enc, wav, mel, out, ws_m, ws_e
+        torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
-    ap.add_argument("--only", choices=["2x", "decoder", "varlen"],
-                    help="run only this secondary measurement and print its JSON (for profiling)")
+    ap.add_argument("--only", choices=["2x", "decoder", "varlen", "headline"],
+                    help="run only this measurement and print its JSON (for profiling)")
     ap.add_argument("--no-decoder", action="store_true",
                     help="skip the language-model decoder step")
     ap.add_argument("--no-2x", action="store_true",
@@ -413,6 +556,8 @@ def main():
                     help="skip the bounded-memory stream measurement (10-minute stream)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the 32-clip variable-length workload with the adapter")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the graph replay, bf16-operand and single-clip latency lines")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before the steps, copy 256 MiB device-to-device once (a kernel of known "
                          "traffic, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -442,7 +587,6 @@ def main():
     op_dt = W.MT_F16 if args.operands == "f16" else W.MT_BF16
     enc = W.mt_encoder_create(W.encoder_config(geom, op_dt), dev_w)
     torch.cuda.synchronize()
-    del dev_w
     wav = torch.from_numpy(np.concatenate(clips)).cuda()
     mel = torch.empty((sum(lens_T), 128), dtype=torch.float32, device="cuda")
     M = sum(W.mt_encoder_frames(t) for t in lens_T)
@@ -452,17 +596,24 @@ def main():
                          device="cuda")
     stream = torch.cuda.current_stream()
 
+    def step_on(e, s):
+        W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=s)
+        W.mt_encode(e, mel, lens_T, window, out=out, ws=ws_enc, stream=s)
+        return out
+
     def step():
-        W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream)
-        W.mt_encode(enc, mel, lens_T, window, out=out, ws=ws_enc, stream=stream)
+        return step_on(enc, stream)
 
     if args.only == "2x":
+        del dev_w
         print(json.dumps(measure_2x(W, synth, torch, wav, lens, lens_T, mel, ws_mel)), flush=True)
         return
     if args.only == "decoder":
+        del dev_w
         print(json.dumps(measure_decoder(W, synth, torch)), flush=True)
         return
     if args.only == "varlen":
+        del dev_w
         print(json.dumps(measure_varlen_adapter(W, synth, torch, np, weights)), flush=True)
         return
 
@@ -478,24 +629,26 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    dominant = "fc1"
-    W.mt_trace_arm(dominant, max_launches=geom["n_layers"] * args.steps + 8)
-    W.mt_trace_collect()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    fc1_ms, fc1_n = W.mt_trace_collect()
-    W.mt_trace_arm(None)
+    # ---- the timed steps: no stage timer armed
+    ms, ms_mean, per_step = timed_steps(torch, step, stream, args.steps)
 
     audio_s = sum(lens) / 16000.0
     flops = algorithmic_flops(geom, lens_T, window)
     total_flops = sum(flops.values())
+    if args.only == "headline":
+        print(json.dumps({"ms_per_step": round(ms, 4), "value": round(audio_s / (ms * 1e-3), 2)}),
+              flush=True)
+        return
+
+    # ---- fc1 (the roofline kernel): its launches timed in a separate pass
+    fc1_steps = 5
+    W.mt_trace_arm("fc1", max_launches=geom["n_layers"] * fc1_steps + 8)
+    W.mt_trace_collect()
+    for _ in range(fc1_steps):
+        step()
+    torch.cuda.synchronize()
+    fc1_ms, fc1_n = W.mt_trace_collect()
+    W.mt_trace_arm(None)
     fc1_flops = 2.0 * M * geom["d_ffn"] * geom["d_model"]
     fc1_avg = fc1_ms / max(fc1_n, 1)
     fc1_tflops = fc1_flops / (fc1_avg * 1e-3) / 1e12
@@ -513,22 +666,26 @@ def main():
             breakdown[st] = round(t, 4)
         W.mt_trace_arm(None)
         mel_bytes = 4 * sum(lens) + 4 * 128 * sum(lens_T)
-        breakdown["mel_GBps"] = round(mel_bytes / (breakdown["mel"] * 1e-3) / 1e9, 1)
+        breakdown["mel_GBps"] = round(mel_bytes / ((breakdown["mel"] + breakdown["mel_norm"]) * 1e-3) / 1e9, 1)
 
     res = {
-        "metric": "encoder audio-sec/sec (bf16, batch 16 x 30 s clips); % of bf16 MFMA peak",
+        "metric": "encoder audio-sec/sec (batch 16 x 30 s clips, bf16-valued weights, fp16 matrix "
+                  "operands, fp32 accumulate); % of 16-bit MFMA peak",
         "value": round(audio_s / (ms * 1e-3), 2),
         "unit": "audio-s/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
+        "ms_per_step_min_max": [round(min(per_step), 4), round(max(per_step), 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": args.operands,
         "data": "synthetic (seeded tones + noise + silent gaps; seeded random weights)",
-        "config": {"workload": wl.name, "clips": len(lens), "clip_seconds": 30, "window": window,
+        "config": {"workload": wl.name.replace("bf16", "bf16w_%s_operands" % args.operands),
+                   "clips": len(lens), "clip_seconds": 30, "window": window,
                    "weights": "bf16 values", "operands": args.operands, "accumulate": "f32",
                    "mel_frames": sum(lens_T), "encoder_frames": M, "layers": geom["n_layers"]},
         "mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -538,12 +695,40 @@ def main():
                      "bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fc1_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": fc1_traffic_bytes(), "avg_launch_ms": round(fc1_avg, 5),
-                     "launches": fc1_n,
+                     "launches": fc1_n, "timing": "separate pass of %d steps" % fc1_steps,
                      "algorithmic_bytes": 2 * (M * geom["d_model"] + geom["d_ffn"] * geom["d_model"]
                                                + M * geom["d_ffn"])},
     }
     if breakdown:
         res["breakdown_ms_per_step"] = breakdown
+        gemm_st = ["conv2", "conv3", "conv_out", "qkv", "attn", "o", "fc1", "fc2", "proj1", "proj2"]
+        g_ms = sum(breakdown[s] for s in gemm_st)
+        g_fl = sum(flops[k] for k in ("conv2", "conv3", "conv_out", "qkv", "attn", "o", "ffn", "head"))
+        res["gemm_attn_frac"] = round(g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    if not args.no_extra:
+        gms, same = graph_replay(torch, lambda: step_on(enc, torch.cuda.current_stream()), reps=50,
+                                 warmup=10)
+        res["graph_replay"] = {"ms_per_step_median": round(gms, 4), "replays": 50, "warmup": 10,
+                               "audio_s_per_s": round(audio_s / (gms * 1e-3), 1),
+                               "equals_eager": same}
+        # the same batch with bf16 activations at the matrix cores
+        enc_b = W.mt_encoder_create(W.encoder_config(geom, W.MT_BF16 if op_dt == W.MT_F16 else W.MT_F16),
+                                    dev_w)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            step_on(enc_b, stream)
+        bms, _, _ = timed_steps(torch, lambda: step_on(enc_b, stream), stream, 20)
+        res["bf16_operands" if op_dt == W.MT_F16 else "f16_operands"] = {
+            "ms_per_step_median": round(bms, 4), "audio_s_per_s": round(audio_s / (bms * 1e-3), 1),
+            "mfma_frac": round(total_flops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "parity": "bf16 activations: within the bar on the 16 x 30 s batch and the 10-minute "
+                      "stream, outside it (max|d|/RMS > 0.02) on the 32-clip adapter workload"}
+        enc_b.close()
+        del enc_b
+    del dev_w
+    torch.cuda.synchronize()
+    if not args.no_extra:
+        res["single_clip_latency"] = latency_single_clip(W, synth, torch, np, weights)
     if not args.no_stream:
         res["stream_10min"] = stream_measure(W, enc, synth, torch, np)
         res["prompt_splice"] = splice_measure(W, out, lens_T, synth, torch, np)

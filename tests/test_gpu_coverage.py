@@ -1,0 +1,157 @@
+"""GPU parity, full-size workloads: every clip of the 16 x 30 s batch, bf16
+matrix operands, and the bounded-memory stream against the oracle.
+
+  * each of the 16 clips of the 16 x 30 s batch, encoded alone through all 32
+    layers, equals its rows of the batch bitwise (fp16 and bf16 operands), so
+    the oracle-sampled clips stand for every clip of the batch;
+  * bf16 activations at the matrix cores (MT_BF16): the 16 x 30 s batch and
+    the 10-minute stream within the parity bar; the 32-clip adapter workload
+    outside it (documented, bounded);
+  * mt_encode_stream (the 10-minute stream chunk by chunk) against the
+    oracle: the oracle's log-mel of the whole stream, each sampled window
+    encoded from its receptive field with the window's stream position.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import encoder as OE
+from oracle import logmel as OL
+from tests.helpers import GpuModel, assert_bf16_rows, gpu_logmel, row_metrics, split_rows
+
+pytestmark = pytest.mark.gpu
+
+FULL = synth.FULL_GEOM
+
+# bf16 activations on the adapter workload: max |diff| / RMS measured 0.027
+# (clip 9); the bound keeps a regression from going unnoticed, it is not the
+# parity bar (0.02), which this operand type does not meet there.
+BF16_ADAPTER_BOUND = 0.035
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def weights_bf16():
+    return synth.make_weights(FULL, bf16=True)
+
+
+@pytest.fixture(scope="module")
+def P64(weights_bf16):
+    return OE.as_f64(weights_bf16)
+
+
+@pytest.fixture(scope="module")
+def models(weights_bf16):
+    return {"f16": GpuModel(FULL, "f16", weights_bf16), "bf16": GpuModel(FULL, "bf16", weights_bf16)}
+
+
+@pytest.fixture(scope="module")
+def batch16():
+    w = synth.workload(2)
+    clips = synth.make_clips(w)
+    mel = gpu_logmel(clips)
+    return w, clips, split_rows(mel, [len(c) // 160 for c in clips])
+
+
+@pytest.fixture(scope="module")
+def stream10():
+    w = synth.workload(3)
+    wav = synth.make_clips(w)[0]
+    return w, wav, OL.log_mel(wav)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_batch16x30s_every_clip_alone_bitwise(models, batch16, dt):
+    w, _, mels = batch16
+    m = models[dt]
+    say(f"16x30s ({dt}): batch vs each clip alone")
+    rows = split_rows(m.encode(mels, w.window), [375] * 16)
+    for i, mel in enumerate(mels):
+        alone = m.encode([mel], w.window)
+        assert np.array_equal(alone, rows[i]), f"clip {i}: alone != its rows in the batch"
+
+
+def test_bf16_batch16x30s_sampled(models, batch16, P64):
+    w, clips, mels = batch16
+    got = split_rows(models["bf16"].encode(mels, w.window), [375] * 16)
+    for i in (0, 7, 15):
+        ref = OE.encode_clip(OL.log_mel(clips[i]), P64, FULL, w.window)
+        m = assert_bf16_rows(got[i], ref, what=f"bf16 16x30s clip {i}")
+        say(f"  bf16 clip {i}: min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def _stream_windows(got, ref_mel, P64, W, windows, N):
+    T = ref_mel.shape[0]
+    for k in windows:
+        s = max(0, 8 * (k * W - 1))
+        e = min(T, 8 * (k + 1) * W + 8)
+        seg = OE.encode_clip(ref_mel[s:e], P64, FULL, W, t0=s // 8)
+        r0 = k * W - s // 8
+        n = min(W, N - k * W)
+        yield k, got[k * W:k * W + n], seg[r0:r0 + n]
+
+
+def test_bf16_stream_10min_sampled_windows(models, stream10, P64):
+    w, wav, ref_mel = stream10
+    say("bf16 10 min stream")
+    got = models["bf16"].encode([gpu_logmel([wav])], w.window)
+    assert got.shape == (7500, 2048)
+    for k, g, r in _stream_windows(got, ref_mel, P64, w.window, (0, 1, 40, 72), 7500):
+        m = assert_bf16_rows(g, r, what=f"bf16 stream window {k}")
+        say(f"  window {k}: min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+@pytest.mark.parametrize("cw", [5, 1])
+def test_encode_stream_vs_oracle(models, stream10, P64, cw):
+    # the bounded-memory path itself (not the whole-stream path) against the
+    # oracle's definition of the stream's windows
+    import torch
+    import windowed_attention_audio_amd as W
+    w, wav, ref_mel = stream10
+    say(f"mt_encode_stream, {cw} window(s) per chunk, vs oracle")
+    got = W.mt_encode_stream(models["f16"].enc, torch.from_numpy(wav).cuda(), w.window, cw)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert got.shape == (7500, 2048)
+    for k, g, r in _stream_windows(got, ref_mel, P64, w.window, (0, 1, 40, 72), 7500):
+        m = assert_bf16_rows(g, r, what=f"stream chunk_windows={cw} window {k}")
+        say(f"  window {k}: min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def test_bf16_varlen_adapter_outside_bar(weights_bf16):
+    # bf16 activations through the SwiGLU adapter: the product of the gate
+    # and up projections doubles the tower's relative error, which puts the
+    # worst row past the 0.02 bar.  Cosine still meets its bar; max|d|/RMS is
+    # held to a documented bound.
+    w = synth.workload(4)
+    geom = synth.geom_for(w)
+    wts = synth.with_adapter(weights_bf16, geom, bf16=True)
+    ad = GpuModel(geom, "bf16", wts)
+    clips = synth.make_clips(w)
+    mel = gpu_logmel(clips)
+    T = [len(c) // 160 for c in clips]
+    N = [OE.encoder_frames(t) for t in T]
+    got = split_rows(ad.encode(split_rows(mel, T), w.window), N)
+    P = OE.as_f64(wts)
+    worst = 0.0
+    for i in (9, 6, 20):
+        ref = OE.encode_clip(OL.log_mel(clips[i]), P, geom, w.window)
+        m = row_metrics(got[i], ref)
+        say(f"  bf16 adapter clip {i}: min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+        assert m["cos"].min() >= 0.999
+        worst = max(worst, float(m["maxabs_rms"].max()))
+    assert worst <= BF16_ADAPTER_BOUND

@@ -107,7 +107,8 @@ def test_varlen_packed_adapter_sampled(weights_bf16):
     rows = split_rows(got, N)
     P = OE.as_f64(wts)
     order = np.argsort(N)
-    for i in (int(order[0]), int(order[len(order) // 2]), 5):
+    # shortest, median, longest, clip 9 (the worst of the bf16 operands) and two more
+    for i in (int(order[0]), int(order[len(order) // 2]), int(order[-1]), 9, 5, 20):
         ref = OE.encode_clip(OL.log_mel(clips[i]), P, geom, w.window)
         m = assert_bf16_rows(rows[i], ref, what=f"varlen clip {i} (N={N[i]})")
         say(f"  clip {i} N={N[i]}: min cos {m['cos'].min():.6f} "
