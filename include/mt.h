@@ -151,6 +151,19 @@ mt_status mt_logmel_workspace_size(const mt_batch* wav, size_t* bytes);
 mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* ws,
                     size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and output as mt_logmel, without a workspace argument.  The
+ * per-call tables and per-clip maxima live in a fixed array of the library,
+ * 128 KiB per device, reserved until the process ends; batches of more than
+ * MT_LOGMEL_NOALLOC_MAX_SEQS sequences get MT_ERR_WORKSPACE before anything
+ * runs.  Nothing is allocated on any call.  Every call on one device uses that
+ * device's array: calls that can overlap on one device (several streams or
+ * threads) race, and the caller must order them (for example on one
+ * stream).  Each call resets what it reads before use. */
+#define MT_LOGMEL_NOALLOC_MAX_SEQS 4096
+mt_status mt_logmel_noalloc(const float* wav, const mt_batch* wav_b, float* mel, void* stream);
+
 /* ---- encoder ---------------------------------------------------------- */
 
 /* Number of weight tensors create() expects for this geometry:

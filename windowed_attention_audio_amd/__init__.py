@@ -31,7 +31,7 @@ FRONTENDS = {"conv2d_8x": MT_FRONTEND_CONV2D_8X, "conv1d_2x": MT_FRONTEND_CONV1D
 
 EXPORTS = (
     "mt_mel_frames", "mt_encoder_frames", "mt_encoder_frames_for", "mt_logmel_workspace_size",
-    "mt_logmel",
+    "mt_logmel", "mt_logmel_noalloc",
     "mt_encoder_n_weights", "mt_encoder_packed_bytes", "mt_encoder_create",
     "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
     "mt_encode_stream_workspace_size", "mt_encode_stream",
@@ -91,6 +91,7 @@ def lib():
         L.mt_encoder_frames_for.argtypes = [ctypes.c_int32, ctypes.c_int64]
         L.mt_logmel_workspace_size.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(c_sz)]
         L.mt_logmel.argtypes = [vp, ctypes.POINTER(Batch), vp, vp, c_sz, vp]
+        L.mt_logmel_noalloc.argtypes = [vp, ctypes.POINTER(Batch), vp, vp]
         L.mt_encoder_n_weights.argtypes = [ctypes.POINTER(EncoderConfig)]
         L.mt_encoder_packed_bytes.argtypes = [ctypes.POINTER(EncoderConfig), ctypes.POINTER(c_sz)]
         L.mt_encoder_create.argtypes = [ctypes.POINTER(EncoderConfig), ctypes.POINTER(vp),
@@ -132,7 +133,8 @@ def lib():
         L.mt_status_string.restype = ctypes.c_char_p
         L.mt_status_string.argtypes = [ctypes.c_int]
         L.mt_last_error.restype = ctypes.c_char_p
-        for name in ("mt_logmel_workspace_size", "mt_logmel", "mt_encoder_packed_bytes",
+        for name in ("mt_logmel_workspace_size", "mt_logmel", "mt_logmel_noalloc",
+                     "mt_encoder_packed_bytes",
                      "mt_encoder_create", "mt_encode_workspace_size", "mt_encode",
                      "mt_encode_stream_workspace_size", "mt_encode_stream",
                      "mt_prompt_embed_workspace_size", "mt_prompt_embed",
@@ -207,6 +209,29 @@ def mt_logmel(wav, lens, layout=MT_PACKED, max_len=0, mel=None, ws=None, stream=
                            ctypes.c_void_p(mel.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                            ws.numel(), _stream_ptr(stream)))
     return mel
+
+
+def mt_logmel_noalloc(wav, lens, layout=MT_PACKED, max_len=0, mel=None, stream=None):
+    """mt_logmel without a workspace (the library's fixed per-device scratch
+    array holds the tables and per-clip maxima; at most
+    MT_LOGMEL_NOALLOC_MAX_SEQS sequences; calls on one device must not
+    overlap)."""
+    import torch
+    assert wav.is_cuda and wav.dtype == torch.float32 and wav.is_contiguous()
+    if layout == MT_PADDED:
+        max_len = wav.shape[1]
+        shape = (len(lens), max_len // 160, 128)
+    else:
+        shape = (sum(int(n) // 160 for n in lens), 128)
+    b = make_batch(lens, layout, max_len)
+    if mel is None:
+        mel = torch.empty(shape, dtype=torch.float32, device=wav.device)
+    _check(lib().mt_logmel_noalloc(ctypes.c_void_p(wav.data_ptr()), ctypes.byref(b),
+                                   ctypes.c_void_p(mel.data_ptr()), _stream_ptr(stream)))
+    return mel
+
+
+MT_LOGMEL_NOALLOC_MAX_SEQS = 4096
 
 
 def encoder_config(geom: dict, dtype: int, with_head: bool = True, ln_eps: float = 1e-5):

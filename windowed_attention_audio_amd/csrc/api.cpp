@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <cmath>
 #include <string>
 #include <vector>
@@ -653,6 +654,72 @@ mt_status stream_mel(const float* wav, int64_t n, int64_t m0, int64_t nf, float*
   return MT_OK;
 }
 
+// ------------------------------------------------------------- log-mel launch
+// The launch sequence of mt_logmel on a planned batch, with its tables and
+// per-clip maxima in `w` (the caller's workspace, or the fixed scratch array
+// of mt_logmel_noalloc): table upload, the maxima set to -inf, the frame
+// kernel, the clamp pass.
+mt_status run_logmel(const float* wav, const mt_batch* wav_b, const MelPlan& p, float* mel, char* w,
+                     hipStream_t s) {
+  // one upload: sample_off | row_off | seq_len | cu_frames (contiguous regions)
+  std::vector<uint32_t> words(p.off_gmax / 4, 0);
+  memcpy((char*)words.data() + p.off_sample, p.sample_off.data(), 8 * (size_t)p.B);
+  memcpy((char*)words.data() + p.off_row, p.row_off.data(), 8 * (size_t)p.B);
+  memcpy((char*)words.data() + p.off_len, p.seq_len.data(), 4 * (size_t)p.B);
+  memcpy((char*)words.data() + p.off_cu, p.cu_frames.data(), 4 * (size_t)(p.B + 1));
+  HIP_TRY(upload_words((uint32_t*)w, words.data(), (int64_t)words.size(), s), "upload tables");
+  int* gmax = (int*)(w + p.off_gmax);
+  const float ninf = -INFINITY;
+  int key;
+  memcpy(&key, &ninf, 4);
+  key = key >= 0 ? key : key ^ 0x7fffffff;
+  HIP_TRY(launch_fill_i32(gmax, key, p.B, s), "fill");
+  MelArgs a;
+  a.wav = wav;
+  a.mel = mel;
+  a.seq_sample_off = (const int64_t*)(w + p.off_sample);
+  a.seq_len = (const int32_t*)(w + p.off_len);
+  a.cu_frames = (const int32_t*)(w + p.off_cu);
+  a.seq_row_off = (const int64_t*)(w + p.off_row);
+  a.gmax = gmax;
+  a.nseq = p.B;
+  a.total_frames = p.total_frames;
+  a.out_rows = p.out_rows;
+  a.padded = wav_b->layout == MT_PADDED;
+  a.frame_off = 0;
+  STAGE(launch_mel(a, s), "mel");
+  STAGE(launch_mel_norm(a, p.tmax, s), "mel_norm");
+  return MT_OK;
+}
+
+// ------------------------------------------------------------- fixed scratch
+// mt_logmel_noalloc's tables and per-clip maxima: a fixed device array, one
+// copy per device, kept until the process ends.  Host code uses the address
+// hipGetSymbolAddress returns for the current device (taken once per device,
+// with that device current), never the array's name, which in host code is
+// only a stand-in for the symbol.
+constexpr size_t NOALLOC_SCRATCH_BYTES = 128 << 10;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+mt_status scratch_for_current_device(char** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MT_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr || (uintptr_t)ptr % ALIGN)
+      return fail(MT_ERR_HIP, "hipGetSymbolAddress(scratch) gave an unusable address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return MT_OK;
+}
+
 }  // namespace
 
 // ================================================================== decoder
@@ -1074,37 +1141,25 @@ mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* w
     return fail(MT_ERR_INVALID_ARG, "mt_logmel: ws must be 256-byte and mel 16-byte aligned");
   if (ws_bytes < p.bytes)
     return fail(MT_ERR_WORKSPACE, "mt_logmel: workspace %zu bytes < required %zu", ws_bytes, p.bytes);
-  hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  // one upload: sample_off | row_off | seq_len | cu_frames (contiguous regions)
-  std::vector<uint32_t> words(p.off_gmax / 4, 0);
-  memcpy((char*)words.data() + p.off_sample, p.sample_off.data(), 8 * (size_t)p.B);
-  memcpy((char*)words.data() + p.off_row, p.row_off.data(), 8 * (size_t)p.B);
-  memcpy((char*)words.data() + p.off_len, p.seq_len.data(), 4 * (size_t)p.B);
-  memcpy((char*)words.data() + p.off_cu, p.cu_frames.data(), 4 * (size_t)(p.B + 1));
-  HIP_TRY(upload_words((uint32_t*)w, words.data(), (int64_t)words.size(), s), "upload tables");
-  int* gmax = (int*)(w + p.off_gmax);
-  const float ninf = -INFINITY;
-  int key;
-  memcpy(&key, &ninf, 4);
-  key = key >= 0 ? key : key ^ 0x7fffffff;
-  HIP_TRY(launch_fill_i32(gmax, key, p.B, s), "fill");
-  MelArgs a;
-  a.wav = wav;
-  a.mel = mel;
-  a.seq_sample_off = (const int64_t*)(w + p.off_sample);
-  a.seq_len = (const int32_t*)(w + p.off_len);
-  a.cu_frames = (const int32_t*)(w + p.off_cu);
-  a.seq_row_off = (const int64_t*)(w + p.off_row);
-  a.gmax = gmax;
-  a.nseq = p.B;
-  a.total_frames = p.total_frames;
-  a.out_rows = p.out_rows;
-  a.padded = wav_b->layout == MT_PADDED;
-  a.frame_off = 0;
-  STAGE(launch_mel(a, s), "mel");
-  STAGE(launch_mel_norm(a, p.tmax, s), "mel_norm");
-  return MT_OK;
+  return run_logmel(wav, wav_b, p, mel, (char*)ws, (hipStream_t)stream);
+}
+
+mt_status mt_logmel_noalloc(const float* wav, const mt_batch* wav_b, float* mel, void* stream) {
+  MelPlan p;
+  mt_status st = plan_mel(wav_b, p);
+  if (st != MT_OK) return st;
+  if (!wav || !mel) return fail(MT_ERR_INVALID_ARG, "mt_logmel_noalloc: NULL device pointer");
+  if ((uintptr_t)mel % 16) return fail(MT_ERR_INVALID_ARG, "mt_logmel_noalloc: mel must be 16-byte aligned");
+  // 4096 sequences take 114 944 bytes of tables and maxima
+  if (p.B > MT_LOGMEL_NOALLOC_MAX_SEQS || p.bytes > NOALLOC_SCRATCH_BYTES)
+    return fail(MT_ERR_WORKSPACE,
+                "mt_logmel_noalloc: %d sequences need %zu bytes of scratch, more than the library's "
+                "fixed %zu (at most %d sequences)", p.B, p.bytes, NOALLOC_SCRATCH_BYTES,
+                MT_LOGMEL_NOALLOC_MAX_SEQS);
+  char* w = nullptr;
+  st = scratch_for_current_device(&w);
+  if (st != MT_OK) return st;
+  return run_logmel(wav, wav_b, p, mel, w, (hipStream_t)stream);
 }
 
 int32_t mt_encoder_n_weights(const mt_encoder_config* cfg) {
