@@ -1,10 +1,14 @@
 """Builds libmt.so (the HIP kernels and the C ABI) for gfx950 in-tree.
 
-    python -m windowed_attention_audio_amd.build [--host-only]
+    python -m windowed_attention_audio_amd.build [--host-check]
 
---host-only additionally builds libmt_host_check.so from api.cpp with g++ and
-stub launchers, so the argument validation can be run under sanitizers on a
-machine without a GPU (used by the CPU test-suite).
+--host-check instead builds _build/host_abi_check: the C ABI (api.cpp)
+compiled with g++ under AddressSanitizer and UndefinedBehaviorSanitizer,
+linked with the stub launchers of csrc/host_stubs.cpp (no GPU code; every
+"device" pointer is host memory and each launcher touches the ends of the
+ranges its kernel would access) and the driver tests/host_abi_check.cpp,
+which calls every rejection path of every entry point and valid calls on
+exactly sized buffers.  The CPU test-suite builds and runs it.
 """
 
 import concurrent.futures as cf
@@ -81,5 +85,34 @@ def build(verbose=False):
     return LIB
 
 
+HOST_CHECK = os.path.join(BUILD, "host_abi_check")
+
+
+def rocm_include():
+    root = os.environ.get("ROCM_PATH") or os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    return os.path.join(root, "include")
+
+
+def build_host_check():
+    """The sanitizer build of the C ABI on the host (see the module docstring);
+    returns the path of the executable."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = HOST_CHECK + ".tmp"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-D__align__(x)=__attribute__((aligned(x)))",
+           "-DHIP_SYMBOL(x)=x", "-I", rocm_include(), "-I", INCLUDE, "-I", CSRC,
+           "-x", "c++", os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "host_stubs.cpp"),
+           os.path.join(ROOT, "tests", "host_abi_check.cpp"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building the host check failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, HOST_CHECK)
+    return HOST_CHECK
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--host-check" in sys.argv[1:]:
+        print(build_host_check())
+    else:
+        print(build(verbose=True))

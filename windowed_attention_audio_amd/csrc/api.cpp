@@ -351,6 +351,15 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   if (weff > MAX_WINDOW && enc->dt == DT_F32)
     return fail(MT_ERR_UNSUPPORTED, "mt_encode: window %d over sequences of up to %lld frames "
                 "exceeds the fp32 on-chip maximum %d", window, (long long)p.maxN, MAX_WINDOW);
+  // Windows longer than MAX_WINDOW stream their keys: that kernel addresses a
+  // window's rows of the qkv buffer (3 d_model values each) with 32-bit byte
+  // offsets, reaching up to four 64-row tiles past the window's end.
+  const int64_t w_rows = (weff + 63) / 64 * 64 + 256;
+  if (enc->dt != DT_F32 && weff > MAX_WINDOW && w_rows * 3 * (int64_t)c.d_model * (int64_t)enc->es > INT32_MAX)
+    return fail(MT_ERR_UNSUPPORTED, "mt_encode: a window of %lld frames is too long for 32-bit offsets "
+                "(at most %lld frames at d_model %d)", (long long)weff,
+                (long long)(INT32_MAX / (3 * (int64_t)c.d_model * (int64_t)enc->es) - 256) / 64 * 64,
+                c.d_model);
   p.wpad = (int)((weff + 63) / 64 * 64);  // whole key chunks of 64 (on chip up to MAX_WINDOW)
   p.out_stride = mb->layout == MT_PADDED ? frames_of(c.frontend, mb->max_len) : 0;
 
