@@ -229,7 +229,19 @@ mt_status mt_encode_workspace_size(const mt_encoder* enc, const mt_batch* mel_b,
  *           d_model when with_head == 0).  MT_FRONTEND_CONV1D_2X with
  *           with_head == 1: ln_post of the residual stream, fp32.
  *   ws      device workspace of >= mt_encode_workspace_size bytes, 256-byte
- *           aligned; its contents on entry do not matter. */
+ *           aligned; its contents on entry do not matter.
+ * fp16 range: with MT_F16 operands every value converted to fp16 is clamped
+ * to +-65504, and the clamps are reported: once the call's work has run (in
+ * stream order), the first 32-bit word of ws holds a mask of MT_SAT_* bits,
+ * one per stage that clamped at least one value (0: none).  Other operand
+ * types leave it 0.  The attention kernel's fp16 values need no report: its
+ * probabilities lie in [0, 256] and its outputs within the range of v. */
+#define MT_SAT_FRONTEND 1 /* conv1, conv2, conv3 outputs (2x: conv1) */
+#define MT_SAT_LN 2       /* LayerNorm outputs (ln1, ln2) */
+#define MT_SAT_QKV 4      /* q, k, v */
+#define MT_SAT_FFN 8      /* FFN hidden (GELU of fc1) */
+#define MT_SAT_HEAD 16    /* ln_post and GELU(proj1) hi/lo pairs */
+#define MT_SAT_ADAPTER 32 /* proj2 output into the adapter, SwiGLU hidden */
 mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel_b,
                     int32_t window, float* out, void* ws, size_t ws_bytes, void* stream);
 
@@ -246,7 +258,8 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
  * field (8 frames before, none after) and the encoder.  The result equals
  * mt_logmel + mt_encode of the whole stream with the same window.  Only the
  * 8x front-end streams: an MT_FRONTEND_CONV1D_2X encoder gives
- * MT_ERR_UNSUPPORTED. */
+ * MT_ERR_UNSUPPORTED.  The first 32-bit word of ws holds the fp16 saturation
+ * mask of the whole stream, as for mt_encode. */
 mt_status mt_encode_stream_workspace_size(const mt_encoder* enc, int64_t n_samples, int32_t window,
                                           int32_t chunk_windows, size_t* bytes);
 mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_samples,

@@ -155,3 +155,39 @@ def test_bf16_varlen_adapter_outside_bar(weights_bf16):
         assert m["cos"].min() >= 0.999
         worst = max(worst, float(m["maxabs_rms"].max()))
     assert worst <= BF16_ADAPTER_BOUND
+
+
+def test_fp16_saturation_is_reported(weights_bf16):
+    # fp16 operands clamp at +-65504; the clamp must be reported in the
+    # workspace's saturation mask, not pass silently.  One layer whose fc1
+    # weights are scaled by 2^17 (exact in bf16 and fp16) drives the FFN hidden
+    # activations far past the fp16 range.
+    import torch
+    import windowed_attention_audio_amd as W
+    geom = dict(FULL, n_layers=1)
+    names = [n for n, _ in synth.weight_names(geom)]
+    base = {n: weights_bf16[n] for n in names}
+    big = dict(base)
+    big["layers.0.fc1.weight"] = (base["layers.0.fc1.weight"] * np.float32(2.0 ** 17)).astype(np.float32)
+    mel = torch.from_numpy(OL.log_mel(synth.make_clips(synth.workload(1))[0]).astype(np.float32)).cuda()
+    T = [mel.shape[0]]
+
+    def mask(weights, dt):
+        m = GpuModel(geom, dt, weights)
+        ws = torch.full((W.mt_encode_workspace_size(m.enc, T, 104),), 255, dtype=torch.uint8, device="cuda")
+        out = W.mt_encode(m.enc, mel, T, 104, ws=ws)
+        return W.saturation_mask(ws), out
+
+    assert mask(base, "f16")[0] == 0
+    got, out = mask(big, "f16")
+    say(f"  fp16 mask with fc1 x 2^17: {got}")
+    assert got & W.MT_SAT_FFN
+    assert bool(torch.isfinite(out).all())  # clamped, not inf
+    assert mask(big, "bf16")[0] == 0  # bf16 keeps fp32's range: nothing clamps
+    # the stream path reports into the first word of its own workspace
+    m = GpuModel(geom, "f16", big)
+    wav = torch.from_numpy(synth.make_clips(synth.workload(1))[0]).cuda()
+    ws = torch.full((W.mt_encode_stream_workspace_size(m.enc, wav.numel(), 104, 1),), 255, dtype=torch.uint8,
+                    device="cuda")
+    W.mt_encode_stream(m.enc, wav, 104, 1, ws=ws)
+    assert W.saturation_mask(ws) & W.MT_SAT_FFN

@@ -233,6 +233,16 @@ def mt_logmel_noalloc(wav, lens, layout=MT_PACKED, max_len=0, mel=None, stream=N
 
 MT_LOGMEL_NOALLOC_MAX_SEQS = 4096
 
+# fp16 saturation mask (first 32-bit word of an encode workspace after the call)
+MT_SAT_FRONTEND, MT_SAT_LN, MT_SAT_QKV, MT_SAT_FFN, MT_SAT_HEAD, MT_SAT_ADAPTER = 1, 2, 4, 8, 16, 32
+
+
+def saturation_mask(ws) -> int:
+    """The MT_SAT_* mask an mt_encode / mt_encode_stream call left in its
+    workspace `ws` (a uint8 CUDA tensor); synchronises the stream."""
+    import torch
+    return int(ws[:4].view(torch.int32).item())
+
 
 def encoder_config(geom: dict, dtype: int, with_head: bool = True, ln_eps: float = 1e-5):
     """geom["frontend"]: "conv2d_8x" (default) or "conv1d_2x"."""

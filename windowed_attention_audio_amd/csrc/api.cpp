@@ -48,6 +48,7 @@ mt_status hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 constexpr int64_t HOP = 160;
+constexpr int TABLE_HEAD_WORDS = 64;  // the encode workspace's first 256 bytes: the saturation mask
 constexpr int MAX_WINDOW = 256;
 constexpr int64_t MAX_SEQS = 1 << 20;
 constexpr size_t ALIGN = 256;
@@ -319,8 +320,10 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   const mt_encoder_config& c = enc->cfg;
   const int B = mb->n_seqs;
   p.B = B;
-  p.words.assign(5 * (size_t)(B + 1), 0);
-  int32_t* cuT = p.words.data();
+  // word 0: the fp16 saturation mask (reset to 0 by the table upload), then
+  // padding to 256 bytes, then cu_T | cu_T1 | cu_T2 | cu_N | cu_win
+  p.words.assign(TABLE_HEAD_WORDS + 5 * (size_t)(B + 1), 0);
+  int32_t* cuT = p.words.data() + TABLE_HEAD_WORDS;
   int32_t* cuT1 = cuT + (B + 1);
   int32_t* cuT2 = cuT1 + (B + 1);
   int32_t* cuN = cuT2 + (B + 1);
@@ -419,19 +422,23 @@ namespace {
 
 // Launches the whole encoder for a planned batch (validated by the caller).
 mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, int32_t window,
-                     float* out, char* w, hipStream_t s, const StreamChunk* ch) {
+                     float* out, char* w, hipStream_t s, const StreamChunk* ch, int* sat_word) {
   const mt_encoder_config& c = enc->cfg;
   const int dt = enc->dt;
   const int B = p.B;
   int M = (int)p.M;
   const int C = c.conv_ch, D = c.d_model, F = c.d_ffn, O = c.d_out, A = c.adapter_hidden;
 
-  // tables: words (cu_T | cu_T1 | cu_T2 | cu_N | cu_win), then mel row offsets
+  // tables: the saturation mask word (zeroed here) and padding, words (cu_T |
+  // cu_T1 | cu_T2 | cu_N | cu_win), then mel row offsets
   HIP_TRY(upload_words((uint32_t*)(w + p.o_words), (const uint32_t*)p.words.data(),
                        (int64_t)p.words.size(), s), "upload tables");
   HIP_TRY(upload_words((uint32_t*)(w + p.o_rowoff), (const uint32_t*)p.mel_row_off.data(),
                        2 * (int64_t)B, s), "upload tables");
-  const int32_t* cuT = (const int32_t*)(w + p.o_words);
+  // fp16 conversions report clamps at +-65504 into the mask (a stream's
+  // chunks share the one word of the stream's workspace)
+  int* sat = dt == DT_F16 ? (sat_word ? sat_word : (int*)(w + p.o_words)) : nullptr;
+  const int32_t* cuT = (const int32_t*)(w + p.o_words) + TABLE_HEAD_WORDS;
   const int32_t* cuT1 = cuT + (B + 1);
   const int32_t* cuT2 = cuT1 + (B + 1);
   const int32_t* cuN = cuT2 + (B + 1);
@@ -448,9 +455,11 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   void* ahid = w + p.o_ahid;
 
   auto gemm = [&](const void* A_, int64_t lda, const void* B_, int64_t ldb, int M_, int N_, int K_,
-                  const float* bias, void* C_, int64_t ldc) {
+                  const float* bias, void* C_, int64_t ldc, int sat_bit = 0) {
     GemmArgs g_ = ::gemm(A_, lda, B_, ldb, M_, N_, K_, bias, C_, ldc);
     g_.zeros = enc->zeros;
+    g_.sat = sat_bit ? sat : nullptr;
+    g_.sat_bit = sat_bit;
     return g_;
   };
 
@@ -461,7 +470,7 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
     STAGE(launch_rows_to_half(mel, (const int64_t*)(w + p.o_rowoff), cuT, B, p.sumT, c.n_mels, act2, dt,
                               s), "mel16");
     GemmArgs g = gemm(act2, 0, enc->conv1_w, 3 * c.n_mels, (int)p.sumT, D, 3 * c.n_mels, enc->conv1_b,
-                      act1, D);
+                      act1, D, SAT_FRONTEND);
     g.conv_C = c.n_mels;
     g.conv_Fin = 1;
     g.conv_Fout = 1;
@@ -494,9 +503,11 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   c1.out = act1;
   c1.C = C;
   c1.dtype = dt;
+  c1.sat = sat;
   STAGE(launch_conv1(c1, s), "conv1");
 
-  GemmArgs g = gemm(act1, 0, enc->conv2_w, 9 * C, (int)(p.sumT2 * 32), C, 9 * C, enc->conv2_b, act2, C);
+  GemmArgs g = gemm(act1, 0, enc->conv2_w, 9 * C, (int)(p.sumT2 * 32), C, 9 * C, enc->conv2_b, act2, C,
+                    SAT_FRONTEND);
   g.conv_C = C;
   g.conv_Fin = 64;
   g.conv_Fout = 32;
@@ -504,7 +515,7 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   g.cu_out = cuT2;
   g.nseq = B;
   STAGE(launch_gemm(g, EPI_GELU, dt, true, s), "conv2");
-  g = gemm(act2, 0, enc->conv3_w, 9 * C, (int)(p.M * 16), C, 9 * C, enc->conv3_b, act3, C);
+  g = gemm(act2, 0, enc->conv3_w, 9 * C, (int)(p.M * 16), C, 9 * C, enc->conv3_b, act3, C, SAT_FRONTEND);
   g.conv_C = C;
   g.conv_Fin = 32;
   g.conv_Fout = 16;
@@ -544,12 +555,13 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   const bool half = dt != DT_F32;
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = enc->layers[l];
-    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, dt, false, s), "ln1");
-    STAGE(launch_gemm(gemm(h, D, L.wqkv, D, M, 3 * D, D, L.bqkv, qkv, 3 * D), EPI_ACT, dt, false, s), "qkv");
+    STAGE(launch_layernorm(x, L.ln1_g, L.ln1_b, h, M, D, c.ln_eps, dt, false, s, sat, SAT_LN), "ln1");
+    STAGE(launch_gemm(gemm(h, D, L.wqkv, D, M, 3 * D, D, L.bqkv, qkv, 3 * D, SAT_QKV), EPI_ACT, dt, false, s),
+          "qkv");
     STAGE(launch_attention(aa, dt, s), "attn");
     STAGE(launch_gemm(gemm(att, D, L.wo, D, M, D, D, L.bo, x, D), EPI_RESID, dt, false, s), "o");
-    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, dt, false, s), "ln2");
-    STAGE(launch_gemm(gemm(h, D, L.w1, D, M, F, D, L.b1, ffn, F), EPI_GELU, dt, false, s), "fc1");
+    STAGE(launch_layernorm(x, L.ln2_g, L.ln2_b, h, M, D, c.ln_eps, dt, false, s, sat, SAT_LN), "ln2");
+    STAGE(launch_gemm(gemm(h, D, L.w1, D, M, F, D, L.b1, ffn, F, SAT_FFN), EPI_GELU, dt, false, s), "fc1");
     STAGE(launch_gemm(gemm(ffn, F, L.w2, F, M, D, F, L.b2, x, D), EPI_RESID, dt, false, s), "fc2");
   }
 
@@ -566,17 +578,19 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
     out_d = O;
     // 16-bit operands: the head's activations enter as hi/lo pairs (K doubled)
     const int KD = half ? 2 * D : D;
-    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt, half, s), "ln_post");
-    STAGE(launch_gemm(gemm(h, KD, enc->wp1, KD, M, D, KD, enc->bp1, ffn, KD),
+    STAGE(launch_layernorm(x, enc->lnp_g, enc->lnp_b, h, M, D, c.ln_eps, dt, half, s, sat, SAT_HEAD),
+          "ln_post");
+    STAGE(launch_gemm(gemm(h, KD, enc->wp1, KD, M, D, KD, enc->bp1, ffn, KD, SAT_HEAD),
                         half ? EPI_GELU_SPLIT : EPI_GELU, dt, false, s), "proj1");
-    GemmArgs g2 = gemm(ffn, KD, enc->wp2, KD, M, O, KD, enc->bp2, A ? ybuf : (void*)out, O);
+    GemmArgs g2 = gemm(ffn, KD, enc->wp2, KD, M, O, KD, enc->bp2, A ? ybuf : (void*)out, O,
+                       A ? SAT_ADAPTER : 0);
     g2.cu_rows = cuN;
     g2.nseq = ch ? 1 : B;
     g2.out_seq_stride = A ? 0 : stride;
     STAGE(launch_gemm(g2, A ? EPI_ACT : EPI_OUT, dt, false, s), "proj2");
     if (A) {
-      STAGE(launch_gemm(gemm(ybuf, O, enc->wgu, O, M, 2 * A, O, nullptr, ahid, A), EPI_SWIGLU, dt,
-                          false, s), "adapter_gu");
+      STAGE(launch_gemm(gemm(ybuf, O, enc->wgu, O, M, 2 * A, O, nullptr, ahid, A, SAT_ADAPTER), EPI_SWIGLU,
+                        dt, false, s), "adapter_gu");
       GemmArgs g3 = gemm(ahid, A, enc->wd, A, M, O, A, nullptr, out, O);
       g3.cu_rows = cuN;
       g3.nseq = ch ? 1 : B;
@@ -601,7 +615,7 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
 struct StreamPlan {
   int64_t n = 0, T = 0, N = 0, Fc = 0, Tc = 0;  // samples, mel frames, encoder frames,
                                                 // frames per chunk, largest chunk's mel frames
-  size_t off_tab = 0, off_gmax = 0, off_mel = 0, off_enc = 0, bytes = 0;
+  size_t off_sat = 0, off_tab = 0, off_gmax = 0, off_mel = 0, off_enc = 0, bytes = 0;
   EncPlan enc;  // plan of the largest chunk (sizes the workspace)
 };
 
@@ -630,6 +644,7 @@ mt_status plan_stream(const mt_encoder* enc, int64_t n_samples, int32_t window, 
   mt_status st = plan_encode(enc, &b, window, sp.enc);
   if (st != MT_OK) return st;
   Carver k;
+  sp.off_sat = k.take(4);  // the fp16 saturation mask of the whole stream
   sp.off_tab = k.take(64);
   sp.off_gmax = k.take(4);
   sp.off_mel = k.take((size_t)sp.Tc * 128 * 4);
@@ -1365,7 +1380,7 @@ mt_status mt_encode(const mt_encoder* enc, const float* mel, const mt_batch* mel
   if (ws_bytes < p.bytes)
     return fail(MT_ERR_WORKSPACE, "mt_encode: workspace %zu bytes < required %zu", ws_bytes, p.bytes);
 
-  return run_encode(enc, p, mel, window, out, (char*)ws, (hipStream_t)stream, nullptr);
+  return run_encode(enc, p, mel, window, out, (char*)ws, (hipStream_t)stream, nullptr, nullptr);
 }
 
 
@@ -1401,6 +1416,7 @@ mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_sa
   memcpy(&key, &ninf, 4);
   key = key >= 0 ? key : key ^ 0x7fffffff;
   HIP_TRY(launch_fill_i32((int*)(w + sp.off_gmax), key, 1, s), "fill");
+  HIP_TRY(launch_fill_i32((int*)(w + sp.off_sat), 0, 1, s), "fill");
   for (int64_t m0 = 0; m0 < sp.T; m0 += sp.Tc) {
     st = stream_mel(wav, sp.n, m0, std::min(sp.Tc, sp.T - m0), mel, w, sp, false, s);
     if (st != MT_OK) return st;
@@ -1427,7 +1443,7 @@ mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_sa
     ch.pos = (int)(e0 - drop);
     ch.drop = drop;
     ch.keep = (int)(e1 - e0);
-    st = run_encode(enc, ep, mel, window, out + e0 * d_out, w + sp.off_enc, s, &ch);
+    st = run_encode(enc, ep, mel, window, out + e0 * d_out, w + sp.off_enc, s, &ch, (int*)(w + sp.off_sat));
     if (st != MT_OK) return st;
   }
   return MT_OK;

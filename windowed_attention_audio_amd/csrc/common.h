@@ -94,6 +94,21 @@ __device__ __forceinline__ float wave_reduce64(float v) {
 __device__ __forceinline__ float wave_sum64(float v) { return wave_reduce64<false>(v); }
 __device__ __forceinline__ float wave_max64(float v) { return wave_reduce64<true>(v); }
 
+// fp16 saturation report.  fp16 conversions clamp at +-65504; a kernel that
+// converts to fp16 tracks, per lane, the largest |value| it converted and
+// then calls this once with every lane of the wavefront that is still
+// running: if any of them exceeded 65504, the first such lane sets `bit` in
+// *sat (a stage mask the host reads back), so a clamp is reported instead of
+// passing silently.  sat == nullptr (other operand types): nothing.
+__device__ __forceinline__ void report_saturation(int* sat, int bit, float amax) {
+  if (!sat) return;
+  const uint64_t over = __ballot(amax > 65504.0f);
+  if (over && (int)(threadIdx.x & 63) == __ffsll((unsigned long long)over) - 1) atomicOr(sat, bit);
+}
+__device__ __forceinline__ float absmax4(float m, float a, float b, float c, float d) {
+  return fmaxf(fmaxf(m, fmaxf(fabsf(a), fabsf(b))), fmaxf(fabsf(c), fabsf(d)));
+}
+
 // Order-preserving map float -> int for atomicMax on floats of any sign.
 __device__ __forceinline__ int float_key(float f) {
   int i = __float_as_int(f);

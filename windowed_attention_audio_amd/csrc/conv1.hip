@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
     for (int k = 0; k < 9; ++k) w[c][k] = a.w[(cg * 8 + c) * 9 + k];
   }
   T* out = (T*)a.out + (int64_t)r * 64 * a.C + cg * 8;
+  [[maybe_unused]] float amax = 0.f;
   for (int f1 = lane_pos; f1 < 64; f1 += pl) {
     float p[9];
 #pragma unroll
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
       for (int k = 0; k < 9; ++k) s += w[c][k] * p[k];
       y[c] = gelu_f(s);
     }
+    if constexpr (__is_same(T, f16_t))
+      amax = fmaxf(absmax4(amax, y[0], y[1], y[2], y[3]), absmax4(0.f, y[4], y[5], y[6], y[7]));
     if constexpr (sizeof(T) == 2) {
       uint4 v;
       v.x = pack2f<T>(y[0], y[1]);
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
       o[1] = make_float4(y[4], y[5], y[6], y[7]);
     }
   }
+  if constexpr (__is_same(T, f16_t)) report_saturation(a.sat, SAT_FRONTEND, amax);
 }
 
 }  // namespace

@@ -149,6 +149,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
   // (rows rbase + 16 i increase; a search per row waited on its chain of
   // dependent loads for every row).  Same result as find_seq for each row.
   [[maybe_unused]] int sq_c = 0, sq_lo = 0, sq_hi = 0;
+  [[maybe_unused]] float amax = 0.f;  // fp16: largest |value| converted (saturation report)
   constexpr bool SEQ = PE || EPI == EPI_OUT;
   if constexpr (SEQ) {
     if (PE || a.out_seq_stride > 0) {
@@ -184,6 +185,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = silu_f(acc[i][j][e]) * acc[i][j + 1][e];
+        if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, o[0], o[1], o[2], o[3]);
         store4((T*)a.C + (int64_t)row * a.ldc + feat, o[0], o[1], o[2], o[3]);
         continue;
       } else {
@@ -192,11 +194,15 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
         if constexpr (EPI == EPI_F32) {
           store4((float*)a.C + (int64_t)row * a.ldc + col, v0, v1, v2, v3);
         } else if constexpr (EPI == EPI_ACT) {
+          if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, v0, v1, v2, v3);
           store4((T*)a.C + (int64_t)row * a.ldc + col, v0, v1, v2, v3);
         } else if constexpr (EPI == EPI_GELU) {
-          store4((T*)a.C + (int64_t)row * a.ldc + col, gelu_f(v0), gelu_f(v1), gelu_f(v2), gelu_f(v3));
+          const float g0 = gelu_f(v0), g1 = gelu_f(v1), g2 = gelu_f(v2), g3 = gelu_f(v3);
+          if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, g0, g1, g2, g3);
+          store4((T*)a.C + (int64_t)row * a.ldc + col, g0, g1, g2, g3);
         } else if constexpr (EPI == EPI_GELU_SPLIT) {
           const float g4[4] = {gelu_f(v0), gelu_f(v1), gelu_f(v2), gelu_f(v3)};
+          if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, g4[0], g4[1], g4[2], g4[3]);
           float lo[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) lo[e] = g4[e] - Elem<T>::to_f(Elem<T>::from_f(g4[e]));
@@ -235,6 +241,9 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
       }
     }
   }
+  if constexpr (__is_same(T, f16_t) &&
+                (EPI == EPI_ACT || EPI == EPI_GELU || EPI == EPI_GELU_SPLIT || EPI == EPI_SWIGLU))
+    report_saturation(a.sat, a.sat_bit, amax);
 }
 
 // EPI_RESID with the residual tile already in registers (R[i][j] = C at the
@@ -665,6 +674,7 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
   const int g = lane >> 4, l16 = lane & 15;
   float4 bias[NI];
   load_bias<NI>(a, n0 + wn * WTN + 4 * g, bias);
+  [[maybe_unused]] float amax = 0.f;  // fp16: largest |value| converted (saturation report)
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -683,10 +693,12 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
         v2 = gelu_f(v2);
         v3 = gelu_f(v3);
       }
+      if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, v0, v1, v2, v3);
       const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
       *(uint2*)(qb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }
   }
+  if constexpr (__is_same(T, f16_t)) report_saturation(a.sat, a.sat_bit, amax);
   __syncthreads();
   // 64 rows x CPR chunks per stage, 512 threads
 #pragma unroll
@@ -731,6 +743,7 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
   const int rw = (wm % WPS) * WTM;  // first row of this wavefront inside its stage
   float4 bias[NI];
   load_bias<NI>(a, n0 + wn * WTN + 4 * g, bias);
+  [[maybe_unused]] float amax = 0.f;  // fp16: largest |value| converted (saturation report)
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -747,10 +760,12 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
         v2 = gelu_f(v2);
         v3 = gelu_f(v3);
       }
+      if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, v0, v1, v2, v3);
       const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
       *(uint2*)(hb + r * (BN * 2) + ((q ^ (r & SWM)) << 4) + ((g & 1) << 3)) = w;
     }
   }
+  if constexpr (__is_same(T, f16_t)) report_saturation(a.sat, a.sat_bit, amax);
   __syncthreads();
   // 128 rows x CPR chunks per stage, 512 threads
 #pragma unroll

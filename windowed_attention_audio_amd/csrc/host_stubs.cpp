@@ -98,6 +98,7 @@ hipError_t launch_conv1(const Conv1Args& a, hipStream_t) {
     rd(a.mel + a.mel_row_off[i] * 128, 4 * 128 * (size_t)(a.cu_T[i + 1] - a.cu_T[i]));
   if (a.cu_T1[a.nseq] != a.total_T1) return hipErrorInvalidValue;
   wr(a.out, (size_t)a.total_T1 * 64 * a.C * esize(a.dtype));
+  if (a.sat) wr(a.sat, 4);
   rd(a.w, 4 * 9 * (size_t)a.C);
   rd(a.b, 4 * (size_t)a.C);
   return hipSuccess;
@@ -117,6 +118,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStre
   rd(a.B, ((size_t)(a.N - 1) * a.ldb + a.K) * es);
   if (a.bias) rd(a.bias, 4 * (size_t)a.N);
   if (a.zeros) rd(a.zeros, 16);
+  if (a.sat) wr(a.sat, 4);
   size_t cols = a.N, ces = 4;
   int64_t rows = a.M;
   switch (epi) {
@@ -138,7 +140,8 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStre
 }
 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D, float,
-                            int dtype, bool split, hipStream_t) {
+                            int dtype, bool split, hipStream_t, int* sat, int) {
+  if (sat) wr(sat, 4);
   rd(x, 4 * (size_t)M * D);
   rd(g, 4 * (size_t)D);
   rd(b, 4 * (size_t)D);

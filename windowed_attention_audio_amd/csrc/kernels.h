@@ -15,6 +15,10 @@ enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // arguments (graph-capturable, no host buffer needs to outlive the call).
 hipError_t upload_words(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s);
 
+// Stages whose fp16 conversions clamped a value at +-65504 (the encode
+// workspace's saturation mask; the values are part of the C ABI, mt.h).
+enum : int { SAT_FRONTEND = 1, SAT_LN = 2, SAT_QKV = 4, SAT_FFN = 8, SAT_HEAD = 16, SAT_ADAPTER = 32 };
+
 // ---------------------------------------------------------------- log-mel
 struct MelArgs {
   const float* wav;
@@ -47,6 +51,7 @@ struct Conv1Args {
   void* out;                 // [sum T1][64][C] channels-last, element type dtype
   int C;
   int dtype;
+  int* sat;                  // fp16: saturation mask (SAT_* bits), else nullptr
 };
 hipError_t launch_conv1(const Conv1Args& a, hipStream_t s);
 
@@ -90,6 +95,8 @@ struct GemmArgs {
   int pos_offset;          // EPI_PE: position of a sequence's row 0
   int64_t out_seq_stride;  // EPI_OUT padded: rows per sequence (0 = packed)
   const void* zeros;       // >= 16 bytes of zeros (device), read by out-of-range loads
+  int* sat;                // fp16 16-bit outputs: saturation mask, bit sat_bit (nullptr: off)
+  int sat_bit;
 };
 
 // dtype: DT_F32, DT_BF16 or DT_F16 operands (fp32 accumulation in every
@@ -99,8 +106,10 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int dtype, bool conv, hipStre
 // ---------------------------------------------------------------- LayerNorm
 // out = LN(x) * g + b per row of D fp32 values, written as dtype (DT_*);
 // split: 16-bit hi/lo pair written as [row][2D] (hi | lo).
+// sat / sat_bit: fp16 saturation report (nullptr: off).
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D,
-                            float eps, int dtype, bool split, hipStream_t s);
+                            float eps, int dtype, bool split, hipStream_t s, int* sat = nullptr,
+                            int sat_bit = 0);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

@@ -19,7 +19,8 @@ template <int VEC, typename T, bool SPLIT>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ g,
                                                         const float* __restrict__ b,
-                                                        void* __restrict__ out, int M, float eps) {
+                                                        void* __restrict__ out, int M, float eps,
+                                                        int* sat, int sat_bit) {
   constexpr int D = 256 * VEC;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / D) + eps);
   const float4* g4 = (const float4*)g;
   const float4* b4 = (const float4*)b;
+  [[maybe_unused]] float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < VEC; ++i) {
     const int c4 = lane + 64 * i;
@@ -51,6 +53,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     y.y = (v[i].y - mean) * rstd * gg.y + bb.y;
     y.z = (v[i].z - mean) * rstd * gg.z + bb.z;
     y.w = (v[i].w - mean) * rstd * gg.w + bb.w;
+    if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, y.x, y.y, y.z, y.w);
     if constexpr (sizeof(T) == 4) {
       ((float4*)out)[(int64_t)row * (D / 4) + c4] = y;
     } else {
@@ -70,41 +73,43 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
       }
     }
   }
+  if constexpr (__is_same(T, f16_t)) report_saturation(sat, sat_bit, amax);
 }
 
 template <int VEC, typename T, bool SPLIT>
 hipError_t ln_run(const float* x, const float* g, const float* b, void* out, int M, float eps,
-                  hipStream_t s) {
+                  hipStream_t s, int* sat, int bit) {
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL((layernorm_kernel<VEC, T, SPLIT>), dim3((M + 3) / 4), dim3(256), 0, s, x, g, b,
-                     out, M, eps);
+                     out, M, eps, sat, bit);
   return hipGetLastError();
 }
 
 template <int VEC>
 hipError_t ln_mode(const float* x, const float* g, const float* b, void* out, int M, float eps,
-                   int dtype, bool split, hipStream_t s) {
-  if (dtype == DT_F32) return split ? hipErrorInvalidValue : ln_run<VEC, float, false>(x, g, b, out, M, eps, s);
+                   int dtype, bool split, hipStream_t s, int* sat, int bit) {
+  if (dtype == DT_F32)
+    return split ? hipErrorInvalidValue : ln_run<VEC, float, false>(x, g, b, out, M, eps, s, nullptr, 0);
   if (dtype == DT_BF16)
-    return split ? ln_run<VEC, bf16_t, true>(x, g, b, out, M, eps, s)
-                 : ln_run<VEC, bf16_t, false>(x, g, b, out, M, eps, s);
-  return split ? ln_run<VEC, f16_t, true>(x, g, b, out, M, eps, s)
-               : ln_run<VEC, f16_t, false>(x, g, b, out, M, eps, s);
+    return split ? ln_run<VEC, bf16_t, true>(x, g, b, out, M, eps, s, nullptr, 0)
+                 : ln_run<VEC, bf16_t, false>(x, g, b, out, M, eps, s, nullptr, 0);
+  return split ? ln_run<VEC, f16_t, true>(x, g, b, out, M, eps, s, sat, bit)
+               : ln_run<VEC, f16_t, false>(x, g, b, out, M, eps, s, sat, bit);
 }
 
 }  // namespace
 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* out, int M, int D,
-                            float eps, int dtype, bool split, hipStream_t s) {
+                            float eps, int dtype, bool split, hipStream_t s, int* sat, int sat_bit) {
   switch (D / 256) {
-    case 1: return ln_mode<1>(x, g, b, out, M, eps, dtype, split, s);
-    case 2: return ln_mode<2>(x, g, b, out, M, eps, dtype, split, s);
-    case 3: return ln_mode<3>(x, g, b, out, M, eps, dtype, split, s);
-    case 4: return ln_mode<4>(x, g, b, out, M, eps, dtype, split, s);
-    case 5: return ln_mode<5>(x, g, b, out, M, eps, dtype, split, s);
-    case 6: return ln_mode<6>(x, g, b, out, M, eps, dtype, split, s);
-    case 7: return ln_mode<7>(x, g, b, out, M, eps, dtype, split, s);
-    case 8: return ln_mode<8>(x, g, b, out, M, eps, dtype, split, s);
+    case 1: return ln_mode<1>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 2: return ln_mode<2>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 3: return ln_mode<3>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 4: return ln_mode<4>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 5: return ln_mode<5>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 6: return ln_mode<6>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 7: return ln_mode<7>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
+    case 8: return ln_mode<8>(x, g, b, out, M, eps, dtype, split, s, sat, sat_bit);
     default: return hipErrorInvalidValue;
   }
 }
