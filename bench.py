@@ -34,13 +34,14 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
 # HBM traffic of one fc1 launch, from two rocprofv3 --pmc runs (FETCH_SIZE,
-# then WRITE_SIZE) of `bench.py --steps 2 --warmup 1 --copy-probe`, each
-# scaled by what the same counter read for the probe's 256 MiB device copy
-# (see profiles/fc1_16x30s_traffic.md).  Keyed by a hash of the GEMM kernel
-# sources: after any change to them the figure is stale and reported as null.
+# then WRITE_SIZE) of `bench.py --only headline --steps 1 --warmup 1
+# --copy-probe`, each scaled by what the same counter read for the probe's
+# 256 MiB device copy (profiles/encoder_16x30s_traffic.md).  Keyed by a hash
+# of the GEMM kernel sources: after any change to them the figure is stale and
+# reported as null.
 FC1_TRAFFIC = {
-    "c07c3b247aa9524f": {"fetch_KiB": 70425.1, "write_KiB": 73440,
-                         "fetch_scale": 262144 / 131093.875, "write_scale": 262144 / 262144.0},
+    "f2a39bf112322af1": {"fetch_KiB": 69958.5, "write_KiB": 72480.0,
+                         "fetch_scale": 262144 / 131087.750, "write_scale": 262144 / 262144.0},
 }
 
 
@@ -546,7 +547,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--operands", choices=["f16", "bf16"], default="f16")
-    ap.add_argument("--only", choices=["2x", "decoder", "varlen", "headline"],
+    ap.add_argument("--only", choices=["2x", "decoder", "varlen", "headline", "mel"],
                     help="run only this measurement and print its JSON (for profiling)")
     ap.add_argument("--no-decoder", action="store_true",
                     help="skip the language-model decoder step")
@@ -615,6 +616,28 @@ def main():
     if args.only == "varlen":
         del dev_w
         print(json.dumps(measure_varlen_adapter(W, synth, torch, np, weights)), flush=True)
+        return
+    if args.only == "mel":
+        # the log-mel stage alone: the 16 x 30 s batch, then the 10-minute
+        # stream, `steps` calls each after `warmup` (for counter profiles)
+        del dev_w
+        w3 = synth.make_clips(synth.workload(3))[0]
+        wav3 = torch.from_numpy(w3).cuda()
+        n3 = wav3.numel()
+        mel3 = torch.empty((n3 // 160, 128), dtype=torch.float32, device="cuda")
+        ws3 = torch.empty(W.mt_logmel_workspace_size([n3]), dtype=torch.uint8, device="cuda")
+        res = {}
+        for name, fn, alg in (
+                ("16x30s", lambda: W.mt_logmel(wav, lens, mel=mel, ws=ws_mel, stream=stream),
+                 4 * sum(lens) + 4 * 128 * sum(lens_T)),
+                ("600s_stream", lambda: W.mt_logmel(wav3, [n3], mel=mel3, ws=ws3, stream=stream),
+                 4 * n3 + 4 * 128 * (n3 // 160))):
+            for _ in range(args.warmup):
+                fn()
+            med, _, _ = timed_steps(torch, fn, stream, args.steps)
+            res[name] = {"ms_median": round(med, 4), "algorithmic_bytes": alg,
+                         "GBps": round(alg / (med * 1e-3) / 1e9, 1)}
+        print(json.dumps(res), flush=True)
         return
 
     if args.copy_probe:
