@@ -13,6 +13,9 @@ Modules
   encoder2x  log-mel -> encoder frames of the full-attention variant with a
              2x time-downsampling front-end (page "CrisperWhisper -> ONNX
              (with cross-attentions)": whisper geometries)
+  live     one long stream encoded window by window as its audio arrives
+           (the clip maximum of the log clamp read as a causal running
+           maximum)
   prompt   adapter frames spliced into the prompt's token embeddings
   decoder  the language-model decoder (Qwen3-1.7B geometry) over a KV cache
 
@@ -20,4 +23,4 @@ Every function below is pinned by tests under ``tests/`` that check it against
 closed forms, invariants, brute force, or an independent library routine.
 """
 
-from . import logmel, encoder, encoder2x, prompt, decoder  # noqa: F401
+from . import logmel, encoder, encoder2x, live, prompt, decoder  # noqa: F401
