@@ -186,6 +186,39 @@ def stream_measure(W, enc, synth, torch, np, chunks=(8, 32), reps=4):
                     "workspace_bytes": ws_m.numel() + ws_e.numel() + mel.numel() * 4,
                     "peak_bytes": torch.cuda.max_memory_allocated() - base + dwav.numel() * 4
                     + out.numel() * 4}
+    # live: the stream pushed in 1 s pieces as it "arrives" (each window
+    # encoded once its samples are in), bounded state
+    piece = 16000
+    live_state = W.mt_stream_state_bytes(enc, wl.window, piece)
+    lout = torch.empty((N, enc.d_out), dtype=torch.float32, device="cuda")
+
+    def live():
+        stl = W.LiveStream(enc, wl.window, piece)
+        r = 0
+        for i in range(0, n, piece):
+            m = min(piece, n - i)
+            got = stl.pending_frames(m)
+            stl.push(dwav[i:i + m], out=lout[r:], stream=stream)
+            r += got
+        stl.finish(out=lout[r:], stream=stream)
+        stl.close()
+
+    live()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    live()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lms = e0.elapsed_time(e1)
+    res["live_1s_pushes"] = {"ms": round(lms, 3), "audio_s_per_s": round(n / 16000.0 / (lms * 1e-3), 1),
+                             "host_wall_ms": round(wall * 1e3, 3), "state_bytes": live_state,
+                             "windows": (N + wl.window - 1) // wl.window,
+                             "note": "one window (8.32 s of audio) encoded per call as soon as its samples "
+                                     "are in; running-maximum log clamp"}
     # log-mel alone on the stream (the HBM-bound stage): per call, median of reps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(41)]
     for _ in range(5):

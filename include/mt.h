@@ -266,6 +266,64 @@ mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_sa
                            int32_t window, int32_t chunk_windows, float* out, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Live encoding of one stream whose audio arrives piece by piece (model card
+ * "MOSS-Transcribe-preview-2B-GGUF", Architecture table, rows "Audio" and
+ * "Audio encoder": windowed attention makes each window depend only on its
+ * own audio beyond the convolutions' receptive field).  The pages do not say
+ * how the log clamp's clip maximum is found when the clip is not yet
+ * complete; the reading taken is a causal running maximum: window k (encoder
+ * frames [kW, (k+1)W)) is clamped at the maximum of the unclamped log-mel
+ * over mel frames 0 .. 8 (k+1) W - 1, the frames its receptive field reaches,
+ * minus 8.  Each window is therefore encoded exactly as the whole-clip path
+ * would encode the stream prefix it needs; the result does not depend on how
+ * the audio is split into pushes, the last window sees the maximum of the
+ * whole stream, and once the stream's loudest frame has arrived the windows
+ * equal mt_encode_stream / mt_logmel + mt_encode of the whole stream.
+ *
+ * A window is encoded as soon as its samples are in (samples up to
+ * 1280 (k+1) W + 39, i.e. W * 80 ms plus 2.5 ms of look-ahead); the state keeps
+ * about 1280 W + max_push recent samples, whatever the stream's length (up to
+ * 2^31 - 1 samples).  8x front-end only.
+ *
+ *   mt_stream_state_bytes  device state bytes for this window and the largest
+ *                          push (max_push samples).
+ *   mt_stream_open         starts a stream in `state` (device, caller-owned,
+ *                          256-byte aligned, >= mt_stream_state_bytes; it must
+ *                          stay alive and be used by this stream only until
+ *                          mt_stream_close).  The first 32-bit word of the
+ *                          state holds the fp16 saturation mask (MT_SAT_*) of
+ *                          everything the stream has encoded.
+ *   mt_stream_push         appends n <= max_push samples (device fp32) and
+ *                          encodes every window whose samples are now all in,
+ *                          writing their frames to out (device fp32
+ *                          [out_frames, d], d as for mt_encode) in order;
+ *                          *n_frames (host) = frames written.  The count is
+ *                          known on the host before the work runs:
+ *                          mt_stream_pending_frames(st, n, 0) gives it.
+ *   mt_stream_finish       marks the end of the stream (at least 201 samples in
+ *                          all) and encodes the remaining frames, the last
+ *                          window partial, with the reflection and zero padding
+ *                          of the stream's real end;
+ *                          mt_stream_pending_frames(st, 0, 1) gives the count.
+ *   mt_stream_close        frees the host handle (not the state).
+ * Every call is asynchronous on `stream`; pushes of one stream must be ordered
+ * (one stream).  Errors: MT_ERR_INVALID_ARG (push after finish, n > max_push,
+ * a finish before 201 samples, NULL pointers), MT_ERR_WORKSPACE (state or out
+ * too small), MT_ERR_UNSUPPORTED (the 2x front-end, a stream longer than
+ * 2^31 - 1 samples); nothing runs and the stream is unchanged when a call
+ * fails its checks (after MT_ERR_HIP the stream must be closed). */
+typedef struct mt_stream mt_stream;
+mt_status mt_stream_state_bytes(const mt_encoder* enc, int32_t window, int64_t max_push, size_t* bytes);
+mt_status mt_stream_open(const mt_encoder* enc, int32_t window, int64_t max_push, void* state,
+                         size_t state_bytes, void* stream, mt_stream** out);
+/* Frames that a push of n_more samples (finish = 0) or the finish (finish = 1,
+ * n_more = 0) would write; -1 if that call would be refused. */
+int64_t mt_stream_pending_frames(const mt_stream* st, int64_t n_more, int32_t finish);
+mt_status mt_stream_push(mt_stream* st, const float* samples, int64_t n, float* out, int64_t out_frames,
+                         int64_t* n_frames, void* stream);
+mt_status mt_stream_finish(mt_stream* st, float* out, int64_t out_frames, int64_t* n_frames, void* stream);
+void mt_stream_close(mt_stream* st);
+
 /* Prompt embedding with the audio spliced in (model card "MOSS-Transcribe-
  * preview-2B-GGUF", Architecture table, rows Prompt and Audio injection): row
  * i of the output is the token-embedding row of tokens[i], except that each

@@ -411,6 +411,75 @@ static void check_encode() {
   delete packed;
 }
 
+// ------------------------------------------------------------------ live stream
+static void check_live() {
+  mt_encoder_config c = small_cfg(MT_F16, 0);
+  Weights w(c);
+  Buf* packed = nullptr;
+  mt_encoder* e = create(c, w, packed);
+  const int W = 5;                 // 6400 samples per window
+  const int64_t max_push = 20000;  // several windows per push, and buffer compaction
+  size_t sb = 0;
+  EXPECT(mt_stream_state_bytes(e, W, max_push, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_state_bytes(nullptr, W, max_push, &sb), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_state_bytes(e, 0, max_push, &sb), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_state_bytes(e, W, 0, &sb), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_state_bytes(e, W, (int64_t)INT32_MAX + 1, &sb), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_state_bytes(e, W, max_push, &sb), MT_OK);
+  Buf state(sb);
+  mt_stream* st = nullptr;
+  EXPECT(mt_stream_open(e, W, max_push, state.p, sb, nullptr, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_open(e, W, max_push, nullptr, sb, nullptr, &st), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_open(e, W, max_push, (char*)state.p + 16, sb - 16, nullptr, &st), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_open(e, W, max_push, state.p, sb - 1, nullptr, &st), MT_ERR_WORKSPACE);
+  EXPECT(mt_stream_open(e, W, max_push, state.p, sb, nullptr, &st), MT_OK);
+  const int d = c.d_out;
+  Buf chunk(4 * max_push);
+  int64_t total = 0, frames = 0, got = 0;
+  // pushes of many sizes: single samples, exactly a window, the largest push
+  const int64_t sizes[] = {1, 39, 6400, 0, 20000, 3, 12345, 20000, 20000, 777, 6401, 19999, 20000};
+  for (int64_t n : sizes) {
+    const int64_t want = mt_stream_pending_frames(st, n, 0);
+    EXPECT_TRUE(want >= 0 && want % W == 0);
+    Buf out(4 * (size_t)d * (size_t)(want > 0 ? want : 1));
+    if (want > 0)
+      EXPECT(mt_stream_push(st, chunk.f(), n, out.f(), want - 1, &got, nullptr), MT_ERR_WORKSPACE);
+    EXPECT(mt_stream_push(st, chunk.f(), n, out.f(), want, &got, nullptr), MT_OK);
+    EXPECT_TRUE(got == want);
+    total += n;
+    frames += got;
+  }
+  EXPECT(mt_stream_push(st, chunk.f(), max_push + 1, nullptr, 0, &got, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_push(st, nullptr, 5, nullptr, 0, &got, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_push(st, chunk.f(), 5, nullptr, 0, nullptr, nullptr), MT_ERR_INVALID_ARG);
+  const int64_t rest = mt_stream_pending_frames(st, 0, 1);
+  const int64_t N = mt_encoder_frames(mt_mel_frames(total));
+  EXPECT_TRUE(rest == N - frames && rest > 0);
+  {
+    Buf out(4 * (size_t)d * (size_t)rest);
+    EXPECT(mt_stream_finish(st, out.f(), rest - 1, &got, nullptr), MT_ERR_WORKSPACE);
+    EXPECT(mt_stream_finish(st, out.f(), rest, &got, nullptr), MT_OK);
+    EXPECT_TRUE(got == rest);
+  }
+  EXPECT(mt_stream_push(st, chunk.f(), 5, nullptr, 0, &got, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_finish(st, nullptr, 0, &got, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT_TRUE(mt_stream_pending_frames(st, 0, 1) == -1);
+  mt_stream_close(st);
+  // a stream that ends before its first window, and one too short to frame
+  EXPECT(mt_stream_open(e, W, max_push, state.p, sb, nullptr, &st), MT_OK);
+  EXPECT(mt_stream_push(st, chunk.f(), 150, nullptr, 0, &got, nullptr), MT_OK);
+  EXPECT(mt_stream_finish(st, nullptr, 0, &got, nullptr), MT_ERR_INVALID_ARG);
+  EXPECT(mt_stream_push(st, chunk.f(), 51, nullptr, 0, &got, nullptr), MT_OK);
+  {
+    Buf out(4 * (size_t)d);
+    EXPECT(mt_stream_finish(st, out.f(), 1, &got, nullptr), MT_OK);
+    EXPECT_TRUE(got == 1);
+  }
+  mt_stream_close(st);
+  mt_encoder_destroy(e);
+  delete packed;
+}
+
 // ------------------------------------------------------------------ prompt splice
 static void check_prompt() {
   const int64_t vocab = 100;
@@ -589,6 +658,7 @@ int main() {
   check_config_rejections();
   check_create_rejections();
   check_encode();
+  check_live();
   check_prompt();
   check_decoder();
   check_misc();

@@ -35,6 +35,8 @@ EXPORTS = (
     "mt_encoder_n_weights", "mt_encoder_packed_bytes", "mt_encoder_create",
     "mt_encoder_destroy", "mt_max_window", "mt_encode_workspace_size", "mt_encode",
     "mt_encode_stream_workspace_size", "mt_encode_stream",
+    "mt_stream_state_bytes", "mt_stream_open", "mt_stream_pending_frames", "mt_stream_push",
+    "mt_stream_finish", "mt_stream_close",
     "mt_prompt_embed_workspace_size", "mt_prompt_embed",
     "mt_decoder_n_weights", "mt_decoder_packed_bytes", "mt_decoder_create", "mt_decoder_destroy",
     "mt_decoder_embedding", "mt_decoder_cache_bytes", "mt_decode_workspace_size", "mt_decode",
@@ -106,6 +108,15 @@ def lib():
                                                       ctypes.c_int32, ctypes.POINTER(c_sz)]
         L.mt_encode_stream.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp,
                                        vp, c_sz, vp]
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.mt_stream_state_bytes.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(c_sz)]
+        L.mt_stream_open.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, vp, c_sz, vp, ctypes.POINTER(vp)]
+        L.mt_stream_pending_frames.argtypes = [vp, ctypes.c_int64, ctypes.c_int32]
+        L.mt_stream_pending_frames.restype = ctypes.c_int64
+        L.mt_stream_push.argtypes = [vp, vp, ctypes.c_int64, vp, ctypes.c_int64, i64p, vp]
+        L.mt_stream_finish.argtypes = [vp, vp, ctypes.c_int64, i64p, vp]
+        L.mt_stream_close.argtypes = [vp]
+        L.mt_stream_close.restype = None
         L.mt_prompt_embed_workspace_size.argtypes = [ctypes.c_int64, ctypes.POINTER(c_sz)]
         L.mt_prompt_embed.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, ctypes.c_int32,
                                       vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp,
@@ -137,6 +148,7 @@ def lib():
                      "mt_encoder_packed_bytes",
                      "mt_encoder_create", "mt_encode_workspace_size", "mt_encode",
                      "mt_encode_stream_workspace_size", "mt_encode_stream",
+                     "mt_stream_state_bytes", "mt_stream_open", "mt_stream_push", "mt_stream_finish",
                      "mt_prompt_embed_workspace_size", "mt_prompt_embed",
                      "mt_decoder_packed_bytes", "mt_decoder_create", "mt_decoder_cache_bytes",
                      "mt_decode_workspace_size", "mt_decode"):
@@ -358,6 +370,72 @@ def mt_encode_stream(enc: Encoder, wav, window, chunk_windows, out=None, ws=None
                                   int(chunk_windows), ctypes.c_void_p(out.data_ptr()),
                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
     return out
+
+
+def mt_stream_state_bytes(enc: Encoder, window, max_push) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mt_stream_state_bytes(enc.handle if enc is not None else None, int(window), int(max_push),
+                                       ctypes.byref(n)))
+    return n.value
+
+
+class LiveStream:
+    """One live stream (mt_stream_open): push() appends audio and returns the
+    frames of the windows it completed, finish() the rest.  The device state
+    is a torch tensor owned by this object."""
+
+    def __init__(self, enc: Encoder, window, max_push, stream=None):
+        import torch
+        self.enc = enc
+        self.window = int(window)
+        self.max_push = int(max_push)
+        nbytes = mt_stream_state_bytes(enc, window, max_push)
+        self.state = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        h = ctypes.c_void_p()
+        _check(lib().mt_stream_open(enc.handle, self.window, self.max_push, ctypes.c_void_p(self.state.data_ptr()),
+                                    nbytes, _stream_ptr(stream), ctypes.byref(h)))
+        self.handle = h
+
+    def pending_frames(self, n_more=0, finish=False) -> int:
+        return lib().mt_stream_pending_frames(self.handle, int(n_more), 1 if finish else 0)
+
+    def _out(self, n):
+        import torch
+        return torch.empty((max(n, 1), self.enc.d_out), dtype=torch.float32, device="cuda")
+
+    def push(self, samples, out=None, stream=None):
+        """samples: fp32 CUDA tensor [n]; returns fp32 [frames, d]."""
+        import torch
+        assert samples.is_cuda and samples.dtype == torch.float32 and samples.is_contiguous()
+        n = samples.numel()
+        want = self.pending_frames(n)
+        if out is None:
+            out = self._out(want)
+        got = ctypes.c_int64()
+        _check(lib().mt_stream_push(self.handle, ctypes.c_void_p(samples.data_ptr()), int(n),
+                                    ctypes.c_void_p(out.data_ptr()), out.shape[0], ctypes.byref(got),
+                                    _stream_ptr(stream)))
+        return out[:got.value]
+
+    def finish(self, out=None, stream=None):
+        want = self.pending_frames(0, finish=True)
+        if out is None:
+            out = self._out(want)
+        got = ctypes.c_int64()
+        _check(lib().mt_stream_finish(self.handle, ctypes.c_void_p(out.data_ptr()), out.shape[0],
+                                      ctypes.byref(got), _stream_ptr(stream)))
+        return out[:got.value]
+
+    def close(self):
+        if self.handle:
+            lib().mt_stream_close(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def mt_prompt_embed_workspace_size(n_tokens) -> int:

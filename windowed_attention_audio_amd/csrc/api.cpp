@@ -311,6 +311,18 @@ struct mt_encoder {
   const void* zeros;
 };
 
+struct mt_stream {
+  const mt_encoder* enc = nullptr;
+  int window = 0;
+  int64_t max_push = 0;
+  char* state = nullptr;
+  int cur = 0;          // buffer holding the recent samples
+  int64_t base = 0;     // stream index of that buffer's first sample
+  int64_t have = 0;     // samples pushed so far
+  int64_t next = 0;     // next window to encode
+  bool finished = false;
+};
+
 namespace {
 
 mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window, EncPlan& p) {
@@ -653,21 +665,24 @@ mt_status plan_stream(const mt_encoder* enc, int64_t n_samples, int32_t window, 
   return MT_OK;
 }
 
-// Mel frames [m0, m0 + nf) of the stream into mel (rows 0 .. nf - 1): tables
-// for one sequence of the stream's full length, frame offset m0.
-mt_status stream_mel(const float* wav, int64_t n, int64_t m0, int64_t nf, float* mel, char* w,
-                     const StreamPlan& sp, bool normalise, hipStream_t s) {
+// Mel frames [m0, m0 + nf) of one stream of n samples into mel (rows 0 ..
+// nf - 1): sample q of the stream is wav[q + sample_off] (a live stream keeps
+// only its recent samples), the reflection at the stream's ends uses n, the
+// frames' maximum goes into *gmax; tables in `tab` (32 bytes).
+mt_status stream_mel_at(const float* wav, int64_t sample_off, int64_t n, int64_t m0, int64_t nf, float* mel,
+                        char* tab, int* gmax, bool normalise, hipStream_t s) {
   // sample_off (8) | row_off (8) | seq_len (4) | cu_frames (8)
-  uint32_t words[7] = {0, 0, 0, 0, (uint32_t)n, 0, (uint32_t)nf};
-  HIP_TRY(upload_words((uint32_t*)(w + sp.off_tab), words, 7, s), "upload tables");
+  uint32_t words[7] = {(uint32_t)(uint64_t)sample_off, (uint32_t)((uint64_t)sample_off >> 32), 0, 0,
+                       (uint32_t)n, 0, (uint32_t)nf};
+  HIP_TRY(upload_words((uint32_t*)tab, words, 7, s), "upload tables");
   MelArgs a;
   a.wav = wav;
   a.mel = mel;
-  a.seq_sample_off = (const int64_t*)(w + sp.off_tab);
-  a.seq_row_off = (const int64_t*)(w + sp.off_tab + 8);
-  a.seq_len = (const int32_t*)(w + sp.off_tab + 16);
-  a.cu_frames = (const int32_t*)(w + sp.off_tab + 20);
-  a.gmax = (int*)(w + sp.off_gmax);
+  a.seq_sample_off = (const int64_t*)tab;
+  a.seq_row_off = (const int64_t*)(tab + 8);
+  a.seq_len = (const int32_t*)(tab + 16);
+  a.cu_frames = (const int32_t*)(tab + 20);
+  a.gmax = gmax;
   a.nseq = 1;
   a.total_frames = nf;
   a.out_rows = nf;
@@ -676,6 +691,113 @@ mt_status stream_mel(const float* wav, int64_t n, int64_t m0, int64_t nf, float*
   STAGE(launch_mel(a, s), "mel");
   if (normalise) STAGE(launch_mel_norm(a, nf, s), "mel_norm");
   return MT_OK;
+}
+
+mt_status stream_mel(const float* wav, int64_t n, int64_t m0, int64_t nf, float* mel, char* w,
+                     const StreamPlan& sp, bool normalise, hipStream_t s) {
+  return stream_mel_at(wav, 0, n, m0, nf, mel, w + sp.off_tab, (int*)(w + sp.off_gmax), normalise, s);
+}
+
+// ------------------------------------------------------------- live stream
+// Windows are encoded as their audio arrives.  Window k (encoder frames
+// [kW, (k+1)W)) needs mel frames up to 8 (k+1) W - 1, i.e. samples up to
+// 1280 (k+1) W + 39: once those are in, it is encoded from mel frames
+// [max(0, 8 kW - 8), 8 (k+1) W) with the log clamp at the running maximum
+// over every mel frame computed so far (frames [0, 8 (k+1) W)), the same
+// chunk arithmetic as mt_encode_stream.  At the end of the stream the rest
+// (with the reflection and zero padding of the stream's real end) follows.
+// The state keeps the recent samples in two buffers used in turn: before an
+// append that would overflow, the samples the next window still needs move to
+// the other buffer.
+struct LivePlan {
+  int64_t cap = 0;  // samples per buffer
+  int64_t Tc = 0;   // mel frames of a window's chunk
+  size_t off_sat = 0, off_gmax = 0, off_tab = 0, off_buf[2] = {0, 0}, off_mel = 0, off_enc = 0, bytes = 0;
+  EncPlan enc;      // plan of a full window's chunk (sizes the workspace)
+};
+
+constexpr int64_t LIVE_MAX_SAMPLES = INT32_MAX;  // sample indices of a stream fit 32 bits
+
+mt_status plan_live(const mt_encoder* enc, int32_t window, int64_t max_push, LivePlan& lp) {
+  if (!enc) return fail(MT_ERR_INVALID_ARG, "encoder is NULL");
+  if (enc->cfg.frontend != MT_FRONTEND_CONV2D_8X)
+    return fail(MT_ERR_UNSUPPORTED, "live streams: only the 8x (Conv2D) front-end streams");
+  if (window < 1) return fail(MT_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+  if (max_push < 1 || max_push > LIVE_MAX_SAMPLES)
+    return fail(MT_ERR_INVALID_ARG, "max_push %lld out of range [1, %lld]", (long long)max_push,
+                (long long)LIVE_MAX_SAMPLES);
+  lp.Tc = 8 * (int64_t)window + 8;
+  lp.cap = 1280 * (int64_t)window + 1680 + max_push;
+  if (lp.cap > LIVE_MAX_SAMPLES)
+    return fail(MT_ERR_UNSUPPORTED, "live streams: window %d with pushes of %lld samples is too large", window,
+                (long long)max_push);
+  int64_t lens[1] = {lp.Tc};
+  mt_batch b;
+  b.layout = MT_PACKED;
+  b.n_seqs = 1;
+  b.len = lens;
+  b.max_len = 0;
+  mt_status st = plan_encode(enc, &b, window, lp.enc);
+  if (st != MT_OK) return st;
+  Carver k;
+  lp.off_sat = k.take(4);  // the fp16 saturation mask of the whole stream
+  lp.off_gmax = k.take(4);
+  lp.off_tab = k.take(32);
+  lp.off_buf[0] = k.take((size_t)lp.cap * 4);
+  lp.off_buf[1] = k.take((size_t)lp.cap * 4);
+  lp.off_mel = k.take((size_t)lp.Tc * 128 * 4);
+  lp.off_enc = k.take(lp.enc.bytes);
+  lp.bytes = k.off;
+  return MT_OK;
+}
+
+// Windows whose samples are all in once `have` samples have arrived (before
+// the end of the stream is known): k + 1 <= (have - 40) / (1280 W).
+int64_t live_complete(int window, int64_t have) {
+  return have >= 40 ? (have - 40) / (1280 * (int64_t)window) : 0;
+}
+
+// First stream sample that window k (or a later one) can still read.
+int64_t live_keep_from(int window, int64_t k) {
+  return std::max<int64_t>(0, 160 * std::max<int64_t>(0, 8 * k * window - 8) - 200);
+}
+
+// Encodes window k of a live stream into out (its rows only).  final: the
+// stream has ended at st->have samples (its real end: reflection, zero
+// padding, a last partial window).
+mt_status live_encode_window(mt_stream* st, const LivePlan& lp, int64_t k, bool final, float* out, hipStream_t s) {
+  const int W = st->window;
+  char* w = st->state;
+  int64_t e1 = (k + 1) * W, m1 = 8 * e1, n_len = LIVE_MAX_SAMPLES;
+  if (final) {
+    const int64_t T = st->have / HOP, N = half_up(half_up(half_up(T)));
+    e1 = std::min(e1, N);
+    m1 = std::min(m1, T);
+    n_len = st->have;
+  }
+  const int64_t e0 = k * W, drop = e0 > 0 ? 1 : 0;
+  const int64_t m0 = std::max<int64_t>(0, 8 * e0 - 8);
+  if (half_up(half_up(half_up(m1 - m0))) != e1 - e0 + drop || m1 - m0 > lp.Tc)
+    return fail(MT_ERR_INVALID_ARG, "live stream: internal window geometry error");
+  float* mel = (float*)(w + lp.off_mel);
+  // the buffer holds stream samples [base, base + cap): sample q at q - base
+  mt_status st_ = stream_mel_at((const float*)(w + lp.off_buf[st->cur]), -st->base, n_len, m0, m1 - m0, mel,
+                                w + lp.off_tab, (int*)(w + lp.off_gmax), true, s);
+  if (st_ != MT_OK) return st_;
+  int64_t lens[1] = {m1 - m0};
+  mt_batch b;
+  b.layout = MT_PACKED;
+  b.n_seqs = 1;
+  b.len = lens;
+  b.max_len = 0;
+  EncPlan ep;
+  st_ = plan_encode(st->enc, &b, W, ep);
+  if (st_ != MT_OK) return st_;
+  StreamChunk ch;
+  ch.pos = (int)(e0 - drop);
+  ch.drop = (int)drop;
+  ch.keep = (int)(e1 - e0);
+  return run_encode(st->enc, ep, mel, W, out, w + lp.off_enc, s, &ch, (int*)(w + lp.off_sat));
 }
 
 // ------------------------------------------------------------- log-mel launch
@@ -1449,6 +1571,136 @@ mt_status mt_encode_stream(const mt_encoder* enc, const float* wav, int64_t n_sa
   return MT_OK;
 }
 
+
+mt_status mt_stream_state_bytes(const mt_encoder* enc, int32_t window, int64_t max_push, size_t* bytes) {
+  if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");
+  LivePlan lp;
+  mt_status st = plan_live(enc, window, max_push, lp);
+  if (st != MT_OK) return st;
+  *bytes = lp.bytes;
+  return MT_OK;
+}
+
+mt_status mt_stream_open(const mt_encoder* enc, int32_t window, int64_t max_push, void* state, size_t state_bytes,
+                         void* stream, mt_stream** out) {
+  if (!out) return fail(MT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  LivePlan lp;
+  mt_status st = plan_live(enc, window, max_push, lp);
+  if (st != MT_OK) return st;
+  if (!state) return fail(MT_ERR_INVALID_ARG, "mt_stream_open: state is NULL");
+  if ((uintptr_t)state % ALIGN) return fail(MT_ERR_INVALID_ARG, "mt_stream_open: state must be 256-byte aligned");
+  if (state_bytes < lp.bytes)
+    return fail(MT_ERR_WORKSPACE, "mt_stream_open: state %zu bytes < required %zu", state_bytes, lp.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)state;
+  const float ninf = -INFINITY;
+  int key;
+  memcpy(&key, &ninf, 4);
+  key = key >= 0 ? key : key ^ 0x7fffffff;
+  HIP_TRY(launch_fill_i32((int*)(w + lp.off_gmax), key, 1, s), "fill");
+  HIP_TRY(launch_fill_i32((int*)(w + lp.off_sat), 0, 1, s), "fill");
+  mt_stream* h = new mt_stream();
+  h->enc = enc;
+  h->window = window;
+  h->max_push = max_push;
+  h->state = w;
+  *out = h;
+  return MT_OK;
+}
+
+int64_t mt_stream_pending_frames(const mt_stream* st, int64_t n_more, int32_t finish) {
+  if (!st || st->finished || n_more < 0 || (finish != 0 && finish != 1)) return -1;
+  const int64_t have = st->have + n_more;
+  if (!finish) return (live_complete(st->window, have) - st->next) * st->window;
+  if (have < 201) return -1;
+  return half_up(half_up(half_up(have / HOP))) - st->next * st->window;
+}
+
+mt_status mt_stream_push(mt_stream* st, const float* samples, int64_t n, float* out, int64_t out_frames,
+                         int64_t* n_frames, void* stream) {
+  if (!st) return fail(MT_ERR_INVALID_ARG, "stream is NULL");
+  if (!n_frames) return fail(MT_ERR_INVALID_ARG, "n_frames is NULL");
+  *n_frames = 0;
+  if (st->finished) return fail(MT_ERR_INVALID_ARG, "mt_stream_push: the stream has finished");
+  if (n < 0 || n > st->max_push)
+    return fail(MT_ERR_INVALID_ARG, "mt_stream_push: %lld samples outside [0, max_push = %lld]", (long long)n,
+                (long long)st->max_push);
+  if (n > 0 && !samples) return fail(MT_ERR_INVALID_ARG, "mt_stream_push: samples is NULL");
+  if (st->have + n > LIVE_MAX_SAMPLES)
+    return fail(MT_ERR_UNSUPPORTED, "mt_stream_push: a stream of more than %lld samples", (long long)LIVE_MAX_SAMPLES);
+  LivePlan lp;
+  mt_status r = plan_live(st->enc, st->window, st->max_push, lp);
+  if (r != MT_OK) return r;
+  const int W = st->window;
+  const int d = st->enc->cfg.with_head ? st->enc->cfg.d_out : st->enc->cfg.d_model;
+  const int64_t k_end = live_complete(W, st->have + n);
+  const int64_t frames = (k_end - st->next) * W;
+  if (frames > 0 && (!out || (uintptr_t)out % 16))
+    return fail(MT_ERR_INVALID_ARG, "mt_stream_push: out is NULL or not 16-byte aligned");
+  if (frames > out_frames)
+    return fail(MT_ERR_WORKSPACE, "mt_stream_push: %lld frames complete, out holds %lld", (long long)frames,
+                (long long)out_frames);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = st->state;
+  if (n > 0) {
+    if (st->have + n - st->base > lp.cap) {
+      // keep what the next window can still read, in the other buffer
+      const int64_t q0 = live_keep_from(W, st->next);
+      if (q0 < st->base || st->have - q0 + n > lp.cap)
+        return fail(MT_ERR_INVALID_ARG, "mt_stream_push: internal buffer plan error");
+      if (st->have > q0)
+        HIP_TRY(launch_copy_f32((const float*)(w + lp.off_buf[st->cur]) + (q0 - st->base),
+                                (float*)(w + lp.off_buf[st->cur ^ 1]), st->have - q0, s), "keep samples");
+      st->cur ^= 1;
+      st->base = q0;
+    }
+    HIP_TRY(launch_copy_f32(samples, (float*)(w + lp.off_buf[st->cur]) + (st->have - st->base), n, s),
+            "append samples");
+    st->have += n;
+  }
+  for (int64_t k = st->next; k < k_end; ++k) {
+    r = live_encode_window(st, lp, k, false, out + (k - st->next) * W * (int64_t)d, s);
+    if (r != MT_OK) return r;
+  }
+  st->next = k_end;
+  *n_frames = frames;
+  return MT_OK;
+}
+
+mt_status mt_stream_finish(mt_stream* st, float* out, int64_t out_frames, int64_t* n_frames, void* stream) {
+  if (!st) return fail(MT_ERR_INVALID_ARG, "stream is NULL");
+  if (!n_frames) return fail(MT_ERR_INVALID_ARG, "n_frames is NULL");
+  *n_frames = 0;
+  if (st->finished) return fail(MT_ERR_INVALID_ARG, "mt_stream_finish: the stream has finished");
+  if (st->have < 201)
+    return fail(MT_ERR_INVALID_ARG, "mt_stream_finish: %lld samples; reflection padding by 200 needs more than 200",
+                (long long)st->have);
+  LivePlan lp;
+  mt_status r = plan_live(st->enc, st->window, st->max_push, lp);
+  if (r != MT_OK) return r;
+  const int W = st->window;
+  const int d = st->enc->cfg.with_head ? st->enc->cfg.d_out : st->enc->cfg.d_model;
+  const int64_t N = half_up(half_up(half_up(st->have / HOP)));
+  const int64_t n_win = (N + W - 1) / W;
+  const int64_t frames = N - st->next * W;
+  if (frames > 0 && (!out || (uintptr_t)out % 16))
+    return fail(MT_ERR_INVALID_ARG, "mt_stream_finish: out is NULL or not 16-byte aligned");
+  if (frames > out_frames)
+    return fail(MT_ERR_WORKSPACE, "mt_stream_finish: %lld frames remain, out holds %lld", (long long)frames,
+                (long long)out_frames);
+  hipStream_t s = (hipStream_t)stream;
+  for (int64_t k = st->next; k < n_win; ++k) {
+    r = live_encode_window(st, lp, k, true, out + (k - st->next) * W * (int64_t)d, s);
+    if (r != MT_OK) return r;
+  }
+  st->next = n_win;
+  st->finished = true;
+  *n_frames = frames;
+  return MT_OK;
+}
+
+void mt_stream_close(mt_stream* st) { delete st; }
 
 mt_status mt_prompt_embed_workspace_size(int64_t n_tokens, size_t* bytes) {
   if (!bytes) return fail(MT_ERR_INVALID_ARG, "bytes is NULL");

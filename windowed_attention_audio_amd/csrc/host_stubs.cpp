@@ -73,8 +73,14 @@ hipError_t launch_mel(const MelArgs& a, hipStream_t) {
   if (a.total_frames == 0) return hipSuccess;
   for (int i = 0; i < a.nseq; ++i) {
     const int64_t T = a.cu_frames[i + 1] - a.cu_frames[i];
-    // frames [frame_off, frame_off + T) of a sequence of seq_len samples
-    rd(a.wav + a.seq_sample_off[i], 4 * (size_t)a.seq_len[i]);
+    // frames [frame_off, frame_off + T) of a sequence of seq_len samples read
+    // samples [160 frame_off - 200, 160 (frame_off + T - 1) + 200), reflected
+    // into [0, seq_len)
+    if (T > 0) {
+      const int64_t lo = std::max<int64_t>(0, 160 * a.frame_off - 200);
+      const int64_t hi = std::min<int64_t>(a.seq_len[i], 160 * (a.frame_off + T - 1) + 200);
+      rd(a.wav + a.seq_sample_off[i] + lo, 4 * (size_t)(hi - lo));
+    }
     wr(a.mel + a.seq_row_off[i] * 128, 4 * 128 * (size_t)T);
     wr(a.gmax + i, 4);
   }
