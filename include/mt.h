@@ -162,7 +162,7 @@ mt_status mt_logmel(const float* wav, const mt_batch* wav_b, float* mel, void* w
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * computation and output as mt_logmel, without a workspace argument.  The
  * per-call tables and per-clip maxima live in a fixed array of the library,
- * 128 KiB per device, reserved until the process ends; batches of more than
+ * 256 KiB per device, reserved until the process ends; batches of more than
  * MT_LOGMEL_NOALLOC_MAX_SEQS sequences get MT_ERR_WORKSPACE before anything
  * runs.  Nothing is allocated on any call.  Every call on one device uses that
  * device's array: calls that can overlap on one device (several streams or

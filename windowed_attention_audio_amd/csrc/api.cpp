@@ -115,11 +115,23 @@ mt_status check_batch(const mt_batch* b, const char* what) {
 // ------------------------------------------------------------------ log-mel plan
 struct MelPlan {
   int B = 0;
+  int nslot = 1;        // slots per sequence for its log-mel maximum
+  int slot_stride = 1;  // ints from one slot to the next
   std::vector<int64_t> sample_off, row_off;
-  std::vector<int32_t> seq_len, cu_frames;
-  int64_t total_frames = 0, out_rows = 0, tmax = 0;
-  size_t off_sample = 0, off_row = 0, off_len = 0, off_cu = 0, off_gmax = 0, bytes = 0;
+  std::vector<int32_t> seq_len, cu_frames, cu_groups;
+  int64_t total_frames = 0, total_groups = 0, out_rows = 0, tmax = 0;
+  size_t off_sample = 0, off_row = 0, off_len = 0, off_cu = 0, off_cug = 0, off_gmax = 0, bytes = 0;
 };
+
+// Slots per sequence for the log-mel maximum, each its own cache line for
+// the frame kernel's atomics: 512 lines over the batch while it is small (a
+// single long stream would otherwise put one atomic of every wavefront on a
+// few lines), one per sequence once the sequences spread them.
+int mel_slots(int B) {
+  int n = 1;
+  while (n < 64 && n * 2 * B <= 512) n *= 2;
+  return n;
+}
 
 mt_status plan_mel(const mt_batch* wb, MelPlan& p) {
   mt_status st = check_batch(wb, "mt_logmel");
@@ -130,8 +142,10 @@ mt_status plan_mel(const mt_batch* wb, MelPlan& p) {
   p.row_off.resize(B);
   p.seq_len.resize(B);
   p.cu_frames.assign(B + 1, 0);
+  p.cu_groups.assign(B + 1, 0);
+  p.nslot = mel_slots(B);
   p.tmax = wb->layout == MT_PADDED ? wb->max_len / HOP : 0;
-  int64_t s_acc = 0, t_acc = 0;
+  int64_t s_acc = 0, t_acc = 0, g_acc = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t n = wb->len[i];
     if (n <= 200)
@@ -147,15 +161,20 @@ mt_status plan_mel(const mt_batch* wb, MelPlan& p) {
     t_acc += T;
     if (t_acc > INT32_MAX / 2) return fail(MT_ERR_UNSUPPORTED, "mt_logmel: batch too long");
     p.cu_frames[i + 1] = (int32_t)t_acc;
+    g_acc += (T + MEL_FPW - 1) / MEL_FPW;
+    p.cu_groups[i + 1] = (int32_t)g_acc;
   }
   p.total_frames = t_acc;
+  p.total_groups = g_acc;
   p.out_rows = wb->layout == MT_PADDED ? (int64_t)B * p.tmax : t_acc;
   Carver c;
   p.off_sample = c.take(8 * (size_t)B);
   p.off_row = c.take(8 * (size_t)B);
   p.off_len = c.take(4 * (size_t)B);
   p.off_cu = c.take(4 * (size_t)(B + 1));
-  p.off_gmax = c.take(4 * (size_t)B);
+  p.off_cug = c.take(4 * (size_t)(B + 1));
+  p.slot_stride = p.nslot > 1 ? 32 : 1;  // several slots: a 128-byte line each
+  p.off_gmax = c.take(4 * (size_t)B * p.nslot * p.slot_stride);
   p.bytes = c.off;
   return MT_OK;
 }
@@ -657,7 +676,7 @@ mt_status plan_stream(const mt_encoder* enc, int64_t n_samples, int32_t window, 
   if (st != MT_OK) return st;
   Carver k;
   sp.off_sat = k.take(4);  // the fp16 saturation mask of the whole stream
-  sp.off_tab = k.take(64);
+  sp.off_tab = k.take(64);  // stream_mel_at's tables (36 bytes)
   sp.off_gmax = k.take(4);
   sp.off_mel = k.take((size_t)sp.Tc * 128 * 4);
   sp.off_enc = k.take(sp.enc.bytes);
@@ -668,13 +687,14 @@ mt_status plan_stream(const mt_encoder* enc, int64_t n_samples, int32_t window, 
 // Mel frames [m0, m0 + nf) of one stream of n samples into mel (rows 0 ..
 // nf - 1): sample q of the stream is wav[q + sample_off] (a live stream keeps
 // only its recent samples), the reflection at the stream's ends uses n, the
-// frames' maximum goes into *gmax; tables in `tab` (32 bytes).
+// frames' maximum goes into *gmax; tables in `tab` (36 bytes).
 mt_status stream_mel_at(const float* wav, int64_t sample_off, int64_t n, int64_t m0, int64_t nf, float* mel,
                         char* tab, int* gmax, bool normalise, hipStream_t s) {
-  // sample_off (8) | row_off (8) | seq_len (4) | cu_frames (8)
-  uint32_t words[7] = {(uint32_t)(uint64_t)sample_off, (uint32_t)((uint64_t)sample_off >> 32), 0, 0,
-                       (uint32_t)n, 0, (uint32_t)nf};
-  HIP_TRY(upload_words((uint32_t*)tab, words, 7, s), "upload tables");
+  // sample_off (8) | row_off (8) | seq_len (4) | cu_frames (8) | cu_groups (8)
+  const int64_t ng = (nf + MEL_FPW - 1) / MEL_FPW;
+  uint32_t words[9] = {(uint32_t)(uint64_t)sample_off, (uint32_t)((uint64_t)sample_off >> 32), 0, 0,
+                       (uint32_t)n, 0, (uint32_t)nf, 0, (uint32_t)ng};
+  HIP_TRY(upload_words((uint32_t*)tab, words, 9, s), "upload tables");
   MelArgs a;
   a.wav = wav;
   a.mel = mel;
@@ -682,8 +702,12 @@ mt_status stream_mel_at(const float* wav, int64_t sample_off, int64_t n, int64_t
   a.seq_row_off = (const int64_t*)(tab + 8);
   a.seq_len = (const int32_t*)(tab + 16);
   a.cu_frames = (const int32_t*)(tab + 20);
+  a.cu_groups = (const int32_t*)(tab + 28);
   a.gmax = gmax;
+  a.nslot = 1;
+  a.slot_stride = 1;
   a.nseq = 1;
+  a.total_groups = ng;
   a.total_frames = nf;
   a.out_rows = nf;
   a.padded = 0;
@@ -742,7 +766,7 @@ mt_status plan_live(const mt_encoder* enc, int32_t window, int64_t max_push, Liv
   Carver k;
   lp.off_sat = k.take(4);  // the fp16 saturation mask of the whole stream
   lp.off_gmax = k.take(4);
-  lp.off_tab = k.take(32);
+  lp.off_tab = k.take(64);  // stream_mel_at's tables (36 bytes)
   lp.off_buf[0] = k.take((size_t)lp.cap * 4);
   lp.off_buf[1] = k.take((size_t)lp.cap * 4);
   lp.off_mel = k.take((size_t)lp.Tc * 128 * 4);
@@ -807,28 +831,34 @@ mt_status live_encode_window(mt_stream* st, const LivePlan& lp, int64_t k, bool 
 // kernel, the clamp pass.
 mt_status run_logmel(const float* wav, const mt_batch* wav_b, const MelPlan& p, float* mel, char* w,
                      hipStream_t s) {
-  // one upload: sample_off | row_off | seq_len | cu_frames (contiguous regions)
+  // one upload: sample_off | row_off | seq_len | cu_frames | cu_groups
+  // (contiguous regions), then the maxima's slots set to -inf
   std::vector<uint32_t> words(p.off_gmax / 4, 0);
   memcpy((char*)words.data() + p.off_sample, p.sample_off.data(), 8 * (size_t)p.B);
   memcpy((char*)words.data() + p.off_row, p.row_off.data(), 8 * (size_t)p.B);
   memcpy((char*)words.data() + p.off_len, p.seq_len.data(), 4 * (size_t)p.B);
   memcpy((char*)words.data() + p.off_cu, p.cu_frames.data(), 4 * (size_t)(p.B + 1));
+  memcpy((char*)words.data() + p.off_cug, p.cu_groups.data(), 4 * (size_t)(p.B + 1));
   HIP_TRY(upload_words((uint32_t*)w, words.data(), (int64_t)words.size(), s), "upload tables");
   int* gmax = (int*)(w + p.off_gmax);
   const float ninf = -INFINITY;
   int key;
   memcpy(&key, &ninf, 4);
   key = key >= 0 ? key : key ^ 0x7fffffff;
-  HIP_TRY(launch_fill_i32(gmax, key, p.B, s), "fill");
+  HIP_TRY(launch_fill_i32(gmax, key, (int64_t)p.B * p.nslot * p.slot_stride, s), "fill");
   MelArgs a;
   a.wav = wav;
   a.mel = mel;
   a.seq_sample_off = (const int64_t*)(w + p.off_sample);
   a.seq_len = (const int32_t*)(w + p.off_len);
   a.cu_frames = (const int32_t*)(w + p.off_cu);
+  a.cu_groups = (const int32_t*)(w + p.off_cug);
   a.seq_row_off = (const int64_t*)(w + p.off_row);
   a.gmax = gmax;
+  a.nslot = p.nslot;
+  a.slot_stride = p.slot_stride;
   a.nseq = p.B;
+  a.total_groups = p.total_groups;
   a.total_frames = p.total_frames;
   a.out_rows = p.out_rows;
   a.padded = wav_b->layout == MT_PADDED;
@@ -844,7 +874,7 @@ mt_status run_logmel(const float* wav, const mt_batch* wav_b, const MelPlan& p, 
 // hipGetSymbolAddress returns for the current device (taken once per device,
 // with that device current), never the array's name, which in host code is
 // only a stand-in for the symbol.
-constexpr size_t NOALLOC_SCRATCH_BYTES = 128 << 10;
+constexpr size_t NOALLOC_SCRATCH_BYTES = 256 << 10;
 static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
 constexpr int MAX_DEVICES = 64;
 std::mutex g_scratch_mu;
@@ -1296,7 +1326,7 @@ mt_status mt_logmel_noalloc(const float* wav, const mt_batch* wav_b, float* mel,
   if (st != MT_OK) return st;
   if (!wav || !mel) return fail(MT_ERR_INVALID_ARG, "mt_logmel_noalloc: NULL device pointer");
   if ((uintptr_t)mel % 16) return fail(MT_ERR_INVALID_ARG, "mt_logmel_noalloc: mel must be 16-byte aligned");
-  // 4096 sequences take 114 944 bytes of tables and maxima
+  // 4096 sequences take 131 584 bytes of tables and maxima (one slot each)
   if (p.B > MT_LOGMEL_NOALLOC_MAX_SEQS || p.bytes > NOALLOC_SCRATCH_BYTES)
     return fail(MT_ERR_WORKSPACE,
                 "mt_logmel_noalloc: %d sequences need %zu bytes of scratch, more than the library's "

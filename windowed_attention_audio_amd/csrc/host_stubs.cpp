@@ -70,7 +70,13 @@ hipError_t upload_words(uint32_t* dst, const uint32_t* src, int64_t n, hipStream
 }
 
 hipError_t launch_mel(const MelArgs& a, hipStream_t) {
-  if (a.total_frames == 0) return hipSuccess;
+  if (a.total_groups == 0) return hipSuccess;
+  if (a.cu_groups[a.nseq] != a.total_groups) return hipErrorInvalidValue;
+  for (int i = 0; i < a.nseq; ++i) {
+    const int64_t T = a.cu_frames[i + 1] - a.cu_frames[i];
+    if (a.cu_groups[i + 1] - a.cu_groups[i] != (T + MEL_FPW - 1) / MEL_FPW) return hipErrorInvalidValue;
+  }
+  wr(a.gmax, 4 * ((size_t)(a.nseq * a.nslot - 1) * a.slot_stride + 1));
   for (int i = 0; i < a.nseq; ++i) {
     const int64_t T = a.cu_frames[i + 1] - a.cu_frames[i];
     // frames [frame_off, frame_off + T) of a sequence of seq_len samples read
@@ -82,7 +88,6 @@ hipError_t launch_mel(const MelArgs& a, hipStream_t) {
       rd(a.wav + a.seq_sample_off[i] + lo, 4 * (size_t)(hi - lo));
     }
     wr(a.mel + a.seq_row_off[i] * 128, 4 * 128 * (size_t)T);
-    wr(a.gmax + i, 4);
   }
   if (a.cu_frames[a.nseq] != a.total_frames) return hipErrorInvalidValue;
   return hipSuccess;
@@ -90,7 +95,7 @@ hipError_t launch_mel(const MelArgs& a, hipStream_t) {
 
 hipError_t launch_mel_norm(const MelArgs& a, int64_t, hipStream_t) {
   wr(a.mel, 4 * 128 * (size_t)a.out_rows);
-  rd(a.gmax, 4 * (size_t)a.nseq);
+  rd(a.gmax, 4 * ((size_t)(a.nseq * a.nslot - 1) * a.slot_stride + 1));
   return hipSuccess;
 }
 

@@ -20,15 +20,25 @@ hipError_t upload_words(uint32_t* dst, const uint32_t* src, int64_t n, hipStream
 enum : int { SAT_FRONTEND = 1, SAT_LN = 2, SAT_QKV = 4, SAT_FFN = 8, SAT_HEAD = 16, SAT_ADAPTER = 32 };
 
 // ---------------------------------------------------------------- log-mel
+// Frames per group of the log-mel kernel (one wavefront each; a group never
+// spans two sequences): sequence i has ceil(T_i / MEL_FPW) groups.
+constexpr int MEL_FPW = 7;
+
 struct MelArgs {
   const float* wav;
   float* mel;
   const int64_t* seq_sample_off;  // [B]  first sample of sequence i in wav
   const int32_t* seq_len;         // [B]  samples n_i
   const int32_t* cu_frames;       // [B+1] prefix of T_i (packed frame numbering)
+  const int32_t* cu_groups;       // [B+1] prefix of ceil(T_i / MEL_FPW)
   const int64_t* seq_row_off;     // [B]  output row of frame 0 of sequence i
-  int* gmax;                      // [B]  ordered-int keys of each clip's max
+  int* gmax;                      // ordered-int keys: each clip's max is the largest
+                                  // of its nslot slots; slot j of sequence i at
+                                  // (i * nslot + j) * slot_stride
+  int nslot;
+  int slot_stride;
   int nseq;
+  int64_t total_groups;
   int64_t total_frames;
   int64_t out_rows;               // rows of the mel output (padded: B * Tmax)
   int padded;

@@ -2,31 +2,43 @@
 // Architecture table, Audio row; gotcha list: the trailing STFT frame is
 // dropped, so a clip of n samples gives floor(n / 160) frames).
 //
-// Pass 1 (mel_frames_kernel): one workgroup of 128 threads per 8 consecutive
-// frames (31 KB of LDS: five workgroups per CU).
-//   load    each frame is 400 samples centred on 160 t, the clip mirrored at
-//           both ends (reflect padding by 200, edge sample not repeated),
-//           times a periodic Hann window; reads of neighbouring frames are
-//           contiguous and coalesced.  The sequence tables (up to 128
-//           sequences) are staged in LDS first, so a frame's sequence is found
-//           without a chain of dependent memory reads.
+// Pass 1 (mel_frames_kernel): one wavefront per workgroup, one group of up to
+// FPW = 7 consecutive frames of one sequence per wavefront (the host numbers
+// each sequence's groups, so a group never spans two sequences).  The phases
+// hand over through the wavefront's own LDS region (no workgroup barrier:
+// the wavefront's LDS operations complete in order, a wait on them and a
+// wave barrier separate the phases).
+//   load    the group's samples as one span of 160 (FPW - 1) + 400 samples
+//           (reflect padding by 200 at the sequence's ends, the edge sample
+//           not repeated), coalesced, 22 loads per lane issued together.
 //   DFT     400 = 16 x 25.  With n = 25 n1 + n2 and k = k1 + 16 k2,
 //           X[k] = sum_n2 W400^(n2 k1) W25^(n2 k2) sum_n1 x[25 n1 + n2] W16^(n1 k1).
 //           Step A: 25 real 16-point DFTs per frame (outputs k1 = 0..8; the
-//           rest follow by conjugate symmetry), halved twice (even / odd
-//           indices).  Step B: per k1, the W400^(n2 k1) factors and the 25-point
-//           DFT as 5 x 5, with 5-point DFTs that pair the terms sharing a
-//           cosine; bins k = k1 + 16 k2 <= 200 are kept.  Window, twiddles and
-//           sums are in double: bins that sit 8 decades below the clip's
-//           loudest bin (the clamp floor) carry rounding of the whole frame,
-//           which in fp32 costs about 1e-4 of the normalised output.
-//   mel     |X[k]|^2 (rounded to fp32) through the sparse Slaney filterbank
-//           (about 2 non-zeros per bin); log10(max(., 1e-10)) in fp32 (a few
-//           units in the last place of values up to ~10, far below the 1e-4
-//           bar after the / 4 of pass 2), the floor itself giving -10 exactly.  The per-frame maxima are reduced in
-//           LDS and folded into each clip's maximum with one atomicMax per
-//           clip present in the workgroup.
-// Pass 2 (mel_norm_kernel, misc.hip): y = (max(x, g_clip - 8) + 4) / 4.
+//           others follow by conjugate symmetry), halved twice (even / odd
+//           indices), 175 tasks in three rounds of the 64 lanes.  Step B:
+//           lane (frame, k1) for k1 = 0..8 only -- 63 lanes -- the
+//           W400^(n2 k1) factors and the 25-point DFT as 5 x 5 with 5-point
+//           DFTs that pair the terms sharing a cosine.  A real frame has
+//           X[400 - k] = conj(X[k]), and 400 - (k1 + 16 k2) = (16 - k1) +
+//           16 (24 - k2): lane k1 in 1..7 hands out its 25 outputs as bins
+//           k1 + 16 k2 <= 200 and 400 - (k1 + 16 k2) < 200, lanes 0 and 8
+//           their 13 bins up to 200, so the 201 bins come once each and no
+//           lane computes k1 = 9..15.  Window, twiddles and sums in double:
+//           bins 8 decades below the clip's loudest bin (the clamp floor)
+//           carry rounding of the whole frame, which in fp32 costs about 1e-4
+//           of the normalised output.
+//   mel     |X[k]|^2 (rounded to fp32) through the Slaney filterbank (at
+//           most nine taps per mel bin), lane (frame, j) doing the mel bins
+//           j, j + 9, ...; log10(max(., 1e-10)) in fp32 from the hardware
+//           log2, the floor giving -10 exactly; rows written as (L + 4) / 4,
+//           staged in LDS and stored as whole 512-byte rows.
+//   max     the wavefront's maximum goes to one of the sequence's `nslot`
+//           slots (chosen by the group index; a cache line each when there
+//           are several) with one atomicMax: few wavefronts meet on one line.
+// Pass 2 (mel_norm_kernel, misc.hip): with g the largest of the sequence's
+// slots, the entries below (g - 8 + 4) / 4 are raised to it -- the same
+// values as (max(L, g - 8) + 4) / 4, since (x + 4) / 4 rounds monotonically
+// -- and only the 16-byte chunks holding such an entry are written back.
 #include "common.h"
 #include "kernels.h"
 #include "mel_tables.inc"
@@ -35,9 +47,8 @@ namespace mt {
 
 namespace {
 
-constexpr int FPB = 8;   // frames per workgroup
-constexpr int NTH = 128; // threads per workgroup (FPB x 16 in step B)
-constexpr int TBL = NTH; // sequences whose tables are staged in LDS
+constexpr int SPAN = 160 * (MEL_FPW - 1) + 400;  // samples of one group
+constexpr int SPAN_ITERS = (SPAN + 63) / 64;
 
 __device__ __forceinline__ double2 cmul(double2 a, double2 b) {
   return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
@@ -65,114 +76,120 @@ __device__ __forceinline__ void dft5(double2 u0, double2 u1, double2 u2, double2
   z[3] = make_double2(A2.x - B2.y, A2.y + B2.x);
 }
 
-__global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
-  // ys (the step-A output) and xs (raw frame samples, later |X|^2 [FPB][201])
-  // share the LDS: each phase reads what it needs into registers before the
-  // barrier after which the next phase overwrites it (29 KB: five workgroups
-  // per CU instead of three).
-  __shared__ double2 ys[FPB][25][9];   // step-A output, k1 = 0..8
-  float(*xs)[400] = (float(*)[400])&ys[0][0][0];
-  __shared__ float fmax_s[FPB];
-  __shared__ int fseq_s[FPB], ft_s[FPB], fn_s[FPB];
-  __shared__ int64_t foff_s[FPB];
-  __shared__ int32_t cu_s[TBL + 1], len_s[TBL];
-  __shared__ int64_t soff_s[TBL];
+// Every LDS access of this wavefront issued so far has completed; the
+// wavefront's lanes may now overwrite what the others read.
+__device__ __forceinline__ void lds_handover() {
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
 
-  const int tid = threadIdx.x;
-  const int64_t f0 = (int64_t)blockIdx.x * FPB;
+__global__ __launch_bounds__(64) void mel_frames_kernel(MelArgs a) {
+  // One region, four uses in turn: the sample span (floats), the step-A
+  // output Y[frame][n2][k1] (k1 = 0..8; a stride of 144 bytes per n2 keeps
+  // the frames' rows on different LDS banks), the powers P[frame][201]
+  // (floats), and from byte 8192 the log-mel rows L[frame][128] (floats).
+  __shared__ double2 buf[MEL_FPW * 25 * 9];
+  float* S = (float*)buf;
+  float* P = (float*)buf;
+  float* Lr = (float*)((char*)buf + 8192);
+  // dump slots for stores a lane makes without effect: P_DUMP after P (below
+  // byte 8192), L_DUMP after the last row of L (relative to any row of L)
+  constexpr int P_DUMP = MEL_FPW * 201;
+  constexpr int L_DUMP = MEL_FPW * 128;
+  static_assert((P_DUMP + 1) * 4 <= 8192 && 8192 + 2 * MEL_FPW * 512 <= (int)sizeof(buf), "LDS plan");
 
-  // frame -> sequence, its frame index in the stream and the sequence's
-  // samples.  Up to TBL sequences the tables are staged in LDS first (one
-  // round trip to memory instead of one per step of the search).
-  const bool staged = a.nseq <= TBL;
-  if (staged) {
-    if (tid <= a.nseq) cu_s[tid] = a.cu_frames[tid];
-    if (tid < a.nseq) {
-      len_s[tid] = a.seq_len[tid];
-      soff_s[tid] = a.seq_sample_off[tid];
-    }
-    __syncthreads();
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x;
+
+  // ---- the group's sequence: a 64-ary search over the group prefix
+  // (cu_groups[0] = 0, strictly increasing): each step probes 64 evenly
+  // spaced entries of [lo, hi) and keeps the last one <= g.
+  int lo = 0, hi = a.nseq;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int p = min(lo + lane * step, hi - 1);
+    const uint64_t le = __ballot(a.cu_groups[p] <= g);
+    const int last = 63 - __clzll((unsigned long long)le);  // the last probe <= g (probe 0 always is)
+    const int nlo = min(lo + last * step, hi - 1);
+    hi = min(lo + (last + 1) * step, hi);
+    lo = nlo;
   }
-  if (tid < FPB) {
-    const int64_t gf = f0 + tid;
-    const int32_t* cu = staged ? cu_s : a.cu_frames;
-    const int sq = gf < a.total_frames ? find_seq(cu, a.nseq, (int)gf) : -1;
-    fseq_s[tid] = sq;
-    ft_s[tid] = sq >= 0 ? (int)gf - cu[sq] + (int)a.frame_off : 0;
-    fn_s[tid] = sq >= 0 ? (staged ? len_s[sq] : a.seq_len[sq]) : 1;
-    foff_s[tid] = sq >= 0 ? (staged ? soff_s[sq] : a.seq_sample_off[sq]) : 0;
-  }
-  __syncthreads();
+  const int sq = __builtin_amdgcn_readfirstlane(lo);
+  const int T = a.cu_frames[sq + 1] - a.cu_frames[sq];
+  const int t0 = (g - a.cu_groups[sq]) * MEL_FPW;  // the group's first frame in the sequence
+  const int nf = min(MEL_FPW, T - t0);
+  const int n = a.seq_len[sq];
+  const int64_t soff = a.seq_sample_off[sq];
+  const int64_t row0 = a.seq_row_off[sq] + t0;
+  const int q0 = 160 * (t0 + (int)a.frame_off) - 200;  // stream sample of span element 0
 
-  // ---- load (the window is applied in double in step A).  All 25 samples
-  // of a thread are requested before the first is stored: a guarded load
-  // per iteration waited for each one in turn.  Frames past the end read
-  // sample 0 and store zeros.
+  // ---- load the span (reflected at the sequence's ends); all loads first.
+  // Interior spans (the usual case, uniform over the wavefront) need no
+  // reflection.
   {
-    constexpr int PER = FPB * 400 / NTH;
-    static_assert(FPB * 400 % NTH == 0, "load plan");
-    float v[PER];
+    float v[SPAN_ITERS];
+    if (q0 >= 0 && q0 + SPAN <= n) {
+      const float* src = a.wav + soff + q0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = tid + NTH * u;
-      const int f = idx / 400, j = idx - f * 400;
-      int64_t src = 0;
-      if (fseq_s[f] >= 0) {
-        const int n = fn_s[f];
-        int q = 160 * ft_s[f] + j - 200;
+      for (int i = 0; i < SPAN_ITERS; ++i) v[i] = src[min(lane + 64 * i, SPAN - 1)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPAN_ITERS; ++i) {
+        int q = q0 + min(lane + 64 * i, SPAN - 1);
         q = q < 0 ? -q : q;
         q = q >= n ? 2 * (n - 1) - q : q;
-        src = foff_s[f] + q;
+        // the frames' own samples land in [0, n) (n > 200); span positions
+        // past a partial group's last frame are only kept in bounds
+        q = min(max(q, 0), n - 1);
+        v[i] = a.wav[soff + q];
       }
-      v[u] = a.wav[src];
     }
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = tid + NTH * u;
-      const int f = idx / 400;
-      xs[f][idx - f * 400] = fseq_s[f] >= 0 ? v[u] : 0.f;
-    }
+    for (int i = 0; i < SPAN_ITERS; ++i)
+      if (lane + 64 * i < SPAN) S[lane + 64 * i] = v[i];
   }
-  __syncthreads();
+  lds_handover();
 
-  // ---- step A: (frame, n2) -> 16-point real DFT over n1 of the windowed
-  // frame, outputs k1 = 0..8.  Halving twice: with s = x[n] + x[n+8],
-  // d = x[n] - x[n+8] (n < 8), the odd k1 are sum_n d[n] W16^(n k1); with
-  // s2 = s[n] + s[n+4], d2 = s[n] - s[n+4] (n < 4), k1 = 0, 4, 8 are sums of
-  // s2 times powers of -i and k1 = 2, 6 are sum_n d2[n] W8^(n k1 / 2).  Both
-  // tasks' samples are read before the barrier: ys overwrites xs.
-  constexpr int TA = (FPB * 25 + NTH - 1) / NTH;  // tasks per thread
+  // ---- step A: task (frame, n2) -> 16-point real DFT over n1 of the
+  // windowed frame, outputs k1 = 0..8.  Halving twice: with s = x[n] +
+  // x[n+8], d = x[n] - x[n+8] (n < 8), the odd k1 are sum_n d[n] W16^(n k1);
+  // with s2 = s[n] + s[n+4], d2 = s[n] - s[n+4] (n < 4), k1 = 0, 4, 8 are sums
+  // of s2 times powers of -i and k1 = 2, 6 are sum_n d2[n] W8^(n k1 / 2).
+  // Every task's samples are read before any output is written (Y overlays
+  // the span).
+  constexpr int NT = MEL_FPW * 25;
+  constexpr int TA = (NT + 63) / 64;
   float xa[TA][16];
 #pragma unroll
-  for (int q = 0; q < TA; ++q) {
-    const int task = min(tid + NTH * q, FPB * 25 - 1);
+  for (int r = 0; r < TA; ++r) {
+    const int task = min(lane + 64 * r, NT - 1);
     const int f = task / 25, n2 = task - f * 25;
 #pragma unroll
-    for (int n1 = 0; n1 < 16; ++n1) xa[q][n1] = xs[f][25 * n1 + n2];
+    for (int n1 = 0; n1 < 16; ++n1) xa[r][n1] = S[160 * f + 25 * n1 + n2];
   }
-  __syncthreads();
+  lds_handover();
   {
     const double r8 = c_tw[50].x;  // cos(pi / 4)
 #pragma unroll
-    for (int q = 0; q < TA; ++q) {
-      const int task = tid + NTH * q;
-      if (task >= FPB * 25) break;
+    for (int r = 0; r < TA; ++r) {
+      const int task = lane + 64 * r;
+      if (task >= NT) break;
       const int f = task / 25, n2 = task - f * 25;
       double x[16];
 #pragma unroll
-      for (int n1 = 0; n1 < 16; ++n1) x[n1] = (double)xa[q][n1] * c_hann[25 * n1 + n2];
+      for (int n1 = 0; n1 < 16; ++n1) x[n1] = (double)xa[r][n1] * c_hann[25 * n1 + n2];
       double s[8], d[8], s2[4], d2[4];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        s[n] = x[n] + x[n + 8];
-        d[n] = x[n] - x[n + 8];
+      for (int m = 0; m < 8; ++m) {
+        s[m] = x[m] + x[m + 8];
+        d[m] = x[m] - x[m + 8];
       }
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        s2[n] = s[n] + s[n + 4];
-        d2[n] = s[n] - s[n + 4];
+      for (int m = 0; m < 4; ++m) {
+        s2[m] = s[m] + s[m + 4];
+        d2[m] = s[m] - s[m + 4];
       }
-      double2* out = ys[f][n2];
+      double2* out = buf + (f * 25 + n2) * 9;
       out[0] = make_double2((s2[0] + s2[2]) + (s2[1] + s2[3]), 0.0);
       out[4] = make_double2(s2[0] - s2[2], s2[3] - s2[1]);
       out[8] = make_double2((s2[0] + s2[2]) - (s2[1] + s2[3]), 0.0);
@@ -184,32 +201,31 @@ __global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
         // n = 0: W16^0 = 1; n = 4: W16^(4 k1) = -i (k1 % 4 == 1) or i
         double re = d[0], im = (k1 & 2) ? d[4] : -d[4];
 #pragma unroll
-        for (int n = 1; n < 8; ++n) {
-          if (n == 4) continue;
-          const double2 w = c_tw[(25 * n * k1) % 400];
-          re = fma(d[n], w.x, re);
-          im = fma(d[n], w.y, im);
+        for (int m = 1; m < 8; ++m) {
+          if (m == 4) continue;
+          const double2 w = c_tw[(25 * m * k1) % 400];
+          re = fma(d[m], w.x, re);
+          im = fma(d[m], w.y, im);
         }
         out[k1] = make_double2(re, im);
       }
     }
   }
-  __syncthreads();
+  lds_handover();
 
-  // ---- step B: (frame, k1) -> W400^(n2 k1), then the 25-point DFT over n2
-  // as 5 x 5 (n2 = 5 a + b, k2 = c + 5 d): five 5-point DFTs over a, the
-  // W25^(b c) factors, five 5-point DFTs over b; bins k = k1 + 16 k2 <= 200
-  // are kept.  The inputs are read before the barrier: xs overwrites ys.
+  // ---- step B: lane (frame, k1), k1 = 0..8 -> W400^(n2 k1), then the
+  // 25-point DFT over n2 as 5 x 5 (n2 = 5 a + b, k2 = c + 5 d): five 5-point
+  // DFTs over a, the W25^(b c) factors, five 5-point DFTs over b.  Powers of
+  // the bins this lane hands out into P (over Y, once every lane has read it).
+  const int fB = lane / 9, k1 = lane - 9 * fB;
+  const bool laneB = lane < MEL_FPW * 9;
   {
-    const int f = tid >> 4, k1 = tid & 15;
     double2 y[25];
 #pragma unroll
-    for (int n2 = 0; n2 < 25; ++n2) {
-      double2 v = k1 <= 8 ? ys[f][n2][k1] : ys[f][n2][16 - k1];
-      if (k1 > 8) v.y = -v.y;  // real input: Y[16 - k1] = conj(Y[k1])
-      y[n2] = cmul(v, c_tw[n2 * k1]);
-    }
-    __syncthreads();
+    for (int n2 = 0; n2 < 25; ++n2) y[n2] = buf[(min(fB, MEL_FPW - 1) * 25 + n2) * 9 + k1];
+    lds_handover();
+#pragma unroll
+    for (int n2 = 1; n2 < 25; ++n2) y[n2] = cmul(y[n2], c_tw[n2 * k1]);
     const double C1 = c_tw[80].x, S1 = -c_tw[80].y, C2 = c_tw[160].x, S2 = -c_tw[160].y;
     double2 z[5][5];  // z[b][c]
 #pragma unroll
@@ -218,71 +234,83 @@ __global__ __launch_bounds__(NTH) void mel_frames_kernel(MelArgs a) {
     for (int b = 1; b < 5; ++b)
 #pragma unroll
       for (int c = 1; c < 5; ++c) z[b][c] = cmul(z[b][c], c_tw[16 * b * c]);  // W25^(b c)
+    // outputs this lane does not hand out (lane 63; k > 200 for k1 = 0, 8)
+    // go to a dump slot past P, so the stores need no branch
+    float* Pf = P + min(fB, MEL_FPW - 1) * 201;
+    const int dump = P_DUMP - min(fB, MEL_FPW - 1) * 201;
+    const bool mirror = laneB && k1 != 0 && k1 != 8;
 #pragma unroll
     for (int c = 0; c < 5; ++c) {
       double2 o[5];  // o[d] = X[k1 + 16 (c + 5 d)]
       dft5(z[0][c], z[1][c], z[2][c], z[3][c], z[4][c], C1, S1, C2, S2, o);
 #pragma unroll
-      for (int dd = 0; dd < 3; ++dd) {
+      for (int dd = 0; dd < 5; ++dd) {
         const int k = k1 + 16 * (c + 5 * dd);
-        if (k <= 200) xs[f][k] = (float)(o[dd].x * o[dd].x + o[dd].y * o[dd].y);
+        const float pw = (float)(o[dd].x * o[dd].x + o[dd].y * o[dd].y);
+        // bin k, or 400 - k (|X[400 - k]|^2 = |X[k]|^2) for k > 200
+        Pf[k <= 200 ? (laneB ? k : dump) : (mirror ? 400 - k : dump)] = pw;
       }
     }
   }
-  __syncthreads();
+  lds_handover();
 
-  // ---- mel + log10; thread (frame = tid/16, part = tid%16) does 8 mel bins
+  // ---- mel + log10; lane (frame, j) does the mel bins j, j + 9, ... with
+  // the dense filter rows (nine weights from the filter's first bin, zero
+  // past its end: the same sums as over the non-zero taps), every row's
+  // three 16-byte loads issued before the first product.  log10 as the
+  // hardware log2 times log10(2) (error ~1e-6 on values up to ~10, below the
+  // 1e-4 bar by far after the / 4), the floor giving -10 exactly.  Rows are
+  // written as (L + 4) / 4: the clamp pass then only raises the entries below
+  // the floor.
+  constexpr int MI = (128 + 8) / 9;  // 15 bins for lanes j < 2, 14 for the rest
+  float lmax = -INFINITY;
   {
-    const int f = tid >> 4, part = tid & 15;
-    const int sq = fseq_s[f];
-    float lmax = -INFINITY;
-    float L[8];
+    float4 w[MI][3];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int m = part + 16 * r;
-      const int first = c_mel_first[m], cnt = c_mel_count[m], off = c_mel_off[m];
-      float e = 0.f;
-      for (int b = 0; b < cnt; ++b) e += c_mel_w[off + b] * xs[f][first + b];
-      L[r] = e > 1e-10f ? log10f(e) : -10.0f;  // the floor: log10(1e-10) = -10 exactly
-      lmax = fmaxf(lmax, L[r]);
+    for (int i = 0; i < MI; ++i) {
+      const int m = min(k1 + 9 * i, 127);
+      const float4* row = (const float4*)(c_mel_pad + MEL_PAD * m);
+      w[i][0] = row[0];
+      w[i][1] = row[1];
+      w[i][2] = row[2];
     }
-    if (sq >= 0) {
-      const int t = (int)(f0 + f) - (staged ? cu_s[sq] : a.cu_frames[sq]);
-      float* out = a.mel + (a.seq_row_off[sq] + t) * 128;
+    const float* Pf = P + min(fB, MEL_FPW - 1) * 201;
+    float* Lf = Lr + min(fB, MEL_FPW - 1) * 128;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) out[part + 16 * r] = L[r];
+    for (int i = 0; i < MI; ++i) {
+      const int m = k1 + 9 * i;
+      const float* p = Pf + (int)w[i][2].y;
+      float e = w[i][0].x * p[0];
+      e += w[i][0].y * p[1];
+      e += w[i][0].z * p[2];
+      e += w[i][0].w * p[3];
+      e += w[i][1].x * p[4];
+      e += w[i][1].y * p[5];
+      e += w[i][1].z * p[6];
+      e += w[i][1].w * p[7];
+      e += w[i][2].x * p[8];
+      const float L = e > 1e-10f ? __builtin_amdgcn_logf(e) * 0.30102999566398120f : -10.0f;
+      const bool keep = laneB && m < 128;
+      Lf[keep ? m : L_DUMP] = (L + 4.0f) * 0.25f;  // Lf[L_DUMP]: past the rows, unused
+      lmax = fmaxf(lmax, keep && fB < nf ? L : -INFINITY);
     }
-    // maximum over the 16 lanes of the frame: DPP row rotations (the maximum
-    // does not depend on the order)
-    lmax = fmaxf(lmax, dpp_f<0x128>(lmax));
-    lmax = fmaxf(lmax, dpp_f<0x124>(lmax));
-    lmax = fmaxf(lmax, dpp_f<0x122>(lmax));
-    lmax = fmaxf(lmax, dpp_f<0x121>(lmax));
-    if (part == 0) fmax_s[f] = lmax;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int cur = fseq_s[0];
-    float m = -INFINITY;
-    for (int f = 0; f < FPB; ++f) {
-      const int sq = fseq_s[f];
-      if (sq != cur) {
-        if (cur >= 0) atomicMax(a.gmax + cur, float_key(m));
-        cur = sq;
-        m = -INFINITY;
-      }
-      m = fmaxf(m, fmax_s[f]);
-    }
-    if (cur >= 0) atomicMax(a.gmax + cur, float_key(m));
-  }
+  lds_handover();
+
+  // ---- whole rows out: nf x 32 float4
+  float* out = a.mel + row0 * 128;
+  for (int i = lane; i < nf * 32; i += 64) ((float4*)out)[i] = ((const float4*)Lr)[i];
+
+  // ---- the wavefront's maximum into one of the sequence's slots
+  lmax = wave_max64(lmax);
+  if (lane == 0) atomicMax(a.gmax + (int64_t)(sq * a.nslot + g % a.nslot) * a.slot_stride, float_key(lmax));
 }
 
 }  // namespace
 
 hipError_t launch_mel(const MelArgs& a, hipStream_t s) {
-  if (a.total_frames == 0) return hipSuccess;
-  const int64_t blocks = (a.total_frames + FPB - 1) / FPB;
-  hipLaunchKernelGGL(mel_frames_kernel, dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+  if (a.total_groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(mel_frames_kernel, dim3((unsigned)a.total_groups), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

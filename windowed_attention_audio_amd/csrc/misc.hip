@@ -1,5 +1,7 @@
 // Small kernels: table upload, fills, the log-mel clamp pass, row copies and
 // the one-time weight repacking.
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -23,34 +25,54 @@ __global__ void fill_i32_kernel(int* p, int v, int64_t n) {
     p[i] = v;
 }
 
-// Log-mel clamp: y = (max(x, g - 8) + 4) / 4 with g the clip's maximum;
-// padded rows beyond a clip are set to 0.  One float4 per thread.
-__global__ void mel_norm_kernel(MelArgs a, int64_t tmax) {
-  const int64_t i4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i4 >= a.out_rows * 32) return;
-  const int64_t row = i4 >> 5;
-  int sq;
-  bool valid;
-  if (a.padded) {
-    sq = (int)(row / tmax);
-    const int64_t t = row - sq * tmax;
-    valid = t < (int64_t)(a.cu_frames[sq + 1] - a.cu_frames[sq]);
-  } else {
-    sq = find_seq(a.cu_frames, a.nseq, (int)row);
-    valid = true;
+// Log-mel clamp.  The frame kernel wrote y = (L + 4) / 4; with g the
+// clip's maximum (the largest of its slots) the result is (max(L, g - 8) +
+// 4) / 4, i.e. y raised to (g - 8 + 4) / 4 where L < g - 8 ((x + 4) / 4 in
+// fp32 is monotone, so comparing y decides the same entries and gives the
+// same values).  A chunk with nothing below the floor is left as it is.
+// Padded rows beyond a clip are set to 0.  A workgroup covers 8 rows, one
+// float4 per thread; its first wavefront reduces each row's slots first (8
+// lanes per row).
+__global__ __launch_bounds__(256) void mel_norm_kernel(MelArgs a, int64_t tmax) {
+  __shared__ float floor_s[8];
+  __shared__ int valid_s[8];
+  const int64_t row0 = (int64_t)blockIdx.x * 8;
+  if (threadIdx.x < 64) {
+    const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const int64_t row = min(row0 + r, a.out_rows - 1);
+    int sq;
+    bool valid;
+    if (a.padded) {
+      sq = (int)(row / tmax);
+      valid = row - sq * tmax < (int64_t)(a.cu_frames[sq + 1] - a.cu_frames[sq]);
+    } else {
+      sq = find_seq(a.cu_frames, a.nseq, (int)row);
+      valid = true;
+    }
+    int key = INT_MIN;  // below every float's key
+    for (int i = part; i < a.nslot; i += 8)  // keys order as the floats do
+      key = max(key, a.gmax[(int64_t)(sq * a.nslot + i) * a.slot_stride]);
+    key = max(key, __shfl_xor(key, 1));
+    key = max(key, __shfl_xor(key, 2));
+    key = max(key, __shfl_xor(key, 4));
+    if (part == 0) {
+      floor_s[r] = (key_float(key) - 8.0f + 4.0f) * 0.25f;
+      valid_s[r] = valid;
+    }
   }
+  __syncthreads();
+  const int64_t i4 = row0 * 32 + threadIdx.x;
+  if (i4 >= a.out_rows * 32) return;
+  const int r = threadIdx.x >> 5;
   float4* p = (float4*)a.mel + i4;
-  if (!valid) {
+  if (!valid_s[r]) {
     *p = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const float lo = key_float(a.gmax[sq]) - 8.0f;
-  float4 v = *p;
-  v.x = (fmaxf(v.x, lo) + 4.0f) * 0.25f;
-  v.y = (fmaxf(v.y, lo) + 4.0f) * 0.25f;
-  v.z = (fmaxf(v.z, lo) + 4.0f) * 0.25f;
-  v.w = (fmaxf(v.w, lo) + 4.0f) * 0.25f;
-  *p = v;
+  const float lo = floor_s[r];
+  const float4 v = *p;
+  if (v.x < lo || v.y < lo || v.z < lo || v.w < lo)
+    *p = make_float4(fmaxf(v.x, lo), fmaxf(v.y, lo), fmaxf(v.z, lo), fmaxf(v.w, lo));
 }
 
 // Rows >= N_i of each padded output sequence are set to 0.
@@ -223,9 +245,8 @@ hipError_t launch_fill_i32(int* p, int v, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_mel_norm(const MelArgs& a, int64_t tmax, hipStream_t s) {
-  const int64_t n = a.out_rows * 32;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(mel_norm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, tmax);
+  if (a.out_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(mel_norm_kernel, dim3((unsigned)((a.out_rows + 7) / 8)), dim3(256), 0, s, a, tmax);
   return hipGetLastError();
 }
 
