@@ -48,7 +48,9 @@ mt_status hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 constexpr int64_t HOP = 160;
-constexpr int TABLE_HEAD_WORDS = 64;  // the encode workspace's first 256 bytes: the saturation mask
+constexpr int TABLE_HEAD_WORDS = 64;
+// fp32 encoders: partial sums of the K-split products (see GemmArgs::part)
+constexpr int64_t SPLIT_PART_FLOATS = 4 << 20;  // the encode workspace's first 256 bytes: the saturation mask
 constexpr int MAX_WINDOW = 256;
 constexpr int64_t MAX_SEQS = 1 << 20;
 constexpr size_t ALIGN = 256;
@@ -305,7 +307,7 @@ struct EncPlan {
   int wpad = 0;
   // workspace offsets
   size_t o_words, o_rowoff, o_twords, o_act1, o_act2, o_act3, o_x, o_h, o_qkv, o_att, o_ffn, o_y, o_ahid,
-      bytes;
+      o_part, bytes;
 };
 
 // One chunk of a stream (mt_encode_stream): the batch is one sequence, a
@@ -424,6 +426,8 @@ mt_status plan_encode(const mt_encoder* enc, const mt_batch* mb, int32_t window,
   p.o_ffn = k.take(fb);
   p.o_y = k.take(A ? M * O * es : 0);
   p.o_ahid = k.take(A ? M * A * es : 0);
+  // fp32 operands: partial sums and tile counters of the K-split products
+  p.o_part = k.take(enc->dt == DT_F32 ? SPLIT_PART_FLOATS * 4 : 0);
   p.bytes = k.off;
   return MT_OK;
 }
@@ -485,12 +489,16 @@ mt_status run_encode(const mt_encoder* enc, const EncPlan& p, const float* mel, 
   void* ybuf = w + p.o_y;
   void* ahid = w + p.o_ahid;
 
+  // fp32: partial sums of the K-split products
+  float* part = dt == DT_F32 ? (float*)(w + p.o_part) : nullptr;
   auto gemm = [&](const void* A_, int64_t lda, const void* B_, int64_t ldb, int M_, int N_, int K_,
                   const float* bias, void* C_, int64_t ldc, int sat_bit = 0) {
     GemmArgs g_ = ::gemm(A_, lda, B_, ldb, M_, N_, K_, bias, C_, ldc);
     g_.zeros = enc->zeros;
     g_.sat = sat_bit ? sat : nullptr;
     g_.sat_bit = sat_bit;
+    g_.part = part;
+    g_.part_floats = part ? SPLIT_PART_FLOATS : 0;
     return g_;
   };
 

@@ -28,6 +28,8 @@
 // k = 8*(l/16)..+7 of the 32-wide step).  For fp32 it is four v_mfma_f32_16x16x4_f32, the e-th
 // one taking element e of every lane's chunk; as both operands use the same
 // assignment of k to (lane group, element), the sum over k is unchanged.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -326,10 +328,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < BP; ++j) brow_ok[j] = (n0 + r0 + j * RPP) < a.N;
 
+  // K split (fp32 products with few output tiles): this workgroup sums the
+  // K steps [kb0, kb1) of its tile and leaves the partial sums to
+  // gemm_split_sum_kernel.
+  const int nkb_all = (a.K + BK - 1) / BK;
+  const int nz = gridDim.y, kz = blockIdx.y;
+  const int kb0 = (int)((int64_t)nkb_all * kz / nz), kb1 = (int)((int64_t)nkb_all * (kz + 1) / nz);
+
   // convolution: track (tap, channel) of this thread's chunk incrementally
-  int ctap = 0, cch = c * EPC;
+  int ctap = 0, cch = 0;
   if constexpr (CONV) {
-    while (cch >= a.conv_C) { cch -= a.conv_C; ++ctap; }
+    const int k0 = kb0 * BK + c * EPC;
+    ctap = k0 / a.conv_C;
+    cch = k0 - ctap * a.conv_C;
   }
 
   uint4 ra[AP], rb[BP];
@@ -387,16 +398,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nkb = (a.K + BK - 1) / BK;
-  gload(0);
+  gload(kb0);
   sstore(0);
   __syncthreads();
 
   const int g = lane >> 4;
   const int l16 = lane & 15;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int buf = (kb - kb0) & 1;
+    if (kb + 1 < kb1) gload(kb + 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int cc = 4 * s + g;
@@ -416,11 +426,59 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) mma_chunk<T>(acc[i][j], bfr[j], af[i]);  // C^T tile
     }
-    if (kb + 1 < nkb) sstore(buf ^ 1);
+    if (kb + 1 < kb1) sstore(buf ^ 1);
     __syncthreads();
   }
 
+  if (nz > 1) {
+    // partial sums as [split][tile][wavefront][i][j][lane] float4, added up
+    // in split order by gemm_split_sum_kernel
+    constexpr int PER = MI * NI * 64;  // float4 per wavefront and split
+    float4* mine = (float4*)a.part + (((int64_t)kz * gridDim.x + blockIdx.x) * 4 + wave) * PER + lane;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        mine[(i * NI + j) * 64] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    return;
+  }
+
   // ---- epilogue: lane holds C[l16][4g + e] of every 16 x 16 tile
+  epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
+}
+
+// The second half of a K-split product (gemm_kernel with gridDim.y = nz >
+// 1): per output tile, the nz partial sums added in split order (the same
+// order every time), then the product's epilogue.
+template <typename T, int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void gemm_split_sum_kernel(GemmArgs a, int nz) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int MI = WTM / 16, NI = WTN / 16;
+  constexpr int PER = MI * NI * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
+  const int m0 = bm * BM, n0 = bn * BN;
+  const int g = lane >> 4, l16 = lane & 15;
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < nz; ++z) {
+    const float4* pz = (const float4*)a.part + (((int64_t)z * gridDim.x + blockIdx.x) * 4 + wave) * PER + lane;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const float4 v = pz[(i * NI + j) * 64];
+        acc[i][j][0] += v.x;
+        acc[i][j][1] += v.y;
+        acc[i][j][2] += v.z;
+        acc[i][j][3] += v.w;
+      }
+  }
   epilogue4<T, EPI, MI, NI>(a, acc, m0 + wm * WTM + l16, n0 + wn * WTN + 4 * g);
 }
 
@@ -1315,11 +1373,25 @@ hipError_t run_w8q(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Register-staged kernel.  With a partial-sum workspace (fp32 products),
+// K is split when the output tiles alone would leave most CUs idle: up to
+// GEMM_SPLIT_MAX splits of at least four 32-wide K steps, about 512
+// workgroups in all, as many as the workspace holds; a second kernel adds
+// the partial sums (the kernel boundary orders them, no fences or counters).
 template <typename T, int BM, int BN, int EPI, bool CONV>
 hipError_t run(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, EPI, CONV>), dim3(tiles), dim3(256), 0, s, a);
+  int nz = 1;
+  if (a.part && tiles < 256) {
+    constexpr int BK = 8 * Elem<T>::per16;
+    const int nkb = (a.K + BK - 1) / BK;
+    nz = std::min(std::min(GEMM_SPLIT_MAX, nkb / 4), (511 + tiles) / tiles);
+    while (nz > 1 && (int64_t)nz * tiles * BM * BN > a.part_floats) --nz;
+    nz = std::max(nz, 1);
+  }
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, EPI, CONV>), dim3(tiles, nz), dim3(256), 0, s, a);
+  if (nz > 1) hipLaunchKernelGGL((gemm_split_sum_kernel<T, BM, BN, EPI>), dim3(tiles), dim3(256), 0, s, a, nz);
   return hipGetLastError();
 }
 
@@ -1353,10 +1425,12 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
       // against 617 / 541; four stages gained another ~6 % on fc2).
       const bool w8 = a.K % 128 == 0 && (int64_t)a.M * a.lda * 2 < (1ll << 31) &&
                       (int64_t)a.N * a.ldb * 2 < (1ll << 31);
-      if (w8 && a.N >= 2048) {
+      // With fewer than 128 such tiles (a single clip, a stream chunk) most
+      // CUs would idle: the smaller tiles below (same K order, same results).
+      const int t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+      if (w8 && a.N >= 2048 && t256 >= 128) {
         if constexpr (EPI != EPI_SWIGLU) {
-          const int tm = (a.M + 255) / 256;
-          const int t256 = tm * ((a.N + 255) / 256), t192 = tm * ((a.N + 191) / 192);
+          const int t192 = ((a.M + 255) / 256) * ((a.N + 191) / 192);
           const double e256 = t256 / (256.0 * ((t256 + 255) / 256));
           const double e192 = t192 / (256.0 * ((t192 + 255) / 256));
           if (e192 > 1.15 * e256) return run_w8<T, 192, EPI>(a, s);
@@ -1389,6 +1463,9 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
     if (a.N % 160 == 0) return run<T, 128, 160, EPI, CONV>(a, s);
     return run<T, 128, 128, EPI, CONV>(a, s);
   } else {
+    // few rows (a short clip): 32 x 64 tiles, not 128 x 128 of which most
+    // rows would be padding
+    if (a.M <= 32) return run<T, 32, 64, EPI, CONV>(a, s);
     return run<T, 128, 128, EPI, CONV>(a, s);
   }
 }

@@ -107,7 +107,15 @@ struct GemmArgs {
   const void* zeros;       // >= 16 bytes of zeros (device), read by out-of-range loads
   int* sat;                // fp16 16-bit outputs: saturation mask, bit sat_bit (nullptr: off)
   int sat_bit;
+  // fp32 operands: when part is set and the product has too few output
+  // tiles to fill the GPU, K is split over up to GEMM_SPLIT_MAX workgroups
+  // per tile (as many as part_floats floats of partial sums allow) and a
+  // second launch adds the partial sums.
+  float* part;
+  int64_t part_floats;
 };
+
+constexpr int GEMM_SPLIT_MAX = 16;
 
 // dtype: DT_F32, DT_BF16 or DT_F16 operands (fp32 accumulation in every
 // case).  conv: gather A as a 3x3 stride-2 convolution input.
