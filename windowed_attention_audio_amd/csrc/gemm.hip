@@ -15,8 +15,10 @@
 //   gemm_w8q_kernel  the same with four stages of 32-wide slices (narrow
 //                    outputs at M = 6000, the convolutions with the tap
 //                    gather);
-//   gemm_lds_kernel  128 x 128 / 64 x 64 tiles, four wavefronts (few rows);
-//   gemm_kernel      register-staged tiles for fp32 operands.
+//   gemm_lds_kernel  128 x 128 / 64 x 64 tiles, four wavefronts, four LDS
+//                    stages (few rows);
+//   gemm_kernel      register-staged tiles for fp32 operands (K split over
+//                    workgroups when the tiles are few).
 // Every 16-bit kernel accumulates each output over K in 32-wide steps in
 // the same order, so a row's result does not depend on the kernel, the tile
 // or the batch it was computed in.  Within LDS each row's 16-byte chunks are XOR-
@@ -486,10 +488,10 @@ __global__ __launch_bounds__(256) void gemm_split_sum_kernel(GemmArgs a, int nz)
 // ---------------------------------------------------------------------------
 // 16-bit operands: WM x WN wavefronts, BM x BN tile, K slices of 64 copied
 // global -> LDS by the matrix-load DMA (global_load_lds_dwordx4: lane j of a
-// wavefront writes bytes [16 j, 16 j + 16) of a 1 KB LDS block), two LDS
-// stages.  The slice for kb + 1 is in flight while slice kb feeds the matrix
-// cores; each wavefront waits only for its own earlier loads (vmcnt) before
-// the barrier that publishes a stage.  Loads that fall outside the matrices
+// wavefront writes bytes [16 j, 16 j + 16) of a 1 KB LDS block), two or
+// four LDS stages.  The next slices are in flight while slice kb feeds the
+// matrix cores; each wavefront waits only for its own earlier loads (vmcnt)
+// before the barrier that publishes a stage.  Loads that fall outside the matrices
 // (row or K tails, convolution padding) read a 16-byte block of zeros.
 // Rows of a stage: A rows [0, BM), then B rows [BM, BM + BN); 128 bytes each,
 // chunk c of row r stored at chunk slot c ^ swz(r).
@@ -500,7 +502,8 @@ __device__ __forceinline__ void wait_vm(int n) {
 #define MT_WAITVM(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); break;
     MT_WAITVM(0) MT_WAITVM(1) MT_WAITVM(2) MT_WAITVM(3) MT_WAITVM(4) MT_WAITVM(5) MT_WAITVM(6)
     MT_WAITVM(7) MT_WAITVM(8) MT_WAITVM(9) MT_WAITVM(10) MT_WAITVM(11) MT_WAITVM(12)
-    MT_WAITVM(13) MT_WAITVM(14) MT_WAITVM(15) MT_WAITVM(16)
+    MT_WAITVM(13) MT_WAITVM(14) MT_WAITVM(15) MT_WAITVM(16) MT_WAITVM(18) MT_WAITVM(20)
+    MT_WAITVM(24)
 #undef MT_WAITVM
     default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
   }
@@ -521,10 +524,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_lds_kernel(GemmArgs a) {
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be 16-aligned");
   static_assert(EPI != EPI_SWIGLU || (WTN % 32) == 0, "SwiGLU pairs need 32-column wave tiles");
   static_assert(BPW <= 16, "too many loads per wavefront");
-  static_assert(NST == 2, "two LDS stages");
+  static_assert(NST == 2 || NST == 4, "two or four LDS stages");
 
   __shared__ uint4 st0[ROWS * 8];
   __shared__ uint4 st1[ROWS * 8];
+  __shared__ uint4 st2[NST == 4 ? ROWS * 8 : 1];
+  __shared__ uint4 st3[NST == 4 ? ROWS * 8 : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -649,16 +654,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_lds_kernel(GemmArgs a) {
     }
   };
 
-  // Two LDS stages: slice kb lives in stage kb % 2 and slice kb + 2 is loaded
-  // while slice kb + 1 is consumed.  The slice count is padded to an even
-  // number (a slice past K loads zeros and adds nothing) and the last slice
-  // is peeled off, so the loop body has no branch that touches the
-  // accumulators (the register allocator keeps them in place).  Phases are
-  // pinned with sched_barrier: the compiler would otherwise wait for all
+  // NST LDS stages: slice kb lives in stage kb % NST, and once its stage is
+  // free slice kb + NST is requested, NST - 1 slices ahead of its use (four
+  // stages for few rows: their workgroups walk K with little matrix-core
+  // work per slice to cover the loads).  The slice count is padded to a
+  // multiple of NST (a slice past K loads zeros and adds nothing) and the
+  // last slice is peeled off, so the loop body has no branch that touches
+  // the accumulators (the register allocator keeps them in place).  Phases
+  // are pinned with sched_barrier: the compiler would otherwise wait for all
   // outstanding LDS reads before the first MFMA of a phase and hoist the DMA
   // address arithmetic in front of the matrix-core work.
   constexpr int MH = MI / 2;
-  const int nkb = ((a.K + 127) / 128) * 2;
+  const int nkb = (a.K + 64 * NST - 1) / (64 * NST) * NST;
   auto step = [&](int kb, const uint4* CUR, const uint4* NXT) {  // kb + 1 < nkb
     mma(fa0, fb0, 0, MH);              // k-step 0 of slice kb (read during the last phase)
     __builtin_amdgcn_sched_barrier(0);
@@ -666,7 +673,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_lds_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     mma(fa0, fb0, MH, MI);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm(0);                        // this wavefront's DMA of slice kb+1 has landed
+    // this wavefront's DMA of slice kb+1 has landed (slices kb+2 .. kb+NST-1
+    // may still be in flight)
+    wait_vm(nblk * max(0, min(nkb - kb - 2, NST - 2)));
     __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));  // lgkmcnt(0): reads of CUR done
     __builtin_amdgcn_s_barrier();      // every wavefront's has; CUR is no longer read
     __builtin_amdgcn_sched_barrier(0);
@@ -674,7 +683,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_lds_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     mma(fa1, fb1, 0, MH);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 2 < nkb) issue((uint4*)CUR, kb + 2);
+    if (kb + NST < nkb) issue((uint4*)CUR, kb + NST);
     __builtin_amdgcn_sched_barrier(0);
     mma(fa1, fb1, MH, MI);
     __builtin_amdgcn_sched_barrier(0);
@@ -682,17 +691,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_lds_kernel(GemmArgs a) {
 
   issue(st0, 0);
   issue(st1, 1);
-  wait_vm(nblk);
+  if constexpr (NST == 4) {
+    issue(st2, 2);
+    issue(st3, 3);
+  }
+  wait_vm(nblk * (NST - 1));
   __builtin_amdgcn_s_barrier();
   ldfrag(st0, 0, fa0, fb0);
-  // unrolled by two so that every LDS access names its stage array: the
+  // unrolled by NST so that every LDS access names its stage array: the
   // compiler then sees that reads of one stage do not alias DMA into another
-  for (int kb = 0; kb < nkb - 2; kb += 2) {
-    step(kb, st0, st1);
-    step(kb + 1, st1, st0);
+  if constexpr (NST == 2) {
+    for (int kb = 0; kb < nkb - 2; kb += 2) {
+      step(kb, st0, st1);
+      step(kb + 1, st1, st0);
+    }
+    step(nkb - 2, st0, st1);
+    ldfrag(st1, 1, fa1, fb1);            // last slice
+  } else {
+    for (int kb = 0; kb < nkb - 4; kb += 4) {
+      step(kb, st0, st1);
+      step(kb + 1, st1, st2);
+      step(kb + 2, st2, st3);
+      step(kb + 3, st3, st0);
+    }
+    step(nkb - 4, st0, st1);
+    step(nkb - 3, st1, st2);
+    step(nkb - 2, st2, st3);
+    ldfrag(st3, 1, fa1, fb1);            // last slice
   }
-  step(nkb - 2, st0, st1);
-  ldfrag(st1, 1, fa1, fb1);            // last slice
   mma(fa0, fb0, 0, MI);
   mma(fa1, fb1, 0, MI);
 
@@ -1453,8 +1479,8 @@ hipError_t pick_tile(const GemmArgs& a, hipStream_t s) {
       // (measured: M = 375, N = 1280, K = 1280 17.7 -> 8.9 us; M = 832,
       // N = 1280, K = 5120 67.3 -> 42.0 us; M = 832, N = 5120: 128 x 128
       // stays ahead with 280 tiles).
-      if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 256) return run_lds<T, 128, 128, 2, 2, 2, EPI, CONV>(a, s);
-      return run_lds<T, 64, 64, 2, 2, 2, EPI, CONV>(a, s);
+      if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 256) return run_lds<T, 128, 128, 2, 2, 4, EPI, CONV>(a, s);
+      return run_lds<T, 64, 64, 2, 2, 4, EPI, CONV>(a, s);
     }
   }
   if constexpr (CONV) {
