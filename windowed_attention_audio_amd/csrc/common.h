@@ -163,4 +163,19 @@ __device__ __forceinline__ void mma_f32x4(f32x4& acc, const uint4& a, const uint
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9
+// encoding: vmcnt bits 3:0 and 15:14); n beyond the listed cases waits for
+// everything, which is always safe.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define MT_WAITVM(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); break;
+    MT_WAITVM(0) MT_WAITVM(1) MT_WAITVM(2) MT_WAITVM(3) MT_WAITVM(4) MT_WAITVM(5) MT_WAITVM(6)
+    MT_WAITVM(7) MT_WAITVM(8) MT_WAITVM(9) MT_WAITVM(10) MT_WAITVM(11) MT_WAITVM(12)
+    MT_WAITVM(13) MT_WAITVM(14) MT_WAITVM(15) MT_WAITVM(16) MT_WAITVM(17) MT_WAITVM(18) MT_WAITVM(19)
+    MT_WAITVM(20) MT_WAITVM(21) MT_WAITVM(22) MT_WAITVM(23) MT_WAITVM(24) MT_WAITVM(28) MT_WAITVM(32)
+#undef MT_WAITVM
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+  }
+}
+
 }  // namespace mt

@@ -496,19 +496,6 @@ __global__ __launch_bounds__(256) void gemm_split_sum_kernel(GemmArgs a, int nz)
 // Rows of a stage: A rows [0, BM), then B rows [BM, BM + BN); 128 bytes each,
 // chunk c of row r stored at chunk slot c ^ swz(r).
 
-__device__ __forceinline__ void wait_vm(int n) {
-  // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding)
-  switch (n) {
-#define MT_WAITVM(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)); break;
-    MT_WAITVM(0) MT_WAITVM(1) MT_WAITVM(2) MT_WAITVM(3) MT_WAITVM(4) MT_WAITVM(5) MT_WAITVM(6)
-    MT_WAITVM(7) MT_WAITVM(8) MT_WAITVM(9) MT_WAITVM(10) MT_WAITVM(11) MT_WAITVM(12)
-    MT_WAITVM(13) MT_WAITVM(14) MT_WAITVM(15) MT_WAITVM(16) MT_WAITVM(18) MT_WAITVM(20)
-    MT_WAITVM(24)
-#undef MT_WAITVM
-    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
-  }
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <typename T, int BM, int BN, int WM, int WN, int NST, int EPI, bool CONV>
