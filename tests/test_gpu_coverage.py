@@ -3,7 +3,8 @@ matrix operands, and the bounded-memory stream against the oracle.
 
   * each of the 16 clips of the 16 x 30 s batch, encoded alone through all 32
     layers, equals its rows of the batch bitwise (fp16 and bf16 operands), so
-    the oracle-sampled clips stand for every clip of the batch;
+    the oracle-sampled clips stand for every clip of the batch; the same for
+    the 32 variable-length clips with the adapter;
   * bf16 activations at the matrix cores (MT_BF16): the 16 x 30 s batch and
     the 10-minute stream within the parity bar; the 32-clip adapter workload
     outside it (documented, bounded);
@@ -130,6 +131,27 @@ def test_encode_stream_vs_oracle(models, stream10, P64, cw):
     for k, g, r in _stream_windows(got, ref_mel, P64, w.window, (0, 1, 40, 72), 7500):
         m = assert_bf16_rows(g, r, what=f"stream chunk_windows={cw} window {k}")
         say(f"  window {k}: min cos {m['cos'].min():.6f} max|d|/rms {m['maxabs_rms'].max():.4f}")
+
+
+def test_varlen_adapter_every_clip_alone_bitwise(weights_bf16):
+    # the 32 variable-length clips of 2-60 s with the adapter, window 52:
+    # each clip encoded alone (its products on the small-row kernels) equals
+    # its rows of the packed batch (13 613 rows: the 256-row kernels)
+    # bitwise, so the clips the oracle samples stand for all 32
+    w = synth.workload(4)
+    geom = synth.geom_for(w)
+    wts = synth.with_adapter(weights_bf16, geom, bf16=True)
+    ad = GpuModel(geom, "f16", wts)
+    clips = synth.make_clips(w)
+    mel = gpu_logmel(clips)
+    T = [len(c) // 160 for c in clips]
+    N = [OE.encoder_frames(t) for t in T]
+    mels = split_rows(mel, T)
+    say(f"32 varlen clips + adapter: batch ({sum(N)} rows) vs each clip alone")
+    rows = split_rows(ad.encode(mels, w.window), N)
+    for i, m in enumerate(mels):
+        alone = ad.encode([m], w.window)
+        assert np.array_equal(alone, rows[i]), f"clip {i} (N={N[i]}): alone != its rows in the batch"
 
 
 def test_bf16_varlen_adapter_outside_bar(weights_bf16):
