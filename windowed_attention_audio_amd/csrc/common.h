@@ -63,6 +63,24 @@ __device__ __forceinline__ float gelu_f(float x) {
   return fmaf(fabsf(x), r, 0.5f * x);
 }
 
+// gelu_f(x) from h = x / 2, with the same bits and one instruction less.
+// Every step of gelu_f is rescaled by a power of two, which commutes with
+// rounding: p |x| = (2 p) |h|, x x c = (h h)(4 c), the polynomial with
+// doubled coefficients is 2 P, fma(-2 P, e, 1) = 2 r, and fma(|h|, 2 r, h)
+// rounds |x| r + x / 2 once, as gelu_f does.  h itself comes from the
+// pre-activation in one instruction: fma(acc, 1/2, b / 2) = (acc + b) / 2
+// (or a dot product whose weights and bias were halved).
+__device__ __forceinline__ float gelu_h(float h) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(2.0f * 0.23164190f, fabsf(h), 1.0f));
+  const float P = t * fmaf(fmaf(fmaf(fmaf(2.0f * 0.5307027145f, t, 2.0f * -0.726576013f), t, 2.0f * 0.7107068705f),
+                                t, 2.0f * -0.142248368f),
+                           t, 2.0f * 0.127414796f);
+  const float r = fmaf(-P, __builtin_amdgcn_exp2f(h * h * (4.0f * -0.72134752044f)), 1.0f);  // 1 - 2 h_tail
+  return fmaf(fabsf(h), r, h);
+}
+// GELU(acc + b) given hb = b / 2.
+__device__ __forceinline__ float gelu_ab(float acc, float hb) { return gelu_h(fmaf(acc, 0.5f, hb)); }
+
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
 // Reductions over the 64 lanes of a wavefront in the butterfly order (the
@@ -105,8 +123,17 @@ __device__ __forceinline__ void report_saturation(int* sat, int bit, float amax)
   const uint64_t over = __ballot(amax > 65504.0f);
   if (over && (int)(threadIdx.x & 63) == __ffsll((unsigned long long)over) - 1) atomicOr(sat, bit);
 }
+// Largest magnitude so far.  Written as medians with +inf (max(x, m) =
+// med3(x, m, inf)), which the compiler folds into two v_max3_f32 with
+// absolute-value modifiers per four values; with fmaxf it first quietened
+// every input that came from another block (up to seven instructions per
+// four values in the GEMM epilogues).  NaNs are ignored, as with fmaxf.
 __device__ __forceinline__ float absmax4(float m, float a, float b, float c, float d) {
-  return fmaxf(fmaxf(m, fmaxf(fabsf(a), fabsf(b))), fmaxf(fabsf(c), fabsf(d)));
+  const float inf = __builtin_inff();
+  m = __builtin_amdgcn_fmed3f(__builtin_fabsf(a), m, inf);
+  m = __builtin_amdgcn_fmed3f(__builtin_fabsf(b), m, inf);
+  m = __builtin_amdgcn_fmed3f(__builtin_fabsf(c), m, inf);
+  return __builtin_amdgcn_fmed3f(__builtin_fabsf(d), m, inf);
 }
 
 // Order-preserving map float -> int for atomicMax on floats of any sign.

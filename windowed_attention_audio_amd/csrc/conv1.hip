@@ -37,12 +37,14 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
   const int tid = threadIdx.x;
   if (tid >= CG * pl) return;
   const int cg = tid % CG, lane_pos = tid / CG;
+  // weights and bias halved (exact): the sums below are then (acc + b) / 2,
+  // bit for bit, the argument gelu_h takes
   float w[8][9], b[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    b[c] = a.b[cg * 8 + c];
+    b[c] = 0.5f * a.b[cg * 8 + c];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) w[c][k] = a.w[(cg * 8 + c) * 9 + k];
+    for (int k = 0; k < 9; ++k) w[c][k] = 0.5f * a.w[(cg * 8 + c) * 9 + k];
   }
   T* out = (T*)a.out + (int64_t)r * 64 * a.C + cg * 8;
   [[maybe_unused]] float amax = 0.f;
@@ -58,10 +60,10 @@ __global__ __launch_bounds__(256) void conv1_kernel(Conv1Args a, int pl) {
       float s = b[c];
 #pragma unroll
       for (int k = 0; k < 9; ++k) s += w[c][k] * p[k];
-      y[c] = gelu_f(s);
+      y[c] = gelu_h(s);
     }
     if constexpr (__is_same(T, f16_t))
-      amax = fmaxf(absmax4(amax, y[0], y[1], y[2], y[3]), absmax4(0.f, y[4], y[5], y[6], y[7]));
+      amax = absmax4(absmax4(amax, y[0], y[1], y[2], y[3]), y[4], y[5], y[6], y[7]);
     if constexpr (sizeof(T) == 2) {
       uint4 v;
       v.x = pack2f<T>(y[0], y[1]);

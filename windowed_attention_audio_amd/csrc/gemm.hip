@@ -90,11 +90,21 @@ __device__ __forceinline__ void load_bias(const GemmArgs& a, const int cbase, fl
   for (int j = 0; j < NI; ++j) b[j] = *(const float4*)(a.bias + min(cbase + 16 * j, a.N - 4));
 }
 
+// GELU epilogues take the halved bias (gelu_ab: same bits as gelu_f(acc + b)).
+template <int EPI, int NI>
+__device__ __forceinline__ void halve_bias_for_gelu(float4 (&b)[NI]) {
+  if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_SPLIT || EPI == EPI_GELU_PE) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) b[j] = make_float4(0.5f * b[j].x, 0.5f * b[j].y, 0.5f * b[j].z, 0.5f * b[j].w);
+  }
+}
+
 template <typename T, int EPI, int MI, int NI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI], const int rbase,
                                           const int cbase) {
   float4 bias[NI];
   load_bias<NI>(a, cbase, bias);
+  halve_bias_for_gelu<EPI, NI>(bias);
   constexpr bool PE = EPI == EPI_PE || EPI == EPI_GELU_PE;
   double tau[PE ? NI * 4 : 1];
 #pragma unroll
@@ -201,11 +211,13 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
           if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, v0, v1, v2, v3);
           store4((T*)a.C + (int64_t)row * a.ldc + col, v0, v1, v2, v3);
         } else if constexpr (EPI == EPI_GELU) {
-          const float g0 = gelu_f(v0), g1 = gelu_f(v1), g2 = gelu_f(v2), g3 = gelu_f(v3);
+          const float g0 = gelu_ab(acc[i][j][0], bias[j].x), g1 = gelu_ab(acc[i][j][1], bias[j].y);
+          const float g2 = gelu_ab(acc[i][j][2], bias[j].z), g3 = gelu_ab(acc[i][j][3], bias[j].w);
           if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, g0, g1, g2, g3);
           store4((T*)a.C + (int64_t)row * a.ldc + col, g0, g1, g2, g3);
         } else if constexpr (EPI == EPI_GELU_SPLIT) {
-          const float g4[4] = {gelu_f(v0), gelu_f(v1), gelu_f(v2), gelu_f(v3)};
+          const float g4[4] = {gelu_ab(acc[i][j][0], bias[j].x), gelu_ab(acc[i][j][1], bias[j].y),
+                               gelu_ab(acc[i][j][2], bias[j].z), gelu_ab(acc[i][j][3], bias[j].w)};
           if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, g4[0], g4[1], g4[2], g4[3]);
           float lo[4];
 #pragma unroll
@@ -225,7 +237,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
           // EPI_PE: the bias-free conv_out plus sinusoids; EPI_GELU_PE: the
           // last convolution's GELU(acc + bias) plus sinusoids
           const int half = a.N / 2;
-          const float v[4] = {v0, v1, v2, v3};
+          const float hb[4] = {bias[j].x, bias[j].y, bias[j].z, bias[j].w};  // halved (GELU) or bias-free
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -235,7 +247,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, f32x4 (&acc)[MI][NI
             double rev = (double)pos * tau[4 * j + e];
             rev -= rint(rev);
             const float fr = (float)rev;
-            o[e] = (EPI == EPI_GELU_PE ? gelu_f(v[e]) : acc[i][j][e]) +
+            o[e] = (EPI == EPI_GELU_PE ? gelu_ab(acc[i][j][e], hb[e]) : acc[i][j][e]) +
                    (col + e < half ? __builtin_amdgcn_sinf(fr) : __builtin_amdgcn_cosf(fr));
           }
           store4((float*)a.C + (int64_t)row * a.ldc + col, o[0], o[1], o[2], o[3]);
@@ -745,6 +757,7 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
   const int g = lane >> 4, l16 = lane & 15;
   float4 bias[NI];
   load_bias<NI>(a, n0 + wn * WTN + 4 * g, bias);
+  halve_bias_for_gelu<EPI, NI>(bias);
   [[maybe_unused]] float amax = 0.f;  // fp16: largest |value| converted (saturation report)
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
@@ -756,13 +769,17 @@ __device__ __forceinline__ void epilogue_staged4(const GemmArgs& a, f32x4 (&acc)
     for (int j = 0; j < NI; ++j) {
       const float4 b = bias[j];
       const int q = (wn * WTN + 16 * j + 4 * g) >> 3;  // chunk of the 4 values
-      float v0 = acc[i][j][0] + b.x, v1 = acc[i][j][1] + b.y, v2 = acc[i][j][2] + b.z,
-            v3 = acc[i][j][3] + b.w;
+      float v0, v1, v2, v3;
       if constexpr (EPI == EPI_GELU) {
-        v0 = gelu_f(v0);
-        v1 = gelu_f(v1);
-        v2 = gelu_f(v2);
-        v3 = gelu_f(v3);
+        v0 = gelu_ab(acc[i][j][0], b.x);
+        v1 = gelu_ab(acc[i][j][1], b.y);
+        v2 = gelu_ab(acc[i][j][2], b.z);
+        v3 = gelu_ab(acc[i][j][3], b.w);
+      } else {
+        v0 = acc[i][j][0] + b.x;
+        v1 = acc[i][j][1] + b.y;
+        v2 = acc[i][j][2] + b.z;
+        v3 = acc[i][j][3] + b.w;
       }
       if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, v0, v1, v2, v3);
       const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
@@ -814,6 +831,7 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
   const int rw = (wm % WPS) * WTM;  // first row of this wavefront inside its stage
   float4 bias[NI];
   load_bias<NI>(a, n0 + wn * WTN + 4 * g, bias);
+  halve_bias_for_gelu<EPI, NI>(bias);
   [[maybe_unused]] float amax = 0.f;  // fp16: largest |value| converted (saturation report)
   __syncthreads();  // every wavefront is done reading operand fragments
 #pragma unroll
@@ -823,13 +841,17 @@ __device__ __forceinline__ void epilogue_staged2(const GemmArgs& a, f32x4 (&acc)
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int r = rw + 16 * i + l16;
-      float v0 = acc[i][j][0] + b.x, v1 = acc[i][j][1] + b.y, v2 = acc[i][j][2] + b.z,
-            v3 = acc[i][j][3] + b.w;
+      float v0, v1, v2, v3;
       if constexpr (EPI == EPI_GELU) {
-        v0 = gelu_f(v0);
-        v1 = gelu_f(v1);
-        v2 = gelu_f(v2);
-        v3 = gelu_f(v3);
+        v0 = gelu_ab(acc[i][j][0], b.x);
+        v1 = gelu_ab(acc[i][j][1], b.y);
+        v2 = gelu_ab(acc[i][j][2], b.z);
+        v3 = gelu_ab(acc[i][j][3], b.w);
+      } else {
+        v0 = acc[i][j][0] + b.x;
+        v1 = acc[i][j][1] + b.y;
+        v2 = acc[i][j][2] + b.z;
+        v3 = acc[i][j][3] + b.w;
       }
       if constexpr (__is_same(T, f16_t)) amax = absmax4(amax, v0, v1, v2, v3);
       const uint2 w = make_uint2(pack2f<T>(v0, v1), pack2f<T>(v2, v3));
