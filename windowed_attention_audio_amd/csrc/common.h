@@ -48,18 +48,19 @@ __device__ __forceinline__ uint32_t pack2f(float a, float b) {
 // erfc after Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
 // erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z),
 // z >= 0, |error| <= 1.5e-7.  With z = |x| / sqrt 2 and the coefficients
-// halved, h = erfc(z) / 2 is the tail mass of the normal law beyond |x|:
-// Phi(x) = 1 - h for x >= 0 and h for x < 0, so GELU = x - x h or x h.
-// Both signs in one expression: x Phi(x) = x / 2 + |x| (1/2 - h).  Written
-// so for few instructions (it runs on every element of conv1-3 and fc1):
-// one reciprocal, one exp2, ten other ops, no compare or select; |error|
-// below 3.5e-7 (float32, measured against the exact erf form on [-12, 12]).
+// halved, q = erfc(z) / 2 is the tail mass of the normal law beyond |x|:
+// Phi(x) = 1 - q for x >= 0 and q for x < 0, so GELU = x - x q or x q.
+// Both signs in one expression: x Phi(x) = x / 2 + |x| (1/2 - q).  Written
+// so for few instructions (every element of conv1-3 and fc1 runs it, in the
+// gelu_h form below): one reciprocal, one exp2, ten other ops, no compare or
+// select; |error| below 3.5e-7 (float32, measured against the exact erf form
+// on [-12, 12]).  gelu_f is the reference form; the kernels call gelu_h.
 __device__ __forceinline__ float gelu_f(float x) {
   const float t = __builtin_amdgcn_rcpf(fmaf(0.23164190f, fabsf(x), 1.0f));  // p / sqrt 2
   const float P =
       t * fmaf(fmaf(fmaf(fmaf(0.5307027145f, t, -0.726576013f), t, 0.7107068705f), t, -0.142248368f),
                t, 0.127414796f);
-  const float r = fmaf(-P, __builtin_amdgcn_exp2f(x * x * -0.72134752044f), 0.5f);  // 1/2 - h
+  const float r = fmaf(-P, __builtin_amdgcn_exp2f(x * x * -0.72134752044f), 0.5f);  // 1/2 - q
   return fmaf(fabsf(x), r, 0.5f * x);
 }
 
@@ -75,7 +76,7 @@ __device__ __forceinline__ float gelu_h(float h) {
   const float P = t * fmaf(fmaf(fmaf(fmaf(2.0f * 0.5307027145f, t, 2.0f * -0.726576013f), t, 2.0f * 0.7107068705f),
                                 t, 2.0f * -0.142248368f),
                            t, 2.0f * 0.127414796f);
-  const float r = fmaf(-P, __builtin_amdgcn_exp2f(h * h * (4.0f * -0.72134752044f)), 1.0f);  // 1 - 2 h_tail
+  const float r = fmaf(-P, __builtin_amdgcn_exp2f(h * h * (4.0f * -0.72134752044f)), 1.0f);  // 1 - 2 q
   return fmaf(fabsf(h), r, h);
 }
 // GELU(acc + b) given hb = b / 2.
