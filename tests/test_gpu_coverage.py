@@ -213,3 +213,68 @@ def test_fp16_saturation_is_reported(weights_bf16):
                     device="cuda")
     W.mt_encode_stream(m.enc, wav, 104, 1, ws=ws)
     assert W.saturation_mask(ws) & W.MT_SAT_FFN
+
+
+# One weight tensor per stage scaled by a power of two (an exponent shift:
+# exact in bf16 and fp16; 2^15 for the tensors with entries near 1, so that
+# every scaled entry stays below 65504) drives that stage's fp16 outputs past
+# the fp16 range.  Each case must set its stage's
+# bit; the front-end lies upstream of every other stage, so only the
+# front-end cases may set the front-end bit.  The batch of 16 clips runs the
+# 256-row tile kernels (their staged epilogues), the single clip the small
+# tiles.
+SAT_CASES = [
+    ("conv1.weight", 15, "MT_SAT_FRONTEND"),
+    ("conv2.weight", 17, "MT_SAT_FRONTEND"),
+    ("conv3.weight", 17, "MT_SAT_FRONTEND"),
+    ("layers.0.ln1.weight", 15, "MT_SAT_LN"),
+    ("layers.0.q.weight", 17, "MT_SAT_QKV"),
+    ("layers.0.fc1.weight", 17, "MT_SAT_FFN"),
+    ("ln_post.weight", 15, "MT_SAT_HEAD"),
+    ("proj1.weight", 17, "MT_SAT_HEAD"),
+    ("proj2.weight", 17, "MT_SAT_ADAPTER"),
+    ("adapter.gate.weight", 17, "MT_SAT_ADAPTER"),
+]
+
+
+@pytest.fixture(scope="module")
+def sat_setup():
+    import torch
+    geom = synth.geom_for(synth.workload(4), n_layers=1)  # with the adapter
+    base = synth.with_adapter(synth.make_weights(geom, bf16=True), geom, bf16=True)
+    clips = synth.make_clips(synth.workload(2))
+    # packed log-mel rows [sum T, 128] with their per-clip frame counts
+    mels = {"16x30s": (gpu_logmel(clips), [len(c) // 160 for c in clips]),
+            "1x30s": (gpu_logmel(clips[:1]), [len(clips[0]) // 160])}
+    torch.cuda.synchronize()
+    return geom, base, mels
+
+
+@pytest.mark.parametrize("batch", ["16x30s", "1x30s"])
+@pytest.mark.parametrize("name,e,bit", SAT_CASES)
+def test_fp16_saturation_bit_per_stage(sat_setup, batch, name, e, bit):
+    import torch
+    import windowed_attention_audio_amd as W
+    geom, base, mels = sat_setup
+    mel, T = mels[batch]
+    assert mel.shape == (sum(T), 128)
+    scaled = dict(base)
+    v = base[name] * np.float32(2.0 ** e)
+    assert float(np.abs(v).max()) < 65504.0
+    scaled[name] = v.astype(np.float32)
+
+    def run(weights):
+        m = GpuModel(geom, "f16", weights)
+        ws = torch.full((W.mt_encode_workspace_size(m.enc, T, 104),), 255, dtype=torch.uint8, device="cuda")
+        out = W.mt_encode(m.enc, torch.from_numpy(mel).cuda(), T, 104, ws=ws)
+        torch.cuda.synchronize()
+        return W.saturation_mask(ws), out
+
+    if name == SAT_CASES[0][0]:
+        assert run(base)[0] == 0
+    got, out = run(scaled)
+    say(f"  {batch} {name} x 2^{e}: mask {got}")
+    assert got & getattr(W, bit), f"{name}: {bit} not reported (mask {got})"
+    if bit != "MT_SAT_FRONTEND":
+        assert not got & W.MT_SAT_FRONTEND
+    assert bool(torch.isfinite(out).all())  # clamped, not inf

@@ -292,3 +292,40 @@ def test_with_adapter_equals_full_draw():
     assert any(k.startswith("adapter.") for k in full)
     for k in full:
         assert np.array_equal(full[k], built[k]), k
+
+
+def test_binding_rejects_inputs_shorter_than_the_lengths():
+    # The C ABI takes raw device pointers: a tensor smaller than its host
+    # lengths say would be read past its end.  The binding compares shapes
+    # with the lengths first and raises (no device needed: shape-only
+    # stand-ins).
+    class Shape:
+        def __init__(self, *shape):
+            self.shape = shape
+
+        def dim(self):
+            return len(self.shape)
+
+        def numel(self):
+            n = 1
+            for x in self.shape:
+                n *= x
+            return n
+
+    chk = W._check_input
+    chk(Shape(48000, 128), [3000] * 16, W.MT_PACKED, 128, "mel")          # exact
+    chk(Shape(48001, 128), [3000] * 16, W.MT_PACKED, 128, "mel")          # larger buffer: fine
+    chk(Shape(16, 3000, 128), [3000] * 16, W.MT_PADDED, 128, "mel")
+    chk(Shape(16 * 480000), [480000] * 16, W.MT_PACKED, 0, "wav")
+    for t, lens, layout, width in [
+            (Shape(48000, 128), [128] * 48000, W.MT_PACKED, 128),  # rows read as sequences
+            (Shape(47999, 128), [3000] * 16, W.MT_PACKED, 128),
+            (Shape(48000, 80), [3000] * 16, W.MT_PACKED, 128),
+            (Shape(16, 2999, 128), [3000] * 16, W.MT_PADDED, 128),
+            (Shape(15, 3000, 128), [3000] * 16, W.MT_PADDED, 128),
+            (Shape(100), [200], W.MT_PACKED, 0)]:
+        with pytest.raises(ValueError):
+            chk(t, lens, layout, width, "x")
+    W._check_output(Shape(6000, 2048), (6000, 2048), "out")
+    with pytest.raises(ValueError):
+        W._check_output(Shape(5999, 2048), (6000, 2048), "out")

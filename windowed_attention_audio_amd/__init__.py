@@ -171,6 +171,29 @@ def make_batch(lens, layout=MT_PACKED, max_len=0):
     return b
 
 
+def _check_input(t, lens, layout, width, what):
+    """The library takes raw device pointers and cannot see buffer sizes: a
+    tensor whose shape does not match the host lengths would be read past its
+    end.  Raise here instead.  width: trailing row width (0 for waveforms)."""
+    lens = [int(x) for x in lens]
+    tail = (width,) if width else ()
+    if layout == MT_PADDED:
+        ok = t.dim() == 2 + len(tail) and t.shape[0] >= len(lens) and t.shape[1] >= max(lens, default=0) \
+            and tuple(t.shape[2:]) == tail
+        want = f"[>= {len(lens)}, >= {max(lens, default=0)}" + (f", {width}]" if width else "]")
+    else:
+        ok = t.dim() == 1 + len(tail) and t.shape[0] >= sum(lens) and tuple(t.shape[1:]) == tail
+        want = f"[>= {sum(lens)}" + (f", {width}]" if width else "]")
+    if not ok:
+        raise ValueError(f"{what}: shape {tuple(t.shape)} does not match the lengths (expected {want})")
+
+
+def _check_output(t, shape, what):
+    import math
+    if t.numel() < math.prod(shape):
+        raise ValueError(f"{what}: {t.numel()} elements, the call writes {math.prod(shape)} ({shape})")
+
+
 def _stream_ptr(stream):
     import torch
     if stream is None:
@@ -206,6 +229,7 @@ def mt_logmel(wav, lens, layout=MT_PACKED, max_len=0, mel=None, ws=None, stream=
     Returns the fp32 log-mel tensor [sum T, 128] or [B, max_len // 160, 128]."""
     import torch
     assert wav.is_cuda and wav.dtype == torch.float32 and wav.is_contiguous()
+    _check_input(wav, lens, layout, 0, "mt_logmel wav")
     if layout == MT_PADDED:
         max_len = wav.shape[1]
         shape = (len(lens), max_len // 160, 128)
@@ -214,6 +238,7 @@ def mt_logmel(wav, lens, layout=MT_PACKED, max_len=0, mel=None, ws=None, stream=
     b = make_batch(lens, layout, max_len)
     if mel is None:
         mel = torch.empty(shape, dtype=torch.float32, device=wav.device)
+    _check_output(mel, shape, "mt_logmel mel")
     nbytes = mt_logmel_workspace_size(lens, layout, max_len)
     if ws is None:
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=wav.device)
@@ -230,6 +255,7 @@ def mt_logmel_noalloc(wav, lens, layout=MT_PACKED, max_len=0, mel=None, stream=N
     overlap)."""
     import torch
     assert wav.is_cuda and wav.dtype == torch.float32 and wav.is_contiguous()
+    _check_input(wav, lens, layout, 0, "mt_logmel_noalloc wav")
     if layout == MT_PADDED:
         max_len = wav.shape[1]
         shape = (len(lens), max_len // 160, 128)
@@ -238,6 +264,7 @@ def mt_logmel_noalloc(wav, lens, layout=MT_PACKED, max_len=0, mel=None, stream=N
     b = make_batch(lens, layout, max_len)
     if mel is None:
         mel = torch.empty(shape, dtype=torch.float32, device=wav.device)
+    _check_output(mel, shape, "mt_logmel_noalloc mel")
     _check(lib().mt_logmel_noalloc(ctypes.c_void_p(wav.data_ptr()), ctypes.byref(b),
                                    ctypes.c_void_p(mel.data_ptr()), _stream_ptr(stream)))
     return mel
@@ -326,6 +353,7 @@ def mt_encode(enc: Encoder, mel, lens, window, layout=MT_PACKED, out=None, ws=No
     Returns fp32 [sum N, d] or [B, N(max_len), d]."""
     import torch
     assert mel.is_cuda and mel.dtype == torch.float32 and mel.is_contiguous()
+    _check_input(mel, lens, layout, enc.cfg.n_mels, "mt_encode mel")
     max_len = mel.shape[1] if layout == MT_PADDED else 0
     d = enc.d_out
     fe = enc.cfg.frontend
@@ -336,6 +364,7 @@ def mt_encode(enc: Encoder, mel, lens, window, layout=MT_PACKED, out=None, ws=No
     b = make_batch(lens, layout, max_len)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=mel.device)
+    _check_output(out, shape, "mt_encode out")
     if ws is None:
         nbytes = mt_encode_workspace_size(enc, lens, window, layout, max_len)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=mel.device)
