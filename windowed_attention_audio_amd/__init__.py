@@ -485,6 +485,9 @@ def mt_prompt_embed(tokens, table, audio, audio_token, out=None, ws=None, stream
     d = table.shape[1]
     if out is None:
         out = torch.empty((len(tokens), d), dtype=torch.float32, device=table.device)
+    _check_output(out, (len(tokens), d), "mt_prompt_embed out")
+    if audio.dim() != 2 or audio.shape[1] != d:
+        raise ValueError(f"mt_prompt_embed: audio {tuple(audio.shape)} against a table of width {d}")
     if ws is None:
         ws = torch.empty(mt_prompt_embed_workspace_size(len(tokens)), dtype=torch.uint8,
                          device=table.device)
@@ -583,10 +586,19 @@ def mt_decode(dec: Decoder, x, seq, pos, cache, max_seqs, max_pos, logits=None, 
     import torch
     n = len(seq)
     assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.shape[0] == n
+    if x.dim() != 2 or x.shape[1] != dec.cfg.d_model or len(pos) != n:
+        raise ValueError(f"mt_decode: x {tuple(x.shape)} with {n} seq / {len(pos)} pos entries "
+                         f"(expected [{n}, {dec.cfg.d_model}])")
+    need = mt_decoder_cache_bytes(dec, max_seqs, max_pos)
+    if cache.numel() * cache.element_size() < need:
+        raise ValueError(f"mt_decode: cache of {cache.numel() * cache.element_size()} bytes, "
+                         f"{max_seqs} x {max_pos} positions need {need}")
     if logits is None:
         logits = torch.empty((n, dec.cfg.vocab), dtype=torch.float32, device=x.device)
     if next_ids is None:
         next_ids = torch.empty(n, dtype=torch.int32, device=x.device)
+    _check_output(logits, (n, dec.cfg.vocab), "mt_decode logits")
+    _check_output(next_ids, (n,), "mt_decode next_ids")
     if ws is None:
         ws = torch.empty(max(mt_decode_workspace_size(dec, seq, pos, max_seqs, max_pos), 1), dtype=torch.uint8,
                          device=x.device)
